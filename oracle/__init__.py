@@ -1,0 +1,157 @@
+"""CPU oracle for token-level sparse attention prefill -- TEST INFRASTRUCTURE ONLY.
+
+Plain fp64 C implementation (``hs2_oracle.c``) of the selection (per-head row
+statistics, group probability score, top-K outside a forced recent window,
+ascending index row) and of the sparse attention over the selected positions.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The GPU library never calls it.
+
+Every function here is a thin ctypes wrapper; the arithmetic is in the C file,
+whose header lists the passages it follows and the readings taken where the
+pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libhs2_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile libhs2_oracle.so in-tree with gcc (plain -O2, no fast-math)."""
+    src = os.path.join(_HERE, "hs2_oracle.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", src,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.hs2o_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, vp, i64, vp, vp, i32]
+    lib.hs2o_select.restype = i32
+    lib.hs2o_group_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i64, i32, vp, vp, vp]
+    lib.hs2o_group_scores.restype = i32
+    lib.hs2o_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, vp, vp, i64,
+                                     vp, vp, i32]
+    lib.hs2o_sparse_attn.restype = i32
+    lib.hs2o_bf16_round.argtypes = [f64]
+    lib.hs2o_bf16_round.restype = ctypes.c_uint16
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    return max(1, min(64, os.cpu_count() or 1))
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, "bf16 tensors are passed as uint16 bit patterns"
+    return a
+
+
+def _cu(cu):
+    return np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+
+
+def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None):
+    """Index rows and K-th scores.
+
+    q [T,Hq,d], k [T,Hkv,d] bf16 bits; rows: None (all T*Hkv rows, row id = t*Hkv+g)
+    or an int64 array of row ids. Returns (idx [n, K+W] int32, kth [n] float64).
+    """
+    lib = _load()
+    q, k, cu = _u16(q), _u16(k), _cu(cu_seqlens)
+    d = q.shape[-1]
+    B = len(cu) - 1
+    T = int(cu[-1])
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = len(rows)
+    else:
+        n = T * Hkv
+    idx = np.empty((n, K + W), dtype=np.int32)
+    kth = np.empty(n, dtype=np.float64)
+    if n == 0:
+        return idx, kth
+    r = lib.hs2o_select(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d, scale, K, W,
+                        rows.ctypes.data if rows is not None else None, n, idx.ctypes.data,
+                        kth.ctypes.data, nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_select: bad arguments")
+    return idx, kth
+
+
+def group_scores(q, k, cu_seqlens, Hq, Hkv, t_global, g, scale=None):
+    """(S [t+1], m [G], l [G]) of row (t_global, g): group score over causal keys and head stats."""
+    lib = _load()
+    q, k, cu = _u16(q), _u16(k), _cu(cu_seqlens)
+    d = q.shape[-1]
+    B = len(cu) - 1
+    i = int(np.searchsorted(cu, t_global, side="right") - 1)
+    t = int(t_global - cu[i])
+    G = Hq // Hkv
+    S = np.empty(t + 1, dtype=np.float64)
+    m = np.empty(G, dtype=np.float64)
+    l = np.empty(G, dtype=np.float64)
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    r = lib.hs2o_group_scores(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d, scale,
+                              int(t_global), int(g), S.ctypes.data, m.ctypes.data, l.ctypes.data)
+    if r != 0:
+        raise ValueError("hs2o_group_scores: bad arguments")
+    return S, m, l
+
+
+def sparse_attn(q, k, v, cu_seqlens, Hq, Hkv, idx, scale=None, tokens=None, nthreads=None,
+                want_f64=True, want_bf16=True):
+    """Sparse attention over idx rows. idx [T, Hkv, KW] int32 (local positions, -1 = none).
+
+    Returns (o64 [n,Hq,d] float64 or None, o16 [n,Hq,d] bf16 bits or None).
+    """
+    lib = _load()
+    q, k, v, cu = _u16(q), _u16(k), _u16(v), _cu(cu_seqlens)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    d = q.shape[-1]
+    B = len(cu) - 1
+    T = int(cu[-1])
+    KW = idx.shape[-1]
+    assert idx.size == T * Hkv * KW
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    if tokens is not None:
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        n = len(tokens)
+    else:
+        n = T
+    o64 = np.empty((n, Hq, d), dtype=np.float64) if want_f64 else None
+    o16 = np.empty((n, Hq, d), dtype=np.uint16) if want_bf16 else None
+    if n == 0:
+        return o64, o16
+    r = lib.hs2o_sparse_attn(q.ctypes.data, k.ctypes.data, v.ctypes.data, cu.ctypes.data, B, Hq,
+                             Hkv, d, scale, KW, idx.ctypes.data,
+                             tokens.ctypes.data if tokens is not None else None, n,
+                             o64.ctypes.data if o64 is not None else None,
+                             o16.ctypes.data if o16 is not None else None,
+                             nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_sparse_attn: bad arguments")
+    return o64, o16
+
+
+def bf16_round(x: float) -> int:
+    return int(_load().hs2o_bf16_round(float(x)))

@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against facts fixed outside it (runs without a GPU).
+
+Each test checks the oracle against something it does not share code with:
+library routines (torch scaled_dot_product_attention, scipy softmax), brute force
+on tiny inputs, closed forms, and invariants of the selection rule. The
+selection rule itself is: per query token t and KV group g, keep the K best
+candidates outside the forced recent window of W tokens, by the sum over the
+group's heads of each head's softmax probability (HySparse2 news summary,
+token-granularity and KV-reuse paragraphs; readings R1-R6 in the oracle header).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synthgen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf(a):
+    return synthgen.bf16_to_float(a).astype(np.float64)
+
+
+def rand_inputs(lengths, Hq, Hkv, d, seed, scale_q=1.0):
+    T = int(sum(lengths))
+    q = synthgen.normal_bf16(seed, 1, (T, Hq, d))
+    k = synthgen.normal_bf16(seed, 2, (T, Hkv, d))
+    v = synthgen.normal_bf16(seed, 3, (T, Hkv, d))
+    if scale_q != 1.0:
+        q = synthgen.float_to_bf16(bf(q) * scale_q)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return q, k, v, cu
+
+
+def group_scores_ref(q, k, cu, Hq, Hkv, tg, g, scale):
+    """Independent S row: scipy softmax per head over causal keys, summed over the group."""
+    i = int(np.searchsorted(cu, tg, side="right") - 1)
+    base, t = int(cu[i]), int(tg - cu[i])
+    G = Hq // Hkv
+    kk = bf(k[base:base + t + 1, g, :])
+    S = np.zeros(t + 1)
+    for hh in range(G):
+        z = scale * (kk @ bf(q[tg, g * G + hh, :]))
+        S += scipy.special.softmax(z)
+    return S
+
+
+# ----------------------------------------------------------------------------
+# C1: with K + W >= L every row is [0, t] and the sparse layer is dense causal
+# attention (library routine: torch SDPA, fp64, per sequence, GQA expanded).
+# ----------------------------------------------------------------------------
+def test_c1_dense_equivalence_against_sdpa():
+    lengths, Hq, Hkv, d = [37, 50, 1], 8, 2, 128
+    K, W = 40, 16
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=11)
+    qs = synthgen.normal_bf16(11, 10, q.shape)
+    idx, _ = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    T = int(cu[-1])
+    idx3 = idx.reshape(T, Hkv, K + W)
+    for i in range(len(lengths)):
+        for t in range(lengths[i]):
+            row = idx3[cu[i] + t]
+            for g in range(Hkv):
+                assert list(row[g, :t + 1]) == list(range(t + 1))
+                assert (row[g, t + 1:] == -1).all()
+    o64, _ = oracle.sparse_attn(qs, k, v, cu, Hq, Hkv, idx3, want_bf16=False)
+    G = Hq // Hkv
+    for i in range(len(lengths)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        Q = torch.from_numpy(bf(qs[a:b])).permute(1, 0, 2)[None]
+        Kt = torch.from_numpy(bf(k[a:b])).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        Vt = torch.from_numpy(bf(v[a:b])).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, is_causal=True)
+        ref = ref[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(o64[a:b], ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# C2: brute force over all size-K subsets on tiny inputs.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 1), (3, 1)])
+def test_c2_bruteforce_topk(G, Hkv):
+    Hq, d = G * Hkv, 8
+    for L in (5, 9, 12):
+        q, k, _, cu = rand_inputs([L], Hq, Hkv, d, seed=100 + L + G, scale_q=3.0)
+        scale = 1.0 / math.sqrt(d)
+        for K in (1, 2, 3):
+            for W in (0, 1, 2):
+                if K + W == 0:
+                    continue
+                idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W, scale=scale)
+                for t in range(L):
+                    for g in range(Hkv):
+                        S = group_scores_ref(q, k, cu, Hq, Hkv, t, g, scale)
+                        row = idx[t * Hkv + g]
+                        cand = list(range(0, max(0, t - W + 1)))
+                        sel = [int(j) for j in row if 0 <= j < t - W + 1]
+                        if len(cand) <= K:
+                            assert sel == cand
+                            assert kth[t * Hkv + g] == -1.0
+                            continue
+                        best = max(sum(S[list(c)]) for c in itertools.combinations(cand, K))
+                        assert len(sel) == K
+                        assert abs(sum(S[sel]) - best) <= 1e-12
+                        unsel = [j for j in cand if j not in sel]
+                        assert min(S[sel]) >= max(S[unsel]) - 1e-15
+                        assert abs(kth[t * Hkv + g] - min(S[sel])) <= 1e-15
+
+
+# ----------------------------------------------------------------------------
+# C3 + C4: structural invariants on ragged varlen batches.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("K,W", [(20, 7), (1, 0), (0, 5), (64, 1)])
+def test_c3_c4_structure(K, W):
+    lengths, Hq, Hkv, d = [1, 5, 130, 300, 64], 4, 2, 32
+    q, k, _, cu = rand_inputs(lengths, Hq, Hkv, d, seed=5)
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    T = int(cu[-1])
+    idx3 = idx.reshape(T, Hkv, K + W)
+    for i, L in enumerate(lengths):
+        for t in range(L):
+            for g in range(Hkv):
+                row = idx3[cu[i] + t, g]
+                n_t = min(t + 1, K + W)
+                valid = row[:n_t]
+                assert (row[n_t:] == -1).all()
+                assert (valid >= 0).all() and (valid <= t).all()
+                assert (np.diff(valid) > 0).all()
+                window = set(range(max(0, t - W + 1), t + 1))
+                assert window <= set(valid.tolist())  # C3
+                n_glob = sum(1 for j in valid if j < t - W + 1)
+                assert n_glob == min(K, max(0, t - W + 1))
+
+
+# ----------------------------------------------------------------------------
+# C5: the group score sums to G over the causal keys (probabilities sum to 1).
+# ----------------------------------------------------------------------------
+def test_c5_group_score_sums_to_G():
+    lengths, Hq, Hkv, d = [200, 77], 8, 2, 128
+    q, k, _, cu = rand_inputs(lengths, Hq, Hkv, d, seed=9, scale_q=2.0)
+    G = Hq // Hkv
+    for tg in (0, 1, 150, 199, 200, 276):
+        for g in range(Hkv):
+            S, m, l = oracle.group_scores(q, k, cu, Hq, Hkv, tg, g)
+            assert abs(S.sum() - G) <= 1e-12
+            assert (S > 0).all()
+            np.testing.assert_allclose(S, group_scores_ref(q, k, cu, Hq, Hkv, tg, g, 1 / math.sqrt(d)),
+                                       rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# C6: Q = 0 makes every score equal; the tie rule (lower position first) then
+# gives T_t = [0, min(K, t-W+1)) and kth = G/(t+1).
+# ----------------------------------------------------------------------------
+def test_c6_zero_query_tie_break():
+    lengths, Hq, Hkv, d, K, W = [90, 41], 4, 2, 128, 10, 6
+    q, k, _, cu = rand_inputs(lengths, Hq, Hkv, d, seed=3)
+    q[:] = 0
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    G = Hq // Hkv
+    for i, L in enumerate(lengths):
+        for t in range(L):
+            for g in range(Hkv):
+                r = (int(cu[i]) + t) * Hkv + g
+                row = idx[r]
+                glob = [int(j) for j in row if 0 <= j < t - W + 1]
+                assert glob == list(range(min(K, max(0, t - W + 1))))
+                if t - W + 1 > K:
+                    assert abs(kth[r] - G / (t + 1)) <= 1e-15
+                else:
+                    assert kth[r] == -1.0
+
+
+# ----------------------------------------------------------------------------
+# C7: sparse attention equals dense attention with -inf outside the index set
+# (masking before the softmax), computed with torch.softmax in fp64.
+# ----------------------------------------------------------------------------
+def test_c7_masked_dense_equivalence():
+    lengths, Hq, Hkv, d, KW = [60, 33], 8, 2, 128, 24
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=21)
+    T = int(cu[-1])
+    rng = np.random.default_rng(0)
+    idx = np.full((T, Hkv, KW), -1, dtype=np.int32)
+    for i, L in enumerate(lengths):
+        for t in range(L):
+            for g in range(Hkv):
+                n = int(rng.integers(1, min(t + 1, KW) + 1))
+                sel = np.sort(rng.choice(t + 1, size=n, replace=False))
+                idx[cu[i] + t, g, :n] = sel
+    o64, _ = oracle.sparse_attn(q, k, v, cu, Hq, Hkv, idx, want_bf16=False)
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(d)
+    for i, L in enumerate(lengths):
+        a = int(cu[i])
+        Kt = torch.from_numpy(bf(k[a:a + L]))
+        Vt = torch.from_numpy(bf(v[a:a + L]))
+        for t in range(L):
+            for h in range(Hq):
+                g = h // G
+                mask = torch.full((L,), float("-inf"), dtype=torch.float64)
+                sel = idx[a + t, g][idx[a + t, g] >= 0]
+                mask[torch.from_numpy(sel.astype(np.int64))] = 0.0
+                z = scale * (Kt[:, g, :] @ torch.from_numpy(bf(q[a + t, h]))) + mask
+                ref = torch.softmax(z, 0) @ Vt[:, g, :]
+                np.testing.assert_allclose(o64[a + t, h], ref.numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# C8: a packed varlen batch gives the per-sequence results concatenated.
+# ----------------------------------------------------------------------------
+def test_c8_varlen_packing_independence():
+    lengths, Hq, Hkv, d, K, W = [70, 3, 129], 4, 2, 64, 16, 8
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=8)
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    T = int(cu[-1])
+    o64, _ = oracle.sparse_attn(q, k, v, cu, Hq, Hkv, idx.reshape(T, Hkv, K + W), want_bf16=False)
+    for i, L in enumerate(lengths):
+        a, b = int(cu[i]), int(cu[i + 1])
+        cu1 = np.array([0, L], dtype=np.int32)
+        idx1, kth1 = oracle.select(q[a:b], k[a:b], cu1, Hq, Hkv, K, W)
+        assert (idx1 == idx[a * Hkv:b * Hkv]).all()
+        assert (kth1 == kth[a * Hkv:b * Hkv]).all()
+        o1, _ = oracle.sparse_attn(q[a:b], k[a:b], v[a:b], cu1, Hq, Hkv,
+                                   idx1.reshape(L, Hkv, K + W), want_bf16=False)
+        assert (o1 == o64[a:b]).all()
+
+
+# ----------------------------------------------------------------------------
+# C9: permuting the heads within a group leaves the selection unchanged.
+# ----------------------------------------------------------------------------
+def test_c9_head_permutation_invariance():
+    lengths, Hq, Hkv, d, K, W = [150], 8, 2, 128, 12, 4
+    q, k, _, cu = rand_inputs(lengths, Hq, Hkv, d, seed=13)
+    G = Hq // Hkv
+    perm = np.concatenate([g * G + np.array([2, 0, 3, 1]) for g in range(Hkv)])
+    qp = np.ascontiguousarray(q[:, perm, :])
+    idx1, kth1 = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    idx2, kth2 = oracle.select(qp, k, cu, Hq, Hkv, K, W)
+    assert (idx1 == idx2).all()
+    for tg in (5, 80, 149):
+        for g in range(Hkv):
+            s1, _, _ = oracle.group_scores(q, k, cu, Hq, Hkv, tg, g)
+            s2, _, _ = oracle.group_scores(qp, k, cu, Hq, Hkv, tg, g)
+            assert (np.abs(s1 - s2) <= 1e-15 * np.abs(s1)).all()
+
+
+# ----------------------------------------------------------------------------
+# Hand-worked example with closed forms (d = 1, one head, scale 1).
+# k = [0, 1, 2, 0.5], q = 1 -> z_j = k_j. At t = 3 with K = 2, W = 1:
+# window {3}, candidates {0,1,2} with S_j = e^{k_j} / (1 + e + e^2 + e^0.5);
+# the top-2 are {2, 1}, so I_3 = [1, 2, 3] and kth = e / (1 + e + e^2 + sqrt(e)).
+# The sparse layer with q' = 1 and v = [10, 20, 30, 40] then gives
+# o_3 = (20 e + 30 e^2 + 40 sqrt(e)) / (e + e^2 + sqrt(e)).
+# ----------------------------------------------------------------------------
+def test_hand_worked_example():
+    one = synthgen.float_to_bf16(np.array([1.0]))[0]
+    kv = synthgen.float_to_bf16(np.array([0.0, 1.0, 2.0, 0.5]))
+    vv = synthgen.float_to_bf16(np.array([10.0, 20.0, 30.0, 40.0]))
+    q = np.full((4, 1, 1), one, dtype=np.uint16)
+    k = kv.reshape(4, 1, 1).astype(np.uint16)
+    v = vv.reshape(4, 1, 1).astype(np.uint16)
+    cu = np.array([0, 4], dtype=np.int32)
+    idx, kth = oracle.select(q, k, cu, 1, 1, 2, 1, scale=1.0)
+    e = math.e
+    Z = 1 + e + e * e + math.sqrt(e)
+    assert list(idx[3]) == [1, 2, 3]
+    assert abs(kth[3] - e / Z) <= 1e-15
+    # t = 2: window {2}, candidates {0,1}: both taken (|C| = 2 <= K)
+    assert list(idx[2]) == [0, 1, 2] and kth[2] == -1.0
+    S, m, l = oracle.group_scores(q, k, cu, 1, 1, 3, 0, scale=1.0)
+    np.testing.assert_allclose(S, np.array([1, e, e * e, math.sqrt(e)]) / Z, rtol=1e-15)
+    assert m[0] == 2.0
+    o64, o16 = oracle.sparse_attn(q, k, v, cu, 1, 1, idx.reshape(4, 1, 3), scale=1.0)
+    ref = (20 * e + 30 * e * e + 40 * math.sqrt(e)) / (e + e * e + math.sqrt(e))
+    assert abs(o64[3, 0, 0] - ref) <= 1e-12
+    # t = 0: only itself -> v_0
+    assert o64[0, 0, 0] == 10.0
+
+
+# ----------------------------------------------------------------------------
+# The selection budget printed on the HySparse2 page (1024 global + 128 recent).
+# ----------------------------------------------------------------------------
+def test_paper_budget_structure():
+    with open(os.path.join(GOLDEN, "paper_budget.json")) as f:
+        cfg = json.load(f)
+    K, W = cfg["K"], cfg["W"]
+    L, Hq, Hkv, d = 1300, 2, 1, 16
+    q, k, _, cu = rand_inputs([L], Hq, Hkv, d, seed=17)
+    rows = np.array([0, 127, 128, 1150, 1151, 1152, 1299], dtype=np.int64)
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W, rows=rows)
+    for r, t in enumerate(rows):
+        valid = idx[r][idx[r] >= 0]
+        assert len(valid) == min(t + 1, K + W)
+        if t + 1 >= K + W:
+            assert (valid[-W:] == np.arange(t - W + 1, t + 1)).all()
+            assert (valid[:K] < t - W + 1).all()
+            assert (kth[r] > 0) if t - W + 1 > K else (kth[r] == -1.0)
+        else:
+            assert (valid == np.arange(t + 1)).all()
+
+
+# ----------------------------------------------------------------------------
+# Regression fixture written by tests/golden/make_golden.py (oracle only).
+# ----------------------------------------------------------------------------
+def test_golden_regression():
+    path = os.path.join(GOLDEN, "oracle_small.json")
+    with open(path) as f:
+        gold = json.load(f)
+    w = gold["workload"]
+    q, k, v, cu = rand_inputs(w["lengths"], w["Hq"], w["Hkv"], w["d"], seed=w["seed"])
+    idx, kth = oracle.select(q, k, cu, w["Hq"], w["Hkv"], w["K"], w["W"])
+    T = int(cu[-1])
+    o64, o16 = oracle.sparse_attn(q, k, v, cu, w["Hq"], w["Hkv"], idx.reshape(T, w["Hkv"], -1))
+    for r, row in gold["idx_rows"].items():
+        assert idx[int(r)].tolist() == row
+    for r, val in gold["kth"].items():
+        assert kth[int(r)] == pytest.approx(val, rel=1e-13, abs=0)
+    np.testing.assert_allclose(o64.sum(axis=(1, 2)), np.array(gold["o_token_sums"]), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_bf16_rounding_of_oracle_and_generator():
+    """Both double->bf16 routines return the nearest bf16, ties to even (brute-force check)."""
+    rng = np.random.default_rng(1)
+    xs = np.concatenate([rng.normal(size=2000) * 10.0 ** rng.integers(-6, 6, 2000),
+                         [0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.0e38, -2.5e-39]])
+    for x in xs:
+        for fn in (oracle.bf16_round, synthgen.bf16_from_double):
+            b = fn(float(x))
+            val = float(synthgen.bf16_to_float(np.array([b], dtype=np.uint16))[0])
+            lo = float(synthgen.bf16_to_float(np.array([b - 1 if b & 0x7FFF else b], dtype=np.uint16))[0])
+            hi = float(synthgen.bf16_to_float(np.array([b + 1], dtype=np.uint16))[0])
+            err = abs(val - x)
+            assert err <= abs(lo - x) + 0.0 and err <= abs(hi - x) + 0.0, (x, b)
+            if err == abs(lo - x) and lo != val or err == abs(hi - x) and hi != val:
+                assert (b & 1) == 0  # tie -> even
