@@ -1,0 +1,201 @@
+"""Prefill benchmark of token-level sparse attention (select + sparse layers) on one MI355X.
+
+One step = one hybrid module over the whole prompt: hs2_prefill_block, i.e. the
+full layer's token selection (row statistics, group scores, top-K + forced
+recent window, index rows) followed by every sparse layer reusing K/V and the
+index rows. Inputs are seeded synthetic bf16 tensors already resident in HBM.
+
+Default workload: B=1, L=32768, Hq=32, Hkv=8, d=128, K=1024, W=128, needle keys,
+1 select + 3 sparse layers. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "prefill tokens/sec (select+sparse attn) at L=32k; % MFMA peak, % HBM BW"
+
+
+def algorithmic_work(lengths, Hq, Hkv, d, K, W):
+    """Selection MFMA flops (two QK^T passes) and sparse-layer bytes per layer."""
+    KW = K + W
+    pairs = sum(L * (L + 1) // 2 for L in lengths)
+    f_sel = 4 * d * Hq * pairs
+    n_sum = 0
+    for L in lengths:
+        m = min(L, KW)
+        n_sum += m * (m + 1) // 2 + (L - m) * KW  # sum_t min(t+1, KW)
+    T = sum(lengths)
+    gathered = Hkv * n_sum * 2 * d * 2           # K and V rows, once per (t, g)
+    idx_bytes = T * Hkv * KW * 4
+    qo_bytes = 2 * T * Hq * d * 2
+    return f_sel, gathered + idx_bytes + qo_bytes, n_sum
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "token_level_sparse_hs2_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file, workload):
+    """HBM bytes per launch measured by rocprofv3 counters, if still valid for this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(workload, {}).get(kernel_file)
+    if not e or e.get("source_sha256_16") != kernel_source_hash(kernel_file):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, w, n_tokens, threads):
+    """The oracle (select for every group + every sparse layer) on a uniform token sample."""
+    import numpy as np
+    import oracle
+    T = w.total
+    toks = np.unique(np.linspace(0, T - 1, n_tokens).round().astype(np.int64))
+    rows = (toks[:, None] * w.Hkv + np.arange(w.Hkv)[None, :]).ravel()
+    t0 = time.perf_counter()
+    o_idx, _ = oracle.select(inp["q_full"], inp["k"], inp["cu_seqlens"], w.Hq, w.Hkv, w.K, w.W,
+                             scale=w.scale, rows=rows, nthreads=threads)
+    full_idx = np.full((T, w.Hkv, w.K + w.W), -1, dtype=np.int32)
+    full_idx[toks] = o_idx.reshape(len(toks), w.Hkv, -1)
+    for qs in inp["q_sparse"]:
+        oracle.sparse_attn(qs, inp["k"], inp["v"], inp["cu_seqlens"], w.Hq, w.Hkv, full_idx,
+                           scale=w.scale, tokens=toks, nthreads=threads, want_bf16=False)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(toks)} tokens evenly spaced over the {T}-token prompt (every KV group, "
+                      f"select + {len(inp['q_sparse'])} sparse layers), fp64 C oracle, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="32k", choices=["tiny", "8k", "32k", "128k", "varlen"])
+    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the work shards by KV group with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthgen
+    import token_level_sparse_hs2_amd as hs2
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from hs2_testlib import GpuCase
+
+    w = synthgen.workload(args.workload)
+    t_in = time.perf_counter()
+    inp = synthgen.make_inputs(w)
+    case = GpuCase(w, inp)
+    gen_s = time.perf_counter() - t_in
+    T, Hq, Hkv, d, K, W = w.total, w.Hq, w.Hkv, w.d, w.K, w.W
+    outs = [torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in case.q_sparse]
+    idx = case.new_idx()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        hs2.hs2_prefill_block(case.dims, case.varlen, case.q_full, case.k, case.v, case.q_sparse,
+                              outs, idx, hs2.HS2_OUT_BF16, case.workspace, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    p50, p99 = float(np.percentile(per_step, 50)), float(np.percentile(per_step, 99))
+
+    # per-kernel launch durations with HIP events on the launch stream
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    sel_ms = timed(lambda: hs2.hs2_select(case.dims, case.varlen, case.q_full, case.k, idx, None,
+                                          case.workspace, stream=stream), args.kernel_reps)
+    sp_ms = timed(lambda: hs2.hs2_sparse_attn(case.dims, case.varlen, case.q_sparse[0], case.k,
+                                              case.v, idx, outs[0], hs2.HS2_OUT_BF16,
+                                              stream=stream), args.kernel_reps)
+    f_sel, b_sp, n_sum = algorithmic_work(w.lengths, Hq, Hkv, d, K, W)
+    sp_gbs = b_sp / (sp_ms * 1e-3) / 1e9
+    sel_tfs = f_sel / (sel_ms * 1e-3) / 1e12
+    value = T / (ms_per_step * 1e-3)
+
+    roofline = {"bound": "hbm", "achieved": round(sp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(sp_gbs / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic("sparse_attn.hip", args.workload),
+                "kernel": "sparse_attn_kernel (one sparse layer)",
+                "algorithmic_bytes_per_launch": b_sp, "avg_launch_ms": round(sp_ms, 4)}
+    select_roof = {"bound": "mfma", "achieved": round(sel_tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                   "unit": "TFLOP/s", "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4),
+                   "algorithmic_flops": f_sel, "avg_call_ms": round(sel_ms, 4),
+                   "note": "whole hs2_select call (scores, top-k, exact-path launches)"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                             else (os.cpu_count() or 1)))
+        cpu = cpu_baseline(inp, w, args.cpu_tokens, threads)
+
+    wl = {"tiny": "B=1 L=1024 Hq=4 Hkv=1 d=128 K=256 W=32, 1 select + 1 sparse layer",
+          "8k": "B=1 L=8192 Hq=32 Hkv=8 d=128 K=1024 W=128, 1 select + 1 sparse layer",
+          "32k": "B=1 L=32768 Hq=32 Hkv=8 d=128 K=1024 W=128, needle keys, 1 select + 3 sparse layers",
+          "128k": "B=1 L=131072 Hq=64 Hkv=8 d=128 K=1024 W=128, needle keys, 1 select + 3 sparse layers",
+          "varlen": f"B=8 lognormal lengths {w.lengths} Hq=32 Hkv=8 d=128 K=1024 W=128, 1 select + 1 sparse layer"}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded bf16 N(0,1) Q/K/V (SplitMix64 + Box-Muller)"
+                + (", needle keys" if w.needles else ""),
+        "config": {"workload": f"{args.workload}: {wl[args.workload]}", "global_batch": len(w.lengths),
+                   "seq_len": max(w.lengths), "tokens": T, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "select": select_roof,
+        "p50_ms": round(p50, 4), "p99_ms": round(p99, 4), "jitter_flag": bool(p99 > 1.3 * p50),
+        "roofline_tokens_per_s": round(T / (f_sel / (MFMA_BF16_PEAK_TFS * 1e12)
+                                            + len(outs) * b_sp / (HBM_PEAK_GBS * 1e9)), 1),
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * hs2.h - C ABI of the token-level sparse attention prefill library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (HySparse2 news summary of the MiMo-V3 architecture; paragraph
+ * on two-level KV sharing, forced-recent paragraph, token-granularity
+ * paragraph, ablation paragraph):
+ *   - a hybrid module is one full-attention layer followed by sparse layers;
+ *     the sparse layers reuse the full layer's KV cache and its token
+ *     selection ("KV Reuse");
+ *   - the full layer's complete attention scores choose the tokens: per query
+ *     token t and KV group g, the K = 1024 best single tokens ("global") plus
+ *     the W = 128 most recent tokens, which are always kept;
+ *   - each sparse layer attends, with its own queries, only to the selected
+ *     positions, renormalising the softmax over them (masking before the
+ *     softmax, SHARP walkthrough section 2.3).
+ *
+ * Exact definitions used by this library (readings where the pages are silent):
+ *   z[t,h,j] = softmax_scale * <q[t,h], k[j,g(h)]>, j <= t, g(h) = h / (Hq/Hkv)
+ *   S[t,g,j] = sum_{h in g} exp(z[t,h,j] - m[t,h]) / l[t,h]
+ *              (m, l: max and sum of exp over all causal keys of head h)
+ *   candidates C_t = [0, t-W]; window W_t = [max(0, t-W+1), t]
+ *   T_t = all of C_t if |C_t| <= K, else the K best by (S desc, position asc)
+ *   I_t = ascending(T_t U W_t): n_t = min(t+1, K+W) entries, then -1 to K+W
+ *   sparse layer: o[t,h] = sum_{j in I_t} softmax_j(scale * <q'[t,h], k[j,g]>) v[j,g]
+ *
+ * Conventions
+ *   - Pointers are device pointers unless the name ends in _host.
+ *   - bf16 tensors are raw 16-bit storage (uint16_t bit patterns).
+ *   - Layouts are contiguous and token-major over the packed varlen batch:
+ *       Q, O   [T, Hq,  head_dim]       K, V   [T, Hkv, head_dim]
+ *       idx    [T, Hkv, top_k + window] int32, local positions (0-based within
+ *              the token's own sequence), ascending, -1 padded.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it: no call synchronises, allocates device memory or
+ *     keeps state between calls, so calls are thread-safe. Inputs must stay
+ *     valid and outputs unread until the stream has passed the call.
+ *   - The caller owns every buffer, including the workspace
+ *     (size from hs2_workspace_size). Workspace contents need no initialisation.
+ *   - Errors: all validation happens before anything is enqueued; on a
+ *     validation error nothing is written. A HIP launch failure returns
+ *     HS2_ERR_HIP (detail from hs2_status_string, per thread).
+ *   - NaN/Inf in the inputs is outside the contract: outputs are then
+ *     unspecified, but idx entries stay in range and no access goes out of
+ *     bounds.
+ */
+#ifndef HS2_H_
+#define HS2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  HS2_OK = 0,
+  HS2_ERR_INVALID_ARG = -1, /* a pointer, size or cu_seqlens entry is invalid */
+  HS2_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim != 128, Hq/Hkv not in {1,2,4,8,16}) */
+  HS2_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than hs2_workspace_size */
+  HS2_ERR_HIP = -4          /* a HIP runtime call failed */
+};
+
+/* Output element type of the sparse attention. */
+enum {
+  HS2_OUT_BF16 = 0, /* bf16 output (round to nearest even); P.V with P as two bf16 parts */
+  HS2_OUT_F32 = 1   /* fp32 output; P.V with P as three bf16 parts (~fp32 precision)
+                       -- the precise mode */
+};
+
+/* Operation selector for hs2_workspace_size. */
+enum { HS2_OP_SELECT = 1, HS2_OP_SPARSE = 2, HS2_OP_PREFILL_BLOCK = 3 };
+
+/* Flags of hs2_dims.flags. */
+enum {
+  /* Skip the sampled threshold: every row with more than top_k candidates is
+     selected by the exact full-row path (slow; results obey the same rule). */
+  HS2_FLAG_EXACT_SELECT = 1u
+};
+
+typedef struct {
+  int32_t num_q_heads;  /* Hq >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv in {1, 2, 4, 8, 16} */
+  int32_t head_dim;     /* must be 128 */
+  int32_t top_k;        /* K >= 0 global tokens per (t, g) */
+  int32_t window;       /* W >= 0 forced recent tokens (includes t itself); K + W >= 1 */
+  float softmax_scale;  /* finite, > 0; usually 1/sqrt(head_dim) */
+  uint32_t flags;       /* HS2_FLAG_* bits, 0 by default */
+} hs2_dims;
+
+typedef struct {
+  int32_t batch;                  /* B >= 0 sequences */
+  const int32_t* cu_seqlens;      /* device [B+1]: cu[0] = 0, non-decreasing */
+  const int32_t* cu_seqlens_host; /* host copy of the same [B+1] */
+  int32_t max_seqlen;             /* >= every L_i and <= HS2_MAX_SEQLEN */
+  int64_t total_tokens;           /* T = cu[B] */
+} hs2_varlen;
+
+#define HS2_MAX_SEQLEN 262144
+
+/*
+ * Bytes of workspace an operation needs for these dimensions.
+ * op: HS2_OP_SELECT, HS2_OP_SPARSE or HS2_OP_PREFILL_BLOCK (n_sparse is unused
+ * by the size). Returns HS2_OK and writes *bytes_out, or a validation error.
+ */
+int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, int n_sparse,
+                       size_t* bytes_out);
+
+/*
+ * Token selection of the full-attention layer (steps: per-head row statistics,
+ * group probability score, top-K outside the window, window forcing, index
+ * assembly). q [T,Hq,128] bf16, k [T,Hkv,128] bf16 in; idx_out [T,Hkv,K+W]
+ * int32 out. kth_score_out (nullable, device [T,Hkv] float): the score S of the
+ * lowest-ranked selected global candidate, or -1 when every candidate was taken.
+ */
+int hs2_select(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+               int32_t* idx_out, float* kth_score_out, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * One sparse attention layer over given index rows: q [T,Hq,128] bf16 (the
+ * layer's own queries), k, v [T,Hkv,128] bf16 (the shared cache), idx
+ * [T,Hkv,K+W] int32. Entries outside [0, t] are ignored; a row with no valid
+ * entry gives a zero output. out [T,Hq,128]: bf16 (HS2_OUT_BF16) or float
+ * (HS2_OUT_F32). Needs no workspace (workspace may be NULL, size 0).
+ */
+int hs2_sparse_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                    const void* v, const int32_t* idx, void* out, int out_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * One hybrid module in prefill: hs2_select on (q_full, k) into idx_out, then
+ * n_sparse sparse layers, layer i reading q_sparse_host_array[i] (device
+ * pointer) and writing out_sparse_host_array[i], all sharing k, v and idx.
+ * The two pointer arrays live on the host and are read during the call.
+ */
+int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void* q_full,
+                      const void* k, const void* v, int n_sparse,
+                      const void* const* q_sparse_host_array, void* const* out_sparse_host_array,
+                      int out_dtype, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Static text for a status; for HS2_ERR_HIP the last HIP error of this thread. */
+const char* hs2_status_string(int status);
+
+/*
+ * Planner query (host only, no GPU needed): the selection work of a varlen
+ * batch is cut into tasks of `rows_per_task` tokens of one sequence, ordered by
+ * decreasing cost (tile index within its sequence, descending; then sequence
+ * ascending). For task index `task` in [0, n_tasks) writes its sequence and
+ * tile index. Returns the number of tasks (>= 0), or a negative status.
+ */
+int64_t hs2_plan_task(const int32_t* cu_seqlens_host, int32_t batch, int32_t rows_per_task,
+                      int64_t task, int32_t* seq_out, int32_t* tile_out);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int hs2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H_ */

@@ -142,8 +142,10 @@ static void row_select(const dims_t* D, const double* S, int64_t t, int32_t* idx
   const int64_t n_cand = t - W + 1 > 0 ? t - W + 1 : 0; /* C_t = [0, t-W] */
   memset(mark, 0, (size_t)(t + 1));
   for (int64_t j = (t - W + 1 > 0 ? t - W + 1 : 0); j <= t; j++) mark[j] = 1; /* W_t */
-  if (n_cand <= K) {
-    for (int64_t j = 0; j < n_cand; j++) mark[j] = 1;
+  if (n_cand <= K || K == 0) {
+    /* all candidates fit in the budget (or the budget is empty) */
+    if (n_cand <= K)
+      for (int64_t j = 0; j < n_cand; j++) mark[j] = 1;
     *kth = -1.0;
   } else {
     for (int64_t j = 0; j < n_cand; j++) { cbuf[j].s = S[j]; cbuf[j].j = j; }
@@ -302,7 +304,8 @@ static int max_len(const dims_t* D) {
 /*
  * Selection (O1..O6). rows: list of row ids t_global*Hkv + g, or NULL for all
  * T*Hkv rows in order. idx_out [n_rows, K+W] int32; kth_out [n_rows] (nullable):
- * the score of the lowest-ranked selected global candidate, -1 when all were taken.
+ * the score of the lowest-ranked selected global candidate, -1 when all were taken
+ * (or when K = 0, so none is).
  */
 int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq, int Hkv,
                 int d, double scale, int K, int W, const int64_t* rows, int64_t n_rows,

@@ -1,0 +1,180 @@
+"""C-ABI contract checks that need no GPU: symbols, validation, workspace sizes, planner.
+
+Validation runs before any HIP call, so every error path here returns without
+touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_sparse_hs2_amd as hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hs2.LIB_PATH):
+        from token_level_sparse_hs2_amd import _build
+        _build.build()
+    return hs2.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hs2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"hs2_select", "hs2_sparse_attn", "hs2_prefill_block", "hs2_workspace_size",
+            "hs2_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert hs2.hs2_version() >= 10000
+
+
+class FakeDev:
+    """Stands in for a device tensor: only its address is used (never dereferenced)."""
+
+    def __init__(self, addr=0x1000):
+        self.addr = addr
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return 1 << 40
+
+    def element_size(self):
+        return 1
+
+
+def varlen(lengths, max_seqlen=None):
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    return hs2.VarlenArgs(FakeDev(0x2000), cu, max_seqlen)
+
+
+def call_select(d, v, ws=FakeDev(), q=FakeDev(), k=FakeDev(), idx=FakeDev()):
+    return hs2.load_library().hs2_select(ctypes.byref(d), ctypes.byref(v.struct), hs2._ptr(q),
+                                         hs2._ptr(k), hs2._ptr(idx), 0, hs2._ptr(ws),
+                                         ws.numel() if ws is not None else 0, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=1024, window=128, head_dim=64), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(num_q_heads=24, num_kv_heads=8, top_k=1024, window=128), hs2.HS2_ERR_UNSUPPORTED),  # G = 3
+    (dict(num_q_heads=30, num_kv_heads=8, top_k=1024, window=128), hs2.HS2_ERR_INVALID_ARG),  # Hq % Hkv
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=-1, window=128), hs2.HS2_ERR_INVALID_ARG),
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=4, window=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=0, window=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=8, window=8, softmax_scale=float("nan")), hs2.HS2_ERR_INVALID_ARG),
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=8, window=8, softmax_scale=-1.0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(num_q_heads=32, num_kv_heads=8, top_k=8, window=8, flags=6), hs2.HS2_ERR_INVALID_ARG),
+    (dict(num_q_heads=0, num_kv_heads=8, top_k=8, window=8), hs2.HS2_ERR_INVALID_ARG),
+])
+def test_dims_validation(lib, kw, status):
+    d = hs2.make_dims(**kw)
+    assert call_select(d, varlen([100])) == status
+
+
+def test_varlen_validation(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    v = varlen([100, 50])
+    v._host[2] = 10  # decreasing
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([100, 50])
+    v.struct.total_tokens = 151  # total != cu[B]
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([100, 50])
+    v._host[0] = 1
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([100, 50], max_seqlen=99)  # below the longest sequence
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([100], max_seqlen=hs2.HS2_MAX_SEQLEN + 1)
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([100])
+    v.struct.cu_seqlens = None
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([100])
+    v.struct.batch = -1
+    assert call_select(d, v) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_null_pointers_and_workspace(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    v = varlen([5000])
+    assert call_select(d, v, q=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call_select(d, v, idx=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call_select(d, v, ws=None) == hs2.HS2_ERR_WORKSPACE
+    need = hs2.hs2_workspace_size(d, v, hs2.HS2_OP_SELECT)
+    small = FakeDev()
+    small.numel = lambda: need - 1
+    assert call_select(d, v, ws=small) == hs2.HS2_ERR_WORKSPACE
+    L = hs2.load_library()
+    # sparse: bad dtype, null output
+    r = L.hs2_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, 1, 7, None, 0, None)
+    assert r == hs2.HS2_ERR_INVALID_ARG
+    r = L.hs2_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, None, 0, None, 0, None)
+    assert r == hs2.HS2_ERR_INVALID_ARG
+    # prefill block: negative layer count, null layer pointer
+    arr = (ctypes.c_void_p * 1)(None)
+    r = L.hs2_prefill_block(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, -1, arr, arr, 0, 1,
+                            1, 1 << 40, None)
+    assert r == hs2.HS2_ERR_INVALID_ARG
+    r = L.hs2_prefill_block(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, arr, arr, 0, 1,
+                            1, 1 << 40, None)
+    assert r == hs2.HS2_ERR_INVALID_ARG
+    assert "workspace" in hs2.hs2_status_string(hs2.HS2_ERR_WORKSPACE)
+
+
+def test_empty_batch_is_a_noop(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    v = hs2.VarlenArgs(FakeDev(0), [0])
+    assert hs2.hs2_workspace_size(d, v, hs2.HS2_OP_SELECT) == 0
+    assert call_select(d, v, q=None, k=None, idx=None, ws=None) == hs2.HS2_OK
+    v = varlen([0, 0])  # zero-length sequences only
+    assert call_select(d, v, q=None, k=None, idx=None, ws=None) == hs2.HS2_OK
+
+
+def test_workspace_sizes_are_bounded(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    for lengths in ([1024], [32768], [131072], [196608, 4096, 50000]):
+        n = hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_PREFILL_BLOCK)
+        assert 0 < n < 6 * (1 << 30)
+        assert hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_SPARSE) == 0
+
+
+@pytest.mark.parametrize("lengths,tok", [
+    ([1], 64), ([64], 64), ([65], 64), ([1000, 1, 130, 64, 0, 5000], 64), ([300, 7, 129], 32),
+    ([17, 17, 17], 16),
+])
+def test_planner_covers_every_tile_once_longest_first(lib, lengths, tok):
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    n, _, _ = hs2.hs2_plan_task(cu, tok, -1)
+    assert n == sum((L + tok - 1) // tok for L in lengths)
+    seen = []
+    for task in range(n):
+        _, s, t = hs2.hs2_plan_task(cu, tok, task)
+        assert 0 <= s < len(lengths) and 0 <= t * tok < lengths[s]
+        seen.append((s, t))
+    assert len(set(seen)) == n
+    tiles = [t for _, t in seen]
+    assert tiles == sorted(tiles, reverse=True)  # tile index (cost) never increases
+    for a, b in zip(seen, seen[1:]):
+        if a[1] == b[1]:
+            assert a[0] < b[0]
+
+
+def test_tokens_per_task_matches_kernel_geometry():
+    assert [hs2.tokens_per_task(g) for g in (1, 2, 4, 8, 16)] == [64, 64, 64, 32, 16]

@@ -1,0 +1,333 @@
+// hs2_api.cpp - the C ABI (include/hs2.h): validation, workspace layout,
+// chunking of the selection work, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "hs2.h"
+#include "hs2_internal.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "no HIP error recorded";
+
+int hip_fail(hipError_t e, const char* what) {
+  std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return HS2_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Geometry {
+  int G = 0, tok = 0;
+  int64_t T = 0;
+  int B = 0;
+  int max_len = 0;      // longest sequence
+  int max_tiles = 0;    // tiles of the longest sequence
+  int64_t n_tasks = 0;  // (sequence, tile) pairs
+  int cand_cap = 0;
+  int64_t tasks_per_chunk = 0;
+  int64_t rows_per_chunk = 0;
+  int bitmap_words = 0;
+  // workspace offsets
+  size_t off_lse = 0, off_cand = 0, off_count = 0, off_flags = 0, off_nflag = 0, off_dense = 0;
+  size_t select_bytes = 0;
+  size_t topk_lds = 0;
+};
+
+bool g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
+  if (!d || !v) return HS2_ERR_INVALID_ARG;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads)
+    return HS2_ERR_INVALID_ARG;
+  if (d->top_k < 0 || d->window < 0 || (int64_t)d->top_k + d->window < 1 ||
+      (int64_t)d->top_k + d->window > (1 << 24))
+    return HS2_ERR_INVALID_ARG;
+  if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return HS2_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)HS2_FLAG_EXACT_SELECT) return HS2_ERR_INVALID_ARG;
+  if (v->batch < 0) return HS2_ERR_INVALID_ARG;
+  if (d->head_dim != hs2::kHeadDim) return HS2_ERR_UNSUPPORTED;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (!g_supported(G)) return HS2_ERR_UNSUPPORTED;
+  geo->G = G;
+  geo->tok = hs2::tokens_per_task(G);
+  geo->B = v->batch;
+  if (v->batch == 0) {
+    if (v->total_tokens != 0) return HS2_ERR_INVALID_ARG;
+    geo->T = 0;
+    return HS2_OK;
+  }
+  if (!v->cu_seqlens || !v->cu_seqlens_host) return HS2_ERR_INVALID_ARG;
+  const int32_t* cu = v->cu_seqlens_host;
+  if (cu[0] != 0) return HS2_ERR_INVALID_ARG;
+  int max_len = 0;
+  int64_t n_tasks = 0;
+  for (int i = 0; i < v->batch; i++) {
+    if (cu[i + 1] < cu[i]) return HS2_ERR_INVALID_ARG;
+    const int L = cu[i + 1] - cu[i];
+    max_len = std::max(max_len, L);
+    n_tasks += hs2::ceil_div(L, geo->tok);
+  }
+  if ((int64_t)cu[v->batch] != v->total_tokens) return HS2_ERR_INVALID_ARG;
+  if (v->max_seqlen < max_len || v->max_seqlen > HS2_MAX_SEQLEN) return HS2_ERR_INVALID_ARG;
+  geo->T = v->total_tokens;
+  geo->max_len = max_len;
+  geo->max_tiles = std::max(1, hs2::ceil_div(max_len, geo->tok));
+  geo->n_tasks = n_tasks;
+
+  // candidate rows: C slots each; chunks of whole tasks under the byte budget
+  const int K = d->top_k;
+  int64_t cap = std::max<int64_t>(hs2::kMinCandCap, 4LL * K);
+  cap = (cap + 63) / 64 * 64;
+  geo->cand_cap = (int)cap;
+  const int64_t rows_per_task = (int64_t)d->num_kv_heads * geo->tok;
+  const int64_t row_bytes = cap * 8;
+  int64_t tpc = hs2::kCandBudgetBytes / (rows_per_task * row_bytes);
+  tpc = std::max<int64_t>(1, std::min<int64_t>(tpc, std::max<int64_t>(1, n_tasks)));
+  geo->tasks_per_chunk = tpc;
+  geo->rows_per_chunk = tpc * rows_per_task;
+  geo->bitmap_words = hs2::ceil_div(std::max(1, max_len), 32);
+
+  size_t off = 0;
+  geo->off_lse = off;
+  off = align_up(off + (size_t)geo->T * d->num_q_heads * sizeof(float));
+  geo->off_cand = off;
+  off = align_up(off + (size_t)geo->rows_per_chunk * cap * sizeof(uint64_t));
+  geo->off_count = off;
+  off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
+  geo->off_flags = off;
+  off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
+  geo->off_nflag = off;
+  off = align_up(off + sizeof(int32_t));
+  geo->off_dense = off;
+  off = align_up(off + (size_t)hs2::kFallbackBlocks * std::max(1, max_len) * sizeof(uint32_t));
+  geo->select_bytes = off;
+  const size_t key_words = std::max<size_t>((size_t)cap, 16 * hs2::kHeadDim);
+  geo->topk_lds = (256 + 16 + 2 * (size_t)geo->bitmap_words + key_words) * sizeof(uint32_t);
+  return HS2_OK;
+}
+
+int check_workspace(const Geometry& geo, void* ws, size_t bytes) {
+  if (geo.select_bytes == 0) return HS2_OK;
+  if (!ws || bytes < geo.select_bytes) return HS2_ERR_WORKSPACE;
+  return HS2_OK;
+}
+
+float scale_log2(const hs2_dims* d) { return d->softmax_scale * 1.4426950408889634f; }
+
+int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
+               const void* k, int32_t* idx_out, float* kth_out, void* ws, hipStream_t s) {
+  if (geo.T == 0) return HS2_OK;
+  char* w = static_cast<char*>(ws);
+  float* lse2 = reinterpret_cast<float*>(w + geo.off_lse);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(w + geo.off_cand);
+  int32_t* count = reinterpret_cast<int32_t*>(w + geo.off_count);
+  int32_t* flags = reinterpret_cast<int32_t*>(w + geo.off_flags);
+  int32_t* nflag = reinterpret_cast<int32_t*>(w + geo.off_nflag);
+  uint32_t* dense = reinterpret_cast<uint32_t*>(w + geo.off_dense);
+
+  const int G = geo.G;
+  const float gk = (float)G / (float)std::max(1, d->top_k);
+  uint32_t gk_bits;
+  std::memcpy(&gk_bits, &gk, 4);
+
+  hs2::ScoreParams sp{};
+  sp.q = static_cast<const uint16_t*>(q);
+  sp.k = static_cast<const uint16_t*>(k);
+  sp.cu = v->cu_seqlens;
+  sp.B = v->batch;
+  sp.Hq = d->num_q_heads;
+  sp.Hkv = d->num_kv_heads;
+  sp.K = d->top_k;
+  sp.W = d->window;
+  sp.max_tiles = geo.max_tiles;
+  sp.c = scale_log2(d);
+  sp.bin_base = (int)(gk_bits >> 20) - (hs2::kBins - 1);
+  sp.cand_cap = geo.cand_cap;
+  sp.flags = d->flags;
+  sp.lse2 = lse2;
+  sp.cand = cand;
+  sp.cand_count = count;
+  sp.flag_list = flags;
+  sp.flag_count = nflag;
+
+  hs2::TopkParams tp{};
+  tp.cu = v->cu_seqlens;
+  tp.B = v->batch;
+  tp.Hq = d->num_q_heads;
+  tp.Hkv = d->num_kv_heads;
+  tp.K = d->top_k;
+  tp.W = d->window;
+  tp.max_tiles = geo.max_tiles;
+  tp.tok = geo.tok;
+  tp.cand_cap = geo.cand_cap;
+  tp.bitmap_words = geo.bitmap_words;
+  tp.c = sp.c;
+  tp.cand = cand;
+  tp.cand_count = count;
+  tp.flag_list = flags;
+  tp.flag_count = nflag;
+  tp.q = sp.q;
+  tp.k = sp.k;
+  tp.lse2 = lse2;
+  tp.dense = dense;
+  tp.max_seqlen = std::max(1, geo.max_len);
+  tp.idx = idx_out;
+  tp.kth = kth_out;
+
+  for (int64_t t0 = 0; t0 < geo.n_tasks; t0 += geo.tasks_per_chunk) {
+    const int64_t nt = std::min(geo.tasks_per_chunk, geo.n_tasks - t0);
+    const int64_t blocks = nt * d->num_kv_heads;
+    const int64_t rows = blocks * geo.tok;
+    if (blocks > 0x7FFFFFFF || rows > 0x7FFFFFFF) return HS2_ERR_UNSUPPORTED;
+    sp.task_begin = t0;
+    tp.task_begin = t0;
+    hipError_t e = hs2::launch_zero_i32(nflag, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "zero flag counter");
+    e = hs2::launch_scores(G, sp, (int)blocks, s);
+    if (e != hipSuccess) return hip_fail(e, "scores kernel");
+    e = hs2::launch_topk(G, tp, (int)rows, geo.topk_lds, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+    e = hs2::launch_fallback(G, tp, geo.topk_lds, s);
+    if (e != hipSuccess) return hip_fail(e, "exact-select kernel");
+  }
+  return HS2_OK;
+}
+
+int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
+               const void* k, const void* vv, const int32_t* idx, void* out, int out_dtype,
+               hipStream_t s) {
+  if (geo.T == 0) return HS2_OK;
+  hs2::SparseParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(vv);
+  p.idx = idx;
+  p.cu = v->cu_seqlens;
+  p.B = v->batch;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.KW = d->top_k + d->window;
+  p.T = geo.T;
+  p.c = scale_log2(d);
+  p.out = out;
+  hipError_t e = hs2::launch_sparse(geo.G, out_dtype == HS2_OUT_F32, p, s);
+  if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs2_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char* hs2_status_string(int status) {
+  switch (status) {
+    case HS2_OK: return "ok";
+    case HS2_ERR_INVALID_ARG: return "invalid argument";
+    case HS2_ERR_UNSUPPORTED: return "unsupported configuration (head_dim must be 128, Hq/Hkv in {1,2,4,8,16})";
+    case HS2_ERR_WORKSPACE: return "workspace missing or too small";
+    case HS2_ERR_HIP: return g_hip_msg;
+    default: return "unknown status";
+  }
+}
+
+int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, int n_sparse,
+                       size_t* bytes_out) {
+  (void)n_sparse;
+  if (!bytes_out) return HS2_ERR_INVALID_ARG;
+  if (op != HS2_OP_SELECT && op != HS2_OP_SPARSE && op != HS2_OP_PREFILL_BLOCK)
+    return HS2_ERR_INVALID_ARG;
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  *bytes_out = (op == HS2_OP_SPARSE || geo.T == 0) ? 0 : geo.select_bytes;
+  return HS2_OK;
+}
+
+int hs2_select(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+               int32_t* idx_out, float* kth_score_out, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (geo.T == 0) return HS2_OK;
+  if (!q || !k || !idx_out) return HS2_ERR_INVALID_ARG;
+  st = check_workspace(geo, workspace, workspace_bytes);
+  if (st != HS2_OK) return st;
+  return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+int hs2_sparse_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                    const void* v, const int32_t* idx, void* out, int out_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (geo.T == 0) return HS2_OK;
+  if (!q || !k || !v || !idx || !out) return HS2_ERR_INVALID_ARG;
+  return run_sparse(dims, varlen, geo, q, k, v, idx, out, out_dtype,
+                    static_cast<hipStream_t>(stream));
+}
+
+int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void* q_full,
+                      const void* k, const void* v, int n_sparse,
+                      const void* const* q_sparse_host_array, void* const* out_sparse_host_array,
+                      int out_dtype, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (n_sparse < 0) return HS2_ERR_INVALID_ARG;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (geo.T == 0) return HS2_OK;
+  if (!q_full || !k || !v || !idx_out) return HS2_ERR_INVALID_ARG;
+  if (n_sparse > 0 && (!q_sparse_host_array || !out_sparse_host_array)) return HS2_ERR_INVALID_ARG;
+  for (int i = 0; i < n_sparse; i++)
+    if (!q_sparse_host_array[i] || !out_sparse_host_array[i]) return HS2_ERR_INVALID_ARG;
+  st = check_workspace(geo, workspace, workspace_bytes);
+  if (st != HS2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_select(dims, varlen, geo, q_full, k, idx_out, nullptr, workspace, s);
+  if (st != HS2_OK) return st;
+  for (int i = 0; i < n_sparse; i++) {
+    st = run_sparse(dims, varlen, geo, q_sparse_host_array[i], k, v, idx_out,
+                    out_sparse_host_array[i], out_dtype, s);
+    if (st != HS2_OK) return st;
+  }
+  return HS2_OK;
+}
+
+int64_t hs2_plan_task(const int32_t* cu_seqlens_host, int32_t batch, int32_t rows_per_task,
+                      int64_t task, int32_t* seq_out, int32_t* tile_out) {
+  if (!cu_seqlens_host || batch < 0 || rows_per_task < 1) return HS2_ERR_INVALID_ARG;
+  if (batch > 0 && cu_seqlens_host[0] != 0) return HS2_ERR_INVALID_ARG;
+  int64_t n_tasks = 0;
+  int max_len = 0;
+  for (int i = 0; i < batch; i++) {
+    if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return HS2_ERR_INVALID_ARG;
+    const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+    max_len = std::max(max_len, L);
+    n_tasks += hs2::ceil_div(L, rows_per_task);
+  }
+  if (task >= 0 && task < n_tasks) {
+    int seq = 0, tile = 0;
+    hs2::plan_decode(cu_seqlens_host, batch, rows_per_task,
+                     std::max(1, hs2::ceil_div(max_len, rows_per_task)), task, &seq, &tile);
+    if (seq_out) *seq_out = seq;
+    if (tile_out) *tile_out = tile;
+  }
+  return n_tasks;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// hs2_internal.h - internals shared by the host planner and the gfx950 kernels
+// of the token-level sparse attention library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+// ---------------------------------------------------------------------------
+// Fixed shapes and tuning constants
+// ---------------------------------------------------------------------------
+constexpr int kHeadDim = 128;   // d (the only supported head size)
+constexpr int kKeyTile = 64;    // keys per LDS tile in the selection sweeps
+constexpr int kSampleStride = 8;  // sample sweep visits key tiles 0, 8, 16, ...
+constexpr int kBins = 256;        // histogram bins per row (8 per octave of S)
+constexpr int kSelThreads = 256;  // threads of every selection workgroup
+constexpr int kMinCandCap = 4096; // candidate slots per row (at least)
+constexpr int64_t kCandBudgetBytes = 4LL << 30;  // candidate buffer cap per chunk
+constexpr int kFallbackBlocks = 256;             // persistent grid of the exact path
+// sampled threshold: rank r = ceil(kTauAlpha * K * n_sample / n_cand) + kTauBeta
+constexpr float kTauAlpha = 1.5f;
+constexpr int kTauBeta = 32;
+
+// MFMA rows per wave = 16 * row tiles; tokens per selection workgroup.
+__host__ __device__ constexpr int row_tiles(int G) { return G >= 4 ? 4 : G; }
+__host__ __device__ constexpr int tokens_per_task(int G) { return 64 * row_tiles(G) / G; }
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Varlen task order (host and device): tasks are (sequence, tile of `tok`
+// tokens). Tiles further into a sequence cost more (more causal keys), so the
+// order is tile index descending, then sequence ascending: a greedy
+// longest-first assignment when the hardware dispatches workgroups in order.
+// P(q) = number of tasks with tile index > q = sum_i max(0, n_i - q - 1).
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int64_t plan_tasks_above(const int32_t* cu, int B, int tok, int q) {
+  int64_t s = 0;
+  for (int i = 0; i < B; i++) {
+    int n = ceil_div(cu[i + 1] - cu[i], tok);
+    if (n - q - 1 > 0) s += n - q - 1;
+  }
+  return s;
+}
+
+__host__ __device__ inline void plan_decode(const int32_t* cu, int B, int tok, int max_tiles,
+                                            int64_t task, int* seq, int* tile) {
+  int lo = 0, hi = max_tiles - 1;  // smallest q with P(q) <= task
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (plan_tasks_above(cu, B, tok, mid) <= task) hi = mid; else lo = mid + 1;
+  }
+  int q = lo;
+  int64_t r = task - plan_tasks_above(cu, B, tok, q);
+  int s = 0;
+  for (int i = 0; i < B; i++) {
+    int n = ceil_div(cu[i + 1] - cu[i], tok);
+    if (n > q) {
+      if (r == 0) { s = i; break; }
+      r--;
+    }
+  }
+  *seq = s;
+  *tile = q;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks
+// ---------------------------------------------------------------------------
+struct ScoreParams {
+  const uint16_t* q;    // [T, Hq, 128] bf16
+  const uint16_t* k;    // [T, Hkv, 128] bf16
+  const int32_t* cu;    // [B+1]
+  int B, Hq, Hkv, K, W;
+  int max_tiles;        // tiles of the longest sequence
+  int64_t task_begin;   // first task of this chunk
+  float c;              // softmax_scale * log2(e)
+  int bin_base;         // (bits(G/K) >> 20) - (kBins - 1)
+  int cand_cap;         // C
+  uint32_t flags;
+  float* lse2;          // [T, Hq] log2-domain log-sum-exp of each full-layer row
+  uint64_t* cand;       // [chunk rows, C]: (S bits << 32) | position
+  int32_t* cand_count;  // [chunk rows]: count, or -1 = exact path
+  int32_t* flag_list;   // [chunk rows]: slots sent to the exact path
+  int32_t* flag_count;  // [1]
+};
+
+struct TopkParams {
+  const int32_t* cu;
+  int B, Hq, Hkv, K, W;
+  int max_tiles;
+  int64_t task_begin;
+  int tok;              // tokens per task
+  int cand_cap;
+  int bitmap_words;     // words per bitmap in LDS (covers max_seqlen)
+  float c;
+  const uint64_t* cand;
+  const int32_t* cand_count;
+  const int32_t* flag_list;
+  const int32_t* flag_count;
+  // exact path
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* lse2;
+  uint32_t* dense;      // [kFallbackBlocks, max_seqlen] S bits
+  int max_seqlen;
+  // outputs
+  int32_t* idx;         // [T, Hkv, K+W]
+  float* kth;           // [T, Hkv] or null
+};
+
+struct SparseParams {
+  const uint16_t* q;    // [T, Hq, 128]
+  const uint16_t* k;    // [T, Hkv, 128]
+  const uint16_t* v;
+  const int32_t* idx;   // [T, Hkv, KW]
+  const int32_t* cu;
+  int B, Hq, Hkv, KW;
+  int64_t T;
+  float c;              // softmax_scale * log2(e)
+  void* out;            // [T, Hq, 128] bf16 or f32
+};
+
+// launchers (defined in the .hip files)
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_topk(int G, const TopkParams& p, int n_rows, size_t lds_bytes, hipStream_t s);
+hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
+hipError_t launch_sparse(int G, bool precise, const SparseParams& p, hipStream_t s);
+
+}  // namespace hs2
