@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (known bytes) for counter scaling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -166,6 +168,12 @@ def main():
                    "unit": "TFLOP/s", "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4),
                    "algorithmic_flops": f_sel, "avg_call_ms": round(sel_ms, 4),
                    "note": "whole hs2_select call (scores, top-k, exact-path launches)"}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:

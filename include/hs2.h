@@ -58,7 +58,8 @@ extern "C" {
 enum {
   HS2_OK = 0,
   HS2_ERR_INVALID_ARG = -1, /* a pointer, size or cu_seqlens entry is invalid */
-  HS2_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim != 128, Hq/Hkv not in {1,2,4,8,16}) */
+  HS2_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim != 128, Hq/Hkv not in
+                               {1,2,4,8,16}, or one sequence's K (L * Hkv * 256 bytes) >= 4 GiB */
   HS2_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than hs2_workspace_size */
   HS2_ERR_HIP = -4          /* a HIP runtime call failed */
 };

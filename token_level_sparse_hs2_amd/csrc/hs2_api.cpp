@@ -75,6 +75,8 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   }
   if ((int64_t)cu[v->batch] != v->total_tokens) return HS2_ERR_INVALID_ARG;
   if (v->max_seqlen < max_len || v->max_seqlen > HS2_MAX_SEQLEN) return HS2_ERR_INVALID_ARG;
+  // kernels address K/V rows within one sequence with 32-bit byte offsets
+  if ((int64_t)max_len * d->num_kv_heads * hs2::kHeadDim * 2 >= (1LL << 32)) return HS2_ERR_UNSUPPORTED;
   geo->T = v->total_tokens;
   geo->max_len = max_len;
   geo->max_tiles = std::max(1, hs2::ceil_div(max_len, geo->tok));

@@ -24,8 +24,9 @@ namespace hs2 {
 constexpr int kChunk = 32;  // index entries per step
 
 template <int G, bool PRECISE>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(SparseParams p) {
-  __shared__ uint4 vlds[4][kChunk][16];  // per wave: 32 keys x 256 B, swizzled 16-byte chunks
+__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
+  __shared__ uint4 klds[4][kChunk][16];  // per wave: 32 K rows x 256 B, swizzled 16-byte chunks
+  __shared__ uint4 vlds[4][kChunk][16];  // per wave: 32 V rows
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int lq = l >> 4, lc = l & 15;
   const int Hkv = p.Hkv, Hq = p.Hq, KW = p.KW;
@@ -53,131 +54,165 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseParams p) {
 #pragma unroll
   for (int i = 0; i < 8; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* kb = p.k + (size_t)g * kHeadDim;
-  const uint16_t* vb = p.v + (size_t)g * kHeadDim;
+  // this sequence's K/V rows of group g; row j starts at byte j * row_stride
+  const char* kseq = reinterpret_cast<const char*>(p.k + ((size_t)base * Hkv + g) * kHeadDim);
+  const char* vseq = reinterpret_cast<const char*>(p.v + ((size_t)base * Hkv + g) * kHeadDim);
+  const uint32_t row_stride = (uint32_t)Hkv * kHeadDim * 2;
   uint4(*vl)[16] = vlds[w];
+  const int n_chunks = (KW + kChunk - 1) / kChunk;
 
-  for (int c0 = 0; c0 < KW; c0 += kChunk) {
-    // index entries for the lane's two A rows
-    int j0 = -1, j1 = -1;
-    if (c0 + lc < KW) j0 = irow[c0 + lc];
-    if (c0 + 16 + lc < KW) j1 = irow[c0 + 16 + lc];
-    const bool ok0 = (j0 >= 0) && (j0 <= t), ok1 = (j1 >= 0) && (j1 <= t);
-    const uint64_t bal0 = __ballot(ok0), bal1 = __ballot(ok1);
-    if ((bal0 | bal1) == 0) continue;
-    const size_t r0 = (size_t)(base + (ok0 ? j0 : 0)) * Hkv * kHeadDim;
-    const size_t r1 = (size_t)(base + (ok1 ? j1 : 0)) * Hkv * kHeadDim;
-
-    // gather K rows into A operands and V rows into LDS
-    bf16x8 ka[2][4];
-    uint4 vr[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      ka[0][ks] = as_bf16x8(to_u32x4(ldg128(kb + r0 + 32 * ks + 8 * lq)));
-      ka[1][ks] = as_bf16x8(to_u32x4(ldg128(kb + r1 + 32 * ks + 8 * lq)));
-      vr[0][ks] = ldg128(vb + r0 + 32 * ks + 8 * lq);
-      vr[1][ks] = ldg128(vb + r1 + 32 * ks + 8 * lq);
-    }
-    wave_lds_fence();  // previous chunk's reads of vl are done
+  // index entries of chunk c for the lane's two A rows (keys 16*mt + lc)
+  auto load_idx = [&](int c, int (&j)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-      const int key = 16 * mt + lc;
-      const int swz = 2 * ((key >> 2) & 3);
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) vl[key][(4 * ks + lq) ^ swz] = vr[mt][ks];
+      const int e = c * kChunk + 16 * mt + lc;
+      j[mt] = (c < n_chunks && e < KW) ? irow[e] : -1;
     }
+  };
+  // gather the chunk's K and V rows, fully coalesced: load r covers keys
+  // 4r .. 4r+3, 16 lanes per 256-byte row (lane: key 4r + lq, 16-byte chunk lc)
+  struct Gather {
+    uint4 kr[8];
+    uint4 vr[8];
+  };
+  auto gather = [&](const int (&j)[2], Gather& gb) {
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const int key = 4 * r + lq;  // entry of the chunk; its index is held by lane (key & 15)
+      const int jj = __shfl(j[key >> 4], key & 15, 64);
+      const bool ok = jj >= 0 && jj <= t;
+      const uint32_t off = (uint32_t)(ok ? jj : 0) * row_stride + 16u * lc;
+      gb.kr[r] = ldg128(kseq + off);
+      gb.vr[r] = ldg128(vseq + off);
+    }
+  };
+  uint4(*kl)[16] = klds[w];
 
-    // scores S^T (keys x heads)
+  constexpr int NSPLIT = PRECISE ? 3 : 2;
+  constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
+
+  auto consume = [&](const int (&j)[2], const Gather& gb) {
+    const bool ok0 = j[0] >= 0 && j[0] <= t, ok1 = j[1] >= 0 && j[1] <= t;
+    const uint64_t bal0 = __ballot(ok0), bal1 = __ballot(ok1);
+    if ((bal0 | bal1) == 0) return;
+    const bool full = (bal0 & bal1) == ~0ull;
+    wave_lds_fence();  // previous chunk's reads of kl / vl are done
+    // rows into LDS. K: 16-byte chunk ch of key r at physical chunk ch ^ (r & 15);
+    // V: at ch ^ (2 * (r & 7)) (suits the transposing reads below)
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const int key = 4 * r + lq;
+      kl[key][lc ^ (key & 15)] = gb.kr[r];
+      vl[key][lc ^ (2 * (key & 7))] = gb.vr[r];
+    }
+    wave_lds_fence();
+    // raw scores S^T (keys x heads); lane: head lc, keys 16*mt + 4*lq + i
     f32x4 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = 16 * mt + lc;
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) s[mt] = mfma16x16x32(ka[mt][ks], qb[ks], s[mt]);
-    }
-    // entry 16*mt + 4*lq + i is valid iff bit (4*lq + i) of the ballot
-    float v2[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      const uint64_t bal = mt ? bal1 : bal0;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const bool ok = (bal >> (4 * lq + i)) & 1ull;
-        v2[mt][i] = ok ? s[mt][i] * c : -INFINITY;
-        mx = fmaxf(mx, v2[mt][i]);
+      for (int ks = 0; ks < 4; ks++) {
+        const bf16x8 ka = as_bf16x8(to_u32x4(kl[key][(4 * ks + lq) ^ (key & 15)]));
+        s[mt] = mfma16x16x32(ka, qb[ks], s[mt]);
       }
     }
+    if (!full) {  // entry 16*mt + 4*lq + i is valid iff bit (4*lq + i) of the ballot
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        const uint64_t bal = mt ? bal1 : bal0;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (!((bal >> (4 * lq + i)) & 1ull)) s[mt][i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m, mx);  // finite: the chunk has a valid entry
-    const float alpha = fast_exp2(m - m_new);
-    float pv[2][4];
+    mx *= c;  // finite: the chunk has a valid entry
+    // the reference m only moves when a score passes it by the slack (never
+    // overflows: terms stay below 2^slack); moving it rescales l and O
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; i++) o[i] *= alpha;
+      m = m_new;
+    }
+    float pv[8];
     float psum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        pv[mt][i] = fast_exp2(v2[mt][i] - m_new);
-        psum += pv[mt][i];
-      }
-    lsum = lsum * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int i = 0; i < 8; i++) o[i] *= alpha;
+    for (int sidx = 0; sidx < 8; sidx++) {
+      pv[sidx] = fast_exp2(fmaf(s[sidx >> 2][sidx & 3], c, -m));
+      psum += pv[sidx];
+    }
+    lsum += psum;
 
     // P^T operand (B): column = head, k slot s <-> key (s < 4 ? 4lq + s : 16 + 4lq + s - 4).
     // P is split into bf16 parts p = p0 + p1 (+ p2 in the precise mode), each the
     // bf16 rounding of what the previous parts leave, so P.V keeps ~16 (~24)
     // mantissa bits of P; V is bf16 already, so every product is exact.
-    constexpr int NSPLIT = PRECISE ? 3 : 2;
     bf16x8 pb[NSPLIT];
-    {
-      float rem[8];
 #pragma unroll
-      for (int sidx = 0; sidx < 8; sidx++) rem[sidx] = pv[sidx >> 2][sidx & 3];
+    for (int part = 0; part < NSPLIT; part++) {
+      u32x4 pk;
 #pragma unroll
-      for (int part = 0; part < NSPLIT; part++) {
-        u32x4 pk;
+      for (int u = 0; u < 4; u++) pk[u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
+      pb[part] = as_bf16x8(pk);
+      if (part + 1 < NSPLIT) {
 #pragma unroll
-        for (int u = 0; u < 4; u++) pk[u] = pack_bf16x2(rem[2 * u], rem[2 * u + 1]);
-        pb[part] = as_bf16x8(pk);
-        if (part + 1 < NSPLIT) {
-#pragma unroll
-          for (int u = 0; u < 4; u++) {
-            rem[2 * u] -= bf16_bits_to_f32(pk[u] & 0xFFFFu);
-            rem[2 * u + 1] -= bf16_bits_to_f32(pk[u] >> 16);
-          }
+        for (int u = 0; u < 4; u++) {
+          pv[2 * u] -= bf16_bits_to_f32(pk[u] & 0xFFFFu);
+          pv[2 * u + 1] -= __uint_as_float(pk[u] & 0xFFFF0000u);
         }
       }
     }
 
-    wave_lds_fence();  // this chunk's V rows are in LDS
-    // V^T operand (A): row d = 16*dt + lc, k slot s <-> key as above
-    const uint16_t* vls = reinterpret_cast<const uint16_t*>(&vl[0][0]);
+    // V^T operand (A): row d = 16*dt + lc, k slots 4h..4h+3 <-> keys 16h + 4lq + e.
+    // One transposing LDS read per half: within each 16-lane group, lane i gets
+    // element (i & 3) of the 8-byte pieces read by lanes (i >> 2) + 4e, so lane j
+    // reads key 16h + 4lq + (j >> 2), d = 16dt + 4(j & 3) .. +3.
+    const int key_lo = 4 * lq + (lc >> 2);
+    const int dsub = 4 * (lc & 3);
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
-      const int d = 16 * dt + lc;
-      const int ch = d >> 3, within = d & 7;
-      uint32_t a[4];
+      typedef short i16x4 __attribute__((ext_vector_type(4)));
+      uint2 hv[2];
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        uint32_t pair[2];
-#pragma unroll
-        for (int e = 0; e < 2; e++) {
-          const int sidx = 2 * u + e;
-          const int key = sidx < 4 ? 4 * lq + sidx : 16 + 4 * lq + (sidx - 4);
-          const int swz = 2 * ((key >> 2) & 3);
-          pair[e] = vls[(key * 16 + (ch ^ swz)) * 8 + within];
-        }
-        a[u] = pair[0] | (pair[1] << 16);
+      for (int h = 0; h < 2; h++) {
+        const int key = 16 * h + key_lo;
+        const int d0 = 16 * dt + dsub;
+        const int phys = (d0 >> 3) ^ (2 * (key & 7));
+        const short* src = reinterpret_cast<const short*>(&vl[key][phys]) + (d0 & 7);
+        hv[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                              (i16x4 __attribute__((address_space(3)))*)(src)));
       }
-      u32x4 av;
-      av[0] = a[0]; av[1] = a[1]; av[2] = a[2]; av[3] = a[3];
+      const u32x4 av = {hv[0].x, hv[0].y, hv[1].x, hv[1].y};
       const bf16x8 va = as_bf16x8(av);
 #pragma unroll
       for (int part = 0; part < NSPLIT; part++) o[dt] = mfma16x16x32(va, pb[part], o[dt]);
     }
+  };
+
+  // software pipeline: the gather of chunk c+1 is in flight while chunk c computes
+  int ja[2], jb[2], jn[2];
+  Gather ga, gb;
+  load_idx(0, ja);
+  load_idx(1, jb);
+  gather(ja, ga);
+  for (int c = 0; c < n_chunks; c += 2) {
+    if (c + 1 < n_chunks) gather(jb, gb);
+    load_idx(c + 2, jn);
+    consume(ja, ga);
+    if (c + 1 >= n_chunks) break;
+    ja[0] = jn[0]; ja[1] = jn[1];
+    if (c + 2 < n_chunks) gather(ja, ga);
+    load_idx(c + 3, jn);
+    consume(jb, gb);
+    jb[0] = jn[0]; jb[1] = jn[1];
   }
 
   lsum += shfl_xor_f(lsum, 16);
