@@ -36,7 +36,9 @@ struct Geometry {
   // workspace offsets
   size_t off_lse = 0, off_cand = 0, off_count = 0, off_flags = 0, off_nflag = 0, off_dense = 0;
   size_t select_bytes = 0;
-  size_t topk_lds = 0;
+  size_t exact_lds = 0;
+  int topk_rows_per_block = 4;
+  bool exact_only = false;  // K above the register-ranked limit: every row takes the exact path
 };
 
 bool g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
@@ -84,7 +86,8 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
 
   // candidate rows: C slots each; chunks of whole tasks under the byte budget
   const int K = d->top_k;
-  int64_t cap = std::max<int64_t>(hs2::kMinCandCap, 4LL * K);
+  geo->exact_only = K > hs2::kMaxRankedK;
+  int64_t cap = geo->exact_only ? 64 : std::max<int64_t>(hs2::kMinCandCap, 2LL * K);
   cap = (cap + 63) / 64 * 64;
   geo->cand_cap = (int)cap;
   const int64_t rows_per_task = (int64_t)d->num_kv_heads * geo->tok;
@@ -109,8 +112,12 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   geo->off_dense = off;
   off = align_up(off + (size_t)hs2::kFallbackBlocks * std::max(1, max_len) * sizeof(uint32_t));
   geo->select_bytes = off;
-  const size_t key_words = std::max<size_t>((size_t)cap, 16 * hs2::kHeadDim);
-  geo->topk_lds = (256 + 16 + 2 * (size_t)geo->bitmap_words + key_words) * sizeof(uint32_t);
+  // exact path: histogram, scratch words, two bitmaps, G query rows in fp32
+  geo->exact_lds =
+      (hs2::kTopkBins + 16 + 2 * (size_t)geo->bitmap_words + 16 * hs2::kHeadDim) * sizeof(uint32_t);
+  // top-K waves: a 256-bin histogram and one bitmap each; up to 4 waves per block
+  const size_t per_wave = (256 + (size_t)geo->bitmap_words) * sizeof(uint32_t);
+  geo->topk_rows_per_block = (int)std::max<size_t>(1, std::min<size_t>(4, 40960 / per_wave));
   return HS2_OK;
 }
 
@@ -151,7 +158,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.c = scale_log2(d);
   sp.bin_base = (int)(gk_bits >> 20) - (hs2::kBins - 1);
   sp.cand_cap = geo.cand_cap;
-  sp.flags = d->flags;
+  sp.flags = d->flags | (geo.exact_only ? (uint32_t)HS2_FLAG_EXACT_SELECT : 0u);
   sp.lse2 = lse2;
   sp.cand = cand;
   sp.cand_count = count;
@@ -189,13 +196,14 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
     if (blocks > 0x7FFFFFFF || rows > 0x7FFFFFFF) return HS2_ERR_UNSUPPORTED;
     sp.task_begin = t0;
     tp.task_begin = t0;
+    tp.n_rows = rows;
     hipError_t e = hs2::launch_zero_i32(nflag, 1, s);
     if (e != hipSuccess) return hip_fail(e, "zero flag counter");
     e = hs2::launch_scores(G, sp, (int)blocks, s);
     if (e != hipSuccess) return hip_fail(e, "scores kernel");
-    e = hs2::launch_topk(G, tp, (int)rows, geo.topk_lds, s);
+    e = hs2::launch_topk(G, tp, (int)rows, geo.topk_rows_per_block, s);
     if (e != hipSuccess) return hip_fail(e, "top-k kernel");
-    e = hs2::launch_fallback(G, tp, geo.topk_lds, s);
+    e = hs2::launch_fallback(G, tp, geo.exact_lds, s);
     if (e != hipSuccess) return hip_fail(e, "exact-select kernel");
   }
   return HS2_OK;

@@ -43,6 +43,19 @@ __device__ __forceinline__ u32x4 to_u32x4(uint4 v) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) with the gfx950 lane-swap ops
+// (v_permlane16_swap / v_permlane32_swap: VALU, no LDS round trip). Called with
+// the same register as both operands, the pair returned holds v[l] and v[l ^ 16]
+// (resp. v[l ^ 32]) in some order.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Order LDS traffic of one wavefront (its own writes become visible to its own
 // later reads); a barrier for the compiler and the memory model, not a
 // workgroup barrier.

@@ -15,12 +15,15 @@ constexpr int kKeyTile = 64;    // keys per LDS tile in the selection sweeps
 constexpr int kSampleStride = 8;  // sample sweep visits key tiles 0, 8, 16, ...
 constexpr int kBins = 256;        // histogram bins per row (8 per octave of S)
 constexpr int kSelThreads = 256;  // threads of every selection workgroup
-constexpr int kMinCandCap = 4096; // candidate slots per row (at least)
+constexpr int kTopkBins = 2048;   // radix bins per pass of the top-K select (11 bits)
+constexpr int kMinCandCap = 2048;  // candidate slots per row: max(2048, 2K) ...
+constexpr int kMaxRankedK = 2048;  // ... held in registers by the top-K wave (<= 64 per lane);
+                                   // a larger K sends every row to the exact path
 constexpr int64_t kCandBudgetBytes = 4LL << 30;  // candidate buffer cap per chunk
-constexpr int kFallbackBlocks = 256;             // persistent grid of the exact path
+constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact path
 // sampled threshold: rank r = ceil(kTauAlpha * K * n_sample / n_cand) + kTauBeta
-constexpr float kTauAlpha = 1.5f;
-constexpr int kTauBeta = 32;
+constexpr float kTauAlpha = 1.2f;
+constexpr int kTauBeta = 24;
 
 // MFMA rows per wave = 16 * row tiles; tokens per selection workgroup.
 __host__ __device__ constexpr int row_tiles(int G) { return G >= 4 ? 4 : G; }
@@ -87,6 +90,7 @@ struct ScoreParams {
 };
 
 struct TopkParams {
+  int64_t n_rows;       // rows of this chunk
   const int32_t* cu;
   int B, Hq, Hkv, K, W;
   int max_tiles;
@@ -125,7 +129,7 @@ struct SparseParams {
 // launchers (defined in the .hip files)
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s);
-hipError_t launch_topk(int G, const TopkParams& p, int n_rows, size_t lds_bytes, hipStream_t s);
+hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_sparse(int G, bool precise, const SparseParams& p, hipStream_t s);
 

@@ -15,7 +15,7 @@
 //     (the full layer's probabilities, summed over the group whose KV cache
 //     and selection the sparse layers reuse -- HySparse2 news summary, KV
 //     Reuse and ablation paragraphs) goes into a per-token LDS histogram, from
-//     which a threshold tau below the top-K boundary is read.
+//     which a threshold tau just below the top-K boundary is estimated.
 //  3. collect: on all candidate tiles (keys j <= t - W; the W most recent
 //     tokens are forced in separately, forced-recent paragraph), every S >= tau
 //     is appended as (S, j) to the token's candidate row in global memory.
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 #pragma unroll
   for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) { m_run[rt][i] = -INFINITY; l_run[rt][i] = 0.f; }
+    for (int i = 0; i < 4; i++) { m_run[rt][i] = -1e30f; l_run[rt][i] = 0.f; }  // finite: no inf-inf
 
   {
     const int kend = t0 + ntok;
@@ -142,37 +142,54 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     load_tile(0, kend, reg);
     store_tile(0, reg);
     __syncthreads();
+    constexpr float kSlack = 8.f;  // log2 units a score may exceed the row reference
     for (int kt = 0; kt < n_kt; kt++) {
       if (kt + 1 < n_kt) load_tile(kt + 1, kend, reg);
       compute(kt & 1);
       const bool diag = kt * kKeyTile + kKeyTile - 1 > t0;  // some key may lie beyond a token
+      if (diag) {
 #pragma unroll
-      for (int rt = 0; rt < RT; rt++) {
+        for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int t = t0 + (w * ROWS_W + 16 * rt + 4 * lq + i) / G;
+#pragma unroll
+            for (int ct = 0; ct < 4; ct++)
+              if (kt * kKeyTile + 16 * ct + lc > t) acc[rt][ct][i] = -INFINITY;
+          }
+      }
+      // the row reference m only moves when a score passes it by the slack (so no
+      // term exceeds 2^slack); moving it rescales l. Raw accumulators compare
+      // directly since the scale c is positive.
+      bool move = false;
+      float mx[RT][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const int r = w * ROWS_W + 16 * rt + 4 * lq + i;
-          const int t = t0 + r / G;
-          float v[4];
-          float mx = -INFINITY;
-#pragma unroll
-          for (int ct = 0; ct < 4; ct++) {
-            const int j = kt * kKeyTile + 16 * ct + lc;
-            v[ct] = acc[rt][ct][i] * c;
-            if (diag && j > t) v[ct] = -INFINITY;
-            mx = fmaxf(mx, v[ct]);
-          }
-          if (mx > m_run[rt][i]) {
-            l_run[rt][i] *= fast_exp2(m_run[rt][i] - mx);
-            m_run[rt][i] = mx;
-          }
-          if (mx > -INFINITY) {
-            float s = 0.f;
-#pragma unroll
-            for (int ct = 0; ct < 4; ct++) s += fast_exp2(v[ct] - m_run[rt][i]);
-            l_run[rt][i] += s;
-          }
+          mx[rt][i] = fmaxf(fmaxf(acc[rt][0][i], acc[rt][1][i]), fmaxf(acc[rt][2][i], acc[rt][3][i])) * c;
+          move |= mx[rt][i] > m_run[rt][i] + kSlack;
         }
+      if (__any(move)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float mn = fmaxf(m_run[rt][i], mx[rt][i]);
+            l_run[rt][i] *= fast_exp2(m_run[rt][i] - mn);
+            m_run[rt][i] = mn;
+          }
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float mneg = -m_run[rt][i];
+          float sum = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 4; ct++) sum += fast_exp2(fmaf(acc[rt][ct][i], c, mneg));
+          l_run[rt][i] += sum;
+        }
       if (kt + 1 < n_kt) store_tile((kt + 1) & 1, reg);
       __syncthreads();
     }
@@ -189,8 +206,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
       for (int off = 1; off < 16; off <<= 1) {
         const float mo = shfl_xor_f(m, off), so = shfl_xor_f(s, off);
         const float mn = fmaxf(m, mo);
-        float a = (m == -INFINITY) ? 0.f : s * fast_exp2(m - mn);
-        float b = (mo == -INFINITY) ? 0.f : so * fast_exp2(mo - mn);
+        const float a = s * fast_exp2(m - mn);  // m, mo finite (>= -1e30)
+        const float b = so * fast_exp2(mo - mn);
         s = a + b;
         m = mn;
       }
@@ -230,7 +247,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   auto group_scores = [&](int rt, int ct, float (&S)[NT]) {
     float e[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) e[i] = fast_exp2(acc[rt][ct][i] * c - lse[rt][i]);
+    for (int i = 0; i < 4; i++) e[i] = fast_exp2(fmaf(acc[rt][ct][i], c, -lse[rt][i]));
     if constexpr (G == 1) {
 #pragma unroll
       for (int u = 0; u < NT; u++) S[u] = e[u];
@@ -288,9 +305,14 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
         int cum = 0;
         for (int b = kBins - 1; b >= 1; b--) {
           const uint32_t wd = sm.hist[tid][b >> 1];
-          cum += (b & 1) ? (int)(wd >> 16) : (int)(wd & 0xFFFFu);
+          const int h = (b & 1) ? (int)(wd >> 16) : (int)(wd & 0xFFFFu);
+          cum += h;
           if (cum >= r) {
-            tau = __uint_as_float((uint32_t)(b + p.bin_base) << 20);
+            // the r-th sample lies (r - (cum - h)) / h deep into bin b from its top;
+            // interpolate linearly in the bit pattern (bins are 1/8 octave)
+            const float depth = (float)(r - (cum - h)) / (float)h;
+            const uint32_t lo_bits = (uint32_t)(b + p.bin_base) << 20;
+            tau = __uint_as_float(lo_bits + (uint32_t)((1.f - depth) * (float)(1u << 20)));
             mode = kModeEmit;
             break;
           }
@@ -327,6 +349,10 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
       compute(kt & 1);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
+        float Sv[4][NT];
+        uint32_t pass[NT];
+#pragma unroll
+        for (int u = 0; u < NT; u++) pass[u] = 0u;
 #pragma unroll
         for (int ct = 0; ct < 4; ct++) {
           float S[NT];
@@ -334,12 +360,25 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
           const int j = kt * kKeyTile + 16 * ct + lc;
 #pragma unroll
           for (int u = 0; u < NT; u++) {
-            if (S[u] >= tau_r[rt][u] && j < nc_r[rt][u]) {
-              const int tl = token_of(rt, u);
-              const int pos = atomicAdd(&sm.cnt[tl], 1);
-              if (pos < C)
-                cand[(size_t)(slot0 + tl) * C + pos] =
-                    ((uint64_t)__float_as_uint(S[u]) << 32) | (uint32_t)j;
+            Sv[ct][u] = S[u];
+            pass[u] |= (S[u] >= tau_r[rt][u] && j < nc_r[rt][u]) ? (1u << ct) : 0u;
+          }
+        }
+        // one LDS atomic per lane and token for its (up to 4) passing keys
+#pragma unroll
+        for (int u = 0; u < NT; u++) {
+          if (pass[u]) {
+            const int tl = token_of(rt, u);
+            int pos = atomicAdd(&sm.cnt[tl], __popc(pass[u]));
+            uint64_t* dst = cand + (size_t)(slot0 + tl) * C;
+#pragma unroll
+            for (int ct = 0; ct < 4; ct++) {
+              if ((pass[u] >> ct) & 1u) {
+                if (pos < C)
+                  dst[pos] = ((uint64_t)__float_as_uint(Sv[ct][u]) << 32) |
+                             (uint32_t)(kt * kKeyTile + 16 * ct + lc);
+                pos++;
+              }
             }
           }
         }

@@ -6,12 +6,13 @@
 // the largest group score S, ties to the lower position; then
 //   I_t = ascending(T_t U [t-W+1, t]), padded with -1 to K+W.
 //
-// topk_kernel: one 256-thread workgroup per row of a chunk. Its candidates
-//   (S >= tau, collected by the scoring sweep) are ranked by a 4-pass 8-bit
-//   radix select on the fp32 bit pattern of S (monotone for S >= 0), which
-//   yields the K-th largest value and how many of the values equal to it to
-//   take. Selected positions go into an LDS bitmap, so the compaction into the
-//   index row comes out in ascending order.
+// topk_kernel: one wavefront per row of a chunk. Its candidates (S >= tau,
+//   collected by the scoring sweep) sit in registers and are ranked by a radix
+//   select on the fp32 bit pattern of S (monotone for S >= 0), starting below
+//   the bits all candidates share, 8 bits per pass; it yields the K-th largest
+//   value and how many of the values equal to it to take (lowest positions
+//   first). Selected positions go into an LDS bitmap, so the compaction into
+//   the index row comes out in ascending order.
 // exact_kernel: persistent workgroups over the rows the sweep could not settle
 //   (too many / too few candidates, or the exact flag). S is recomputed for the
 //   whole row into a scratch row, then the same select and assembly run.
@@ -21,7 +22,7 @@
 namespace hs2 {
 
 struct TopkShared {
-  uint32_t* hist;   // [256]
+  uint32_t* hist;   // [kTopkBins]
   int32_t* misc;    // [16]
   uint32_t* sel;    // [bitmap_words]
   uint32_t* tie;    // [bitmap_words]
@@ -29,12 +30,16 @@ struct TopkShared {
   float* qf;        // [16 * 128] (exact path only)
 };
 
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trip):
+// scans within each 16-lane row, then row broadcasts of lanes 15 and 31.
 __device__ __forceinline__ int wave_incl_scan(int x, int l) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (l >= off) x += y;
-  }
+  (void)l;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
   return x;
 }
 
@@ -56,48 +61,91 @@ __device__ int block_excl_scan(int v, int32_t* misc, int* total) {
   return before + x - v;
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
 // K-th largest key among key(i), i < n (1 <= k <= n). Returns the key and, in
-// *krem, how many elements equal to it belong to the top k.
+// *krem, how many elements equal to it belong to the top k. Radix select on the
+// bits below the keys' common prefix, up to 11 bits (2048 bins) per pass.
 template <class KeyFn>
 __device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int* krem) {
-  const int tid = threadIdx.x, l = tid & 63;
-  uint32_t prefix = 0u, mask = 0u;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = tid; i < n; i += kSelThreads) {
+    const uint32_t b = key(i);
+    mn = min(mn, b);
+    mx = max(mx, b);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (l == 0) {
+    sh.misc[4 + w] = (int)mn;
+    sh.misc[8 + w] = (int)mx;
+  }
+  __syncthreads();
+  mn = (uint32_t)sh.misc[4];
+  mx = (uint32_t)sh.misc[8];
+#pragma unroll
+  for (int i = 1; i < 4; i++) {
+    mn = min(mn, (uint32_t)sh.misc[4 + i]);
+    mx = max(mx, (uint32_t)sh.misc[8 + i]);
+  }
+  __syncthreads();
+  if (mn == mx) {
+    *krem = k;
+    return mn;
+  }
+  int hi = 31 - __clz(mn ^ mx);  // highest bit where the keys differ
+  uint32_t mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
+  uint32_t prefix = mx & mask;
   int kr = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.hist[tid] = 0u;
+  constexpr int kPer = kTopkBins / kSelThreads;  // bins per thread in the scan
+  while (hi >= 0) {
+    const int lo = max(0, hi - 10);
+    const int nb = hi - lo + 1;
+    const uint32_t dmask = (1u << nb) - 1u;
+    for (int i = tid; i < kTopkBins; i += kSelThreads) sh.hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += kSelThreads) {
       const uint32_t b = key(i);
-      if ((b & mask) == prefix) atomicAdd(&sh.hist[(b >> shift) & 255u], 1u);
+      if ((b & mask) == prefix) atomicAdd(&sh.hist[(b >> lo) & dmask], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      const uint32_t h0 = sh.hist[4 * l], h1 = sh.hist[4 * l + 1], h2 = sh.hist[4 * l + 2],
-                     h3 = sh.hist[4 * l + 3];
-      const uint32_t local = h0 + h1 + h2 + h3;
-      uint32_t suf = local;  // inclusive suffix sum over lanes
+    // suffix counts over bins: thread tid owns bins [kPer*tid, kPer*tid + kPer)
+    uint32_t h[kPer];
+    int local = 0;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(suf, off, 64);
-        if (l + off < 64) suf += v;
+    for (int u = 0; u < kPer; u++) {
+      h[u] = sh.hist[kPer * tid + u];
+      local += (int)h[u];
+    }
+    int total;
+    const int excl = block_excl_scan(local, sh.misc, &total);
+    const int above = total - excl - local;  // elements in bins above this thread's
+    if (above < kr && kr <= above + local) {
+      int a = above, d = kPer * tid;
+#pragma unroll
+      for (int u = kPer - 1; u >= 0; u--) {
+        if (a + (int)h[u] >= kr) { d = kPer * tid + u; break; }
+        a += (int)h[u];
       }
-      const uint32_t above = suf - local;
-      if (above < (uint32_t)kr && (uint32_t)kr <= suf) {
-        uint32_t a = above;
-        int d;
-        if (a + h3 >= (uint32_t)kr) d = 4 * l + 3;
-        else if ((a += h3) + h2 >= (uint32_t)kr) d = 4 * l + 2;
-        else if ((a += h2) + h1 >= (uint32_t)kr) d = 4 * l + 1;
-        else { a += h1; d = 4 * l; }
-        sh.misc[0] = d;
-        sh.misc[1] = (int)a;
-      }
+      sh.misc[0] = d;
+      sh.misc[1] = a;
     }
     __syncthreads();
-    const int d = sh.misc[0];
+    const uint32_t d = (uint32_t)sh.misc[0];
     kr -= sh.misc[1];
-    prefix |= (uint32_t)d << shift;
-    mask |= 0xFFu << shift;
+    prefix |= d << lo;
+    mask |= dmask << lo;
+    hi = lo - 1;
     __syncthreads();
   }
   *krem = kr;
@@ -205,8 +253,8 @@ __device__ __forceinline__ RowInfo decode_slot(const TopkParams& p, int64_t slot
 __device__ __forceinline__ TopkShared carve_lds(uint32_t* smem, const TopkParams& p, bool exact) {
   TopkShared sh;
   sh.hist = smem;
-  sh.misc = reinterpret_cast<int32_t*>(smem + 256);
-  sh.sel = smem + 256 + 16;
+  sh.misc = reinterpret_cast<int32_t*>(smem + kTopkBins);
+  sh.sel = smem + kTopkBins + 16;
   sh.tie = sh.sel + p.bitmap_words;
   sh.keys = sh.tie + p.bitmap_words;
   sh.qf = reinterpret_cast<float*>(sh.keys);
@@ -214,34 +262,158 @@ __device__ __forceinline__ TopkShared carve_lds(uint32_t* smem, const TopkParams
   return sh;
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkParams p) {
+// ---------------------------------------------------------------------------
+// Candidate path: one wavefront per row, no workgroup barriers. The row's
+// candidates (at most 64 * NREG) sit in registers: lane l holds entries l + 64 s.
+// LDS per wave: a 256-bin histogram and a bitmap of the row's candidate range.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
+  return v;
+}
+
+template <int NREG>
+__global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   extern __shared__ uint32_t smem[];
-  const TopkShared sh = carve_lds(smem, p, false);
-  const int64_t slot = blockIdx.x;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int waves = blockDim.x >> 6;
+  uint32_t* hist = smem + (size_t)w * (256 + p.bitmap_words);
+  uint32_t* bm = hist + 256;
+  const int64_t slot = (int64_t)blockIdx.x * waves + w;
+  if (slot >= p.n_rows) return;
   const RowInfo r = decode_slot(p, slot);
   if (r.t >= r.L) return;
   const int KW = p.K + p.W;
   const int n_c = r.t - p.W + 1;
   int32_t* row = p.idx + ((size_t)(r.base + r.t) * p.Hkv + r.g) * KW;
   float* kth_out = p.kth ? p.kth + (size_t)(r.base + r.t) * p.Hkv + r.g : nullptr;
-  if (p.K == 0 || n_c <= p.K) {
-    write_trivial_row(n_c, p.K, r.t, KW, row);
-    if (kth_out && threadIdx.x == 0) *kth_out = -1.f;
+  if (p.K == 0 || n_c <= p.K) {  // nothing to rank: [0, t] or the window only
+    const int start = (n_c <= p.K) ? 0 : n_c;
+    const int n = r.t - start + 1;
+    for (int o = l; o < KW; o += 64) row[o] = (o < n) ? start + o : -1;
+    if (kth_out && l == 0) *kth_out = -1.f;
     return;
   }
   const int count = p.cand_count[slot];
   if (count < 0) return;  // settled by exact_kernel
   const uint64_t* cand = p.cand + (size_t)slot * p.cand_cap;
-  for (int i = threadIdx.x; i < count; i += kSelThreads) sh.keys[i] = (uint32_t)(cand[i] >> 32);
-  __syncthreads();
-  int krem;
-  const uint32_t kth = radix_kth([&](int i) { return sh.keys[i]; }, count, p.K, sh, &krem);
+  uint32_t key[NREG], pos[NREG];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int s = 0; s < NREG; s++) {
+    const int i = l + 64 * s;
+    key[s] = 0u;
+    pos[s] = 0u;
+    if (i < count) {
+      const uint64_t e = cand[i];
+      key[s] = (uint32_t)(e >> 32);
+      pos[s] = (uint32_t)e;
+      mn = min(mn, key[s]);
+      mx = max(mx, key[s]);
+    }
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  // radix select of the K-th largest key below the common prefix, 8 bits per pass
+  uint32_t prefix = mx, mask = 0xFFFFFFFFu;
+  int kr = p.K;
+  if (mn != mx) {
+    int hi = 31 - __clz(mn ^ mx);
+    mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
+    prefix = mx & mask;
+    while (hi >= 0) {
+      const int lo = max(0, hi - 7);
+      const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+#pragma unroll
+      for (int u = 0; u < 4; u++) hist[l + 64 * u] = 0u;
+      wave_lds_fence();
+#pragma unroll
+      for (int s = 0; s < NREG; s++)
+        if (l + 64 * s < count && (key[s] & mask) == prefix)
+          atomicAdd(&hist[(key[s] >> lo) & dmask], 1u);
+      wave_lds_fence();
+      // lane l owns bins 4l .. 4l+3; inclusive suffix sums over lanes
+      uint32_t h[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) h[u] = hist[4 * l + u];
+      const uint32_t local = h[0] + h[1] + h[2] + h[3];
+      const uint32_t incl = (uint32_t)wave_incl_scan((int)local, l);
+      const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+      const uint32_t suf = total - incl + local;  // this lane's bins and all above
+      const uint32_t above = suf - local;
+      const bool mine = above < (uint32_t)kr && (uint32_t)kr <= suf;
+      int d = 0;
+      uint32_t a = above;
+      if (mine) {
+        if (a + h[3] >= (uint32_t)kr) d = 4 * l + 3;
+        else if ((a += h[3]) + h[2] >= (uint32_t)kr) d = 4 * l + 2;
+        else if ((a += h[2]) + h[1] >= (uint32_t)kr) d = 4 * l + 1;
+        else { a += h[1]; d = 4 * l; }
+      }
+      const int src = max(0, __ffsll((unsigned long long)__ballot(mine)) - 1);
+      d = __shfl(d, src, 64);
+      a = (uint32_t)__shfl((int)a, src, 64);
+      kr -= (int)a;
+      prefix |= (uint32_t)d << lo;
+      mask |= dmask << lo;
+      hi = lo - 1;
+      wave_lds_fence();
+    }
+  }
+  const uint32_t kth = prefix;  // K-th largest key; kr of the keys equal to it are taken
+  // ties at the boundary: take the kr lowest positions (binary search on position)
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int s = 0; s < NREG; s++) n_eq += (l + 64 * s < count && key[s] == kth) ? 1u : 0u;
+  n_eq = wave_sum_u32(n_eq);
+  uint32_t pos_cut = 0xFFFFFFFFu;  // ties with pos <= pos_cut are taken
+  if (n_eq != (uint32_t)kr) {
+    uint32_t lo = 0, hi = (uint32_t)n_c - 1;  // smallest cut with >= kr ties at or below it
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      uint32_t c = 0;
+#pragma unroll
+      for (int s = 0; s < NREG; s++)
+        c += (l + 64 * s < count && key[s] == kth && pos[s] <= mid) ? 1u : 0u;
+      c = wave_sum_u32(c);
+      if (c >= (uint32_t)kr) hi = mid; else lo = mid + 1;
+    }
+    pos_cut = lo;
+  }
+  // bitmap of the selected positions, then ascending compaction
   const int nwords = ceil_div(n_c, 32);
-  mark_selected([&](int i) { return sh.keys[i]; },
-                [&](int i) { return (uint32_t)(cand[i] & 0xFFFFFFFFu); }, count, kth, krem, nwords,
-                sh);
-  write_selected_row(nwords, n_c, r.t, KW, row, sh);
-  if (kth_out && threadIdx.x == 0) *kth_out = __uint_as_float(kth);
+  for (int i = l; i < nwords; i += 64) bm[i] = 0u;
+  wave_lds_fence();
+#pragma unroll
+  for (int s = 0; s < NREG; s++) {
+    if (l + 64 * s < count && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut)))
+      atomicOr(&bm[pos[s] >> 5], 1u << (pos[s] & 31));
+  }
+  wave_lds_fence();
+  // lane l compacts words [l * per, (l + 1) * per): count, one wave scan, write
+  const int per = ceil_div(nwords, 64);
+  const int wb = min(l * per, nwords), we = min(wb + per, nwords);
+  int cnt = 0;
+  for (int i = wb; i < we; i++) cnt += __popc(bm[i]);
+  const int incl = wave_incl_scan(cnt, l);
+  const int base = __shfl(incl, 63, 64);  // number of selected positions (K)
+  int off = incl - cnt;
+  for (int i = wb; i < we; i++) {
+    uint32_t mm = bm[i];
+    while (mm) {
+      const int b = __ffs(mm) - 1;
+      mm &= mm - 1;
+      if (off < KW) row[off] = i * 32 + b;
+      off++;
+    }
+  }
+  for (int j = n_c + l; j <= r.t; j += 64) {
+    const int o = base + (j - n_c);
+    if (o < KW) row[o] = j;
+  }
+  for (int o = base + (r.t - n_c + 1) + l; o < KW; o += 64) row[o] = -1;
+  if (kth_out && l == 0) *kth_out = __uint_as_float(kth);
 }
 
 template <int G>
@@ -303,15 +475,27 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
   }
 }
 
-hipError_t launch_topk(int G, const TopkParams& p, int n_rows, size_t lds_bytes, hipStream_t s) {
+hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s) {
   (void)G;
   if (n_rows <= 0) return hipSuccess;
-  if (lds_bytes > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (e != hipSuccess) return e;
+  const size_t lds = (size_t)rows_per_block * (256 + p.bitmap_words) * sizeof(uint32_t);
+  const dim3 grid((n_rows + rows_per_block - 1) / rows_per_block), block(64 * rows_per_block);
+  const int nreg = p.cand_cap / 64;
+  if (nreg <= 32) {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<32>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, lds, s, p);
+  } else {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<64>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_kernel<64>, grid, block, lds, s, p);
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(n_rows), dim3(kSelThreads), lds_bytes, s, p);
   return hipGetLastError();
 }
 

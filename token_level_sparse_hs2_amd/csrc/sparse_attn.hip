@@ -129,8 +129,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     mx *= c;  // finite: the chunk has a valid entry
     // the reference m only moves when a score passes it by the slack (never
     // overflows: terms stay below 2^slack); moving it rescales l and O
