@@ -125,6 +125,31 @@ def test_zero_queries_tie_rule_bit_exact():
     assert (idx.cpu().numpy().reshape(o_idx.shape) == o_idx).all()
 
 
+def test_peaked_softmax_rows():
+    """Queries scaled by 8: the full layer's softmax is sharply peaked and a
+    norm-based bound on each row's maximum overshoots by far more than the
+    float range allows, so the statistics sweep must take its exact-maximum
+    route. Selection and the K-th score still follow the oracle."""
+    w = synthgen.custom([64, 200, 2900], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=12)
+    inp = synthgen.make_inputs(w)
+    inp["q_full"] = synthgen.float_to_bf16(synthgen.bf16_to_float(inp["q_full"]) * 8.0)
+    case = GpuCase(w, inp)
+    idx_t, kth_t = case.select()
+    idx = idx_t.cpu().numpy()
+    check_structure(idx, inp["cu_seqlens"], w.K, w.W)
+    stats = acceptance_select(idx, inp, w)
+    log(f"  select: rows {stats['rows']} exact {stats['exact_rows']} overlap {stats['overlap']:.6f} "
+        f"A1 margin {stats['a1_worst_margin']:.3g}")
+    assert_select_ok(stats)
+    kth = kth_t.cpu().numpy().reshape(-1)[stats["row_ids"]]
+    okth = stats["oracle_kth"]
+    assert ((kth == -1.0) == (okth == -1.0)).all()
+    sel = okth > 1e-30
+    rel = np.abs(kth[sel] - okth[sel]) / okth[sel]
+    log(f"  kth relative diff: median {np.median(rel):.3g} max {rel.max():.3g}")
+    assert rel.max() <= 1e-3
+
+
 def test_prefill_block_equals_components():
     import torch
     w = synthgen.custom([1000, 3000], Hq=8, Hkv=2, K=256, W=32, n_sparse=2, seed=9)

@@ -34,7 +34,8 @@ struct Geometry {
   int64_t rows_per_chunk = 0;
   int bitmap_words = 0;
   // workspace offsets
-  size_t off_lse = 0, off_cand = 0, off_count = 0, off_flags = 0, off_nflag = 0, off_dense = 0;
+  size_t off_lse = 0, off_cand = 0, off_count = 0, off_flags = 0, off_nflag = 0, off_dense = 0,
+         off_kmax = 0;
   size_t select_bytes = 0;
   size_t exact_lds = 0;
   int topk_rows_per_block = 4;
@@ -111,6 +112,8 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   off = align_up(off + sizeof(int32_t));
   geo->off_dense = off;
   off = align_up(off + (size_t)hs2::kFallbackBlocks * std::max(1, max_len) * sizeof(uint32_t));
+  geo->off_kmax = off;
+  off = align_up(off + (size_t)v->batch * d->num_kv_heads * sizeof(uint32_t));
   geo->select_bytes = off;
   // exact path: histogram, scratch words, two bitmaps, G query rows in fp32
   geo->exact_lds =
@@ -139,6 +142,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   int32_t* flags = reinterpret_cast<int32_t*>(w + geo.off_flags);
   int32_t* nflag = reinterpret_cast<int32_t*>(w + geo.off_nflag);
   uint32_t* dense = reinterpret_cast<uint32_t*>(w + geo.off_dense);
+  uint32_t* kmax = reinterpret_cast<uint32_t*>(w + geo.off_kmax);
 
   const int G = geo.G;
   const float gk = (float)G / (float)std::max(1, d->top_k);
@@ -164,6 +168,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.cand_count = count;
   sp.flag_list = flags;
   sp.flag_count = nflag;
+  sp.kmax = kmax;
 
   hs2::TopkParams tp{};
   tp.cu = v->cu_seqlens;
@@ -189,6 +194,8 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.idx = idx_out;
   tp.kth = kth_out;
 
+  hipError_t ek = hs2::launch_key_norms(sp.k, v->cu_seqlens, v->batch, d->num_kv_heads, geo.T, kmax, s);
+  if (ek != hipSuccess) return hip_fail(ek, "key norm kernel");
   for (int64_t t0 = 0; t0 < geo.n_tasks; t0 += geo.tasks_per_chunk) {
     const int64_t nt = std::min(geo.tasks_per_chunk, geo.n_tasks - t0);
     const int64_t blocks = nt * d->num_kv_heads;

@@ -11,6 +11,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// lambdas that capture register arrays must be inlined, or the arrays go to scratch
+#define HS2_INLINE __attribute__((always_inline))
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

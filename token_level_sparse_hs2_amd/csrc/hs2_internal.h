@@ -25,9 +25,10 @@ constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact
 constexpr float kTauAlpha = 1.2f;
 constexpr int kTauBeta = 24;
 
-// MFMA rows per wave = 16 * row tiles; tokens per selection workgroup.
-__host__ __device__ constexpr int row_tiles(int G) { return G >= 4 ? 4 : G; }
-__host__ __device__ constexpr int tokens_per_task(int G) { return 64 * row_tiles(G) / G; }
+// Scoring workgroups: 4 waves x 32 * score_row_tiles(G) MFMA rows (tokens x heads);
+// tokens per selection task (one workgroup): 128, 64, 64, 32, 16 for G = 1..16.
+__host__ __device__ constexpr int score_row_tiles(int G) { return G >= 4 ? 2 : 1; }
+__host__ __device__ constexpr int tokens_per_task(int G) { return 4 * 32 * score_row_tiles(G) / G; }
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -80,6 +81,7 @@ struct ScoreParams {
   int64_t task_begin;   // first task of this chunk
   float c;              // softmax_scale * log2(e)
   int bin_base;         // (bits(G/K) >> 20) - (kBins - 1)
+  const uint32_t* kmax; // [B * Hkv] largest key norm of each (sequence, group), float bits
   int cand_cap;         // C
   uint32_t flags;
   float* lse2;          // [T, Hq] log2-domain log-sum-exp of each full-layer row
@@ -128,6 +130,8 @@ struct SparseParams {
 
 // launchers (defined in the .hip files)
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv, int64_t T,
+                            uint32_t* kmax, hipStream_t s);
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);

@@ -1,15 +1,19 @@
 // select_scores.hip - the full-attention layer's scoring sweeps on gfx950.
 //
 // One workgroup owns TOK consecutive query tokens of one sequence and one KV
-// group g (all G query heads of the group: 64*RT MFMA rows, token-major,
-// head-minor, so a lane's accumulator rows are the heads of one token). It
-// sweeps the causal keys in 64-key tiles staged through LDS, with bf16 MFMA
-// QK^T tiles and fp32 accumulation, three times:
+// group g: all G query heads of the group, 4 * 32 * RT MFMA rows in token-major,
+// head-minor order, so the 32x32 accumulator rows a lane holds are the heads of
+// one or more whole tokens (or half a group, joined with the partner lane). It
+// sweeps the causal keys in 64-key tiles staged through LDS, with bf16
+// v_mfma_f32_32x32x16_bf16 and fp32 accumulation, three times:
 //
-//  1. row statistics: per (t, h) the max m and sum l of exp over all causal
-//     keys (online, log2 domain), giving lse2 = m + log2 l. The full layer's
-//     softmax is taken over all causal keys, scale 1/sqrt(d) (attention as in
-//     the SHARP walkthrough, section 1.1).
+//  1. row statistics: per (t, h) the log2-domain log-sum-exp lse2 of the full
+//     layer's softmax over all causal keys with scale 1/sqrt(d) (attention as in
+//     the SHARP walkthrough, section 1.1). The exponents are taken against a
+//     fixed per-row reference, the Cauchy-Schwarz bound c * |q| * max_j |k_j|,
+//     so the sweep needs no running maximum; if that bound is too loose for
+//     some row (sum below 2^-60) the workgroup redoes the sweep with a lazily
+//     moved running maximum.
 //  2. sample: on every 8th key tile, the group score
 //       S[t,g,j] = sum_{h in g} exp2(z2[t,h,j] - lse2[t,h])
 //     (the full layer's probabilities, summed over the group whose KV cache
@@ -29,21 +33,42 @@ namespace hs2 {
 
 enum : int { kModeTrivial = 0, kModeEmit = 1, kModeExact = 2, kModeSample = 3 };
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// C[32x32] += A[32x16] * B[16x32], bf16 in, fp32 accumulate. Lane l supplies A row
+// (l & 31), k = 8*(l >> 5) .. +7 and B column (l & 31), same k; it receives C
+// column (l & 31), rows 8*(r >> 2) + 4*(l >> 5) + (r & 3) for register r.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int G>
 struct ScoreCfg {
-  static constexpr int RT = row_tiles(G);
-  static constexpr int TOK = tokens_per_task(G);
-  static constexpr int ROWS_W = 16 * RT;
-  static constexpr int NT = G >= 4 ? 1 : 4 / G;  // tokens per lane per row tile
+  static constexpr int RT = score_row_tiles(G);       // 32-row tiles per wave
+  static constexpr int ROWS_W = 32 * RT;              // MFMA rows per wave
+  static constexpr int TOK = tokens_per_task(G);      // tokens per workgroup
+  // group elements (token sums) per lane per 32x32 accumulator tile
+  static constexpr int NE = G == 1 ? 16 : G == 2 ? 8 : G == 16 ? 2 : 4;
 };
 
+constexpr int kRing = 4;  // K tiles in flight: compute tile kt while kt+1..kt+3 load
+
+template <int TOK>
 struct ScoreSmem {
-  uint4 ktile[2][kKeyTile][16];       // two 64-key x 256-byte tiles (XOR-swizzled chunks)
-  uint32_t hist[64][kBins / 2];       // two 16-bit bin counters per word
-  float tau[64];
-  int32_t cnt[64];
-  int32_t mode[64];
-  int32_t any_sample, any_emit;
+  // A ring of kRing 64-key x 256-byte K tiles (XOR-swizzled 16-byte chunks). The
+  // sample sweep uses tiles 0-1 only and keeps its histogram where tiles 2.. live.
+  union {
+    uint4 ktile[kRing][kKeyTile][16];
+    struct {
+      uint4 ktile2[2][kKeyTile][16];
+      uint32_t hist[TOK][kBins / 2];  // two 16-bit bin counters per word
+    } s;
+  } u;
+  float rref[256];                   // per-MFMA-row reference subtracted from q . k
+  float tau[TOK];
+  int32_t cnt[TOK];
+  int32_t mode[TOK];
+  int32_t any_sample, any_emit, unsafe;
 };
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
@@ -57,14 +82,66 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Largest key norm of each (sequence, KV group). A workgroup takes 256 tokens of
+// one group, 16 lanes per key row (coalesced 256-byte rows); when its tokens lie
+// in one sequence it reduces to one atomic max on the float bits (norms are >= 0),
+// else each row does its own. kmax must be zeroed first.
+__global__ __launch_bounds__(256) void key_norm_kernel(const uint16_t* k, const int32_t* cu, int B,
+                                                       int Hkv, int64_t T, uint32_t* kmax) {
+  __shared__ float wmax[4];
+  const int g = blockIdx.y, tid = threadIdx.x, lane16 = tid & 15, sub = tid >> 4;
+  const int64_t t_first = (int64_t)blockIdx.x * 256;
+  const int64_t t_last = min(T, t_first + 256) - 1;
+  const int s_first = find_seq(cu, B, t_first), s_last = find_seq(cu, B, t_last);
+  const bool one_seq = s_first == s_last;
+  float m = 0.f;
+  for (int it = 0; it < 16; it++) {
+    const int64_t tok = t_first + 16 * it + sub;
+    float n2 = 0.f;
+    if (tok <= t_last) {
+      const uint4 v = ldg128(k + ((size_t)tok * Hkv + g) * kHeadDim + 8 * lane16);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const float a = __uint_as_float(wv[u] << 16), b = __uint_as_float(wv[u] & 0xFFFF0000u);
+        n2 = fmaf(a, a, fmaf(b, b, n2));
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) n2 += shfl_xor_f(n2, off);
+    const float nrm = sqrtf(n2);
+    if (one_seq) m = fmaxf(m, nrm);
+    else if (lane16 == 0 && tok <= t_last)
+      atomicMax(&kmax[find_seq(cu, B, tok) * Hkv + g], __float_as_uint(nrm));
+  }
+  if (!one_seq) return;  // uniform over the workgroup
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0)
+    atomicMax(&kmax[s_first * Hkv + g],
+              __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+}
+
+hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv, int64_t T,
+                            uint32_t* kmax, hipStream_t s) {
+  hipError_t e = launch_zero_i32(reinterpret_cast<int32_t*>(kmax), B * Hkv, s);
+  if (e != hipSuccess) return e;
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)((T + 255) / 256), (unsigned)Hkv), dim3(256), 0,
+                     s, k, cu, B, Hkv, T, kmax);
+  return hipGetLastError();
+}
+
 template <int G>
 __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
-  using C = ScoreCfg<G>;
-  constexpr int RT = C::RT, TOK = C::TOK, ROWS_W = C::ROWS_W, NT = C::NT;
-  __shared__ ScoreSmem sm;
+  using Cfg = ScoreCfg<G>;
+  constexpr int RT = Cfg::RT, TOK = Cfg::TOK, ROWS_W = Cfg::ROWS_W, NE = Cfg::NE;
+  __shared__ ScoreSmem<TOK> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int lq = l >> 4, lc = l & 15;
+  const int h5 = l >> 5, c5 = l & 31;
   const int g = blockIdx.x % p.Hkv;
   const int64_t task = p.task_begin + blockIdx.x / p.Hkv;
   int seq, tile;
@@ -77,146 +154,235 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   const int Hq = p.Hq, Hkv = p.Hkv, K = p.K, W = p.W;
   const float c = p.c;
 
-  // ---- Q operands (A): row ra = token-major, head-minor ----
-  bf16x8 qa[RT][4];
+  // accumulator register r of row tile rt holds wave row 32 rt + 8 (r >> 2) + 4 h5 + (r & 3)
+  auto row_of = [&](int rt, int r) HS2_INLINE { return w * ROWS_W + 32 * rt + 8 * (r >> 2) + 4 * h5 + (r & 3); };
+  // first register of group element e (the heads of one token, or half of them)
+  auto first_reg = [&](int e) HS2_INLINE {
+    if constexpr (G == 1) return e;
+    else if constexpr (G == 2) return 4 * (e >> 1) + 2 * (e & 1);
+    else if constexpr (G == 16) return 8 * e;
+    else return 4 * e;
+  };
+  auto token_of = [&](int rt, int e) HS2_INLINE { return row_of(rt, first_reg(e)) / G; };
+  const bool owner = (G <= 4) || h5 == 0;  // for G >= 8 lanes l and l ^ 32 share a token
+
+  // ---- Q operands (A): row ra (token-major, head-minor), d = 16 ks + 8 h5 .. +7 ----
+  bf16x8 qa[RT][8];
 #pragma unroll
   for (int rt = 0; rt < RT; rt++) {
-    const int ra = w * ROWS_W + 16 * rt + lc;
+    const int ra = w * ROWS_W + 32 * rt + c5;
     const int ta = ra / G, ha = ra % G;
+    float qn2 = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
+    for (int ks = 0; ks < 8; ks++) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ta < ntok)
         v = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
-                            32 * ks + 8 * lq));
+                            16 * ks + 8 * h5));
       qa[rt][ks] = as_bf16x8(v);
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const float a = __uint_as_float(v[u] << 16), b = __uint_as_float(v[u] & 0xFFFF0000u);
+        qn2 = fmaf(a, a, fmaf(b, b, qn2));
+      }
     }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(qn2), __float_as_uint(qn2),
+                                                     false, false);
+    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    // reference of sweep 1: the Cauchy-Schwarz bound |q| * max_j |k_j| >= q . k_j
+    if (h5 == 0) sm.rref[ra] = sqrtf(tot) * __uint_as_float(p.kmax[seq * Hkv + g]);
   }
 
+  // K tiles go global -> LDS directly (no staging registers). One load moves 4
+  // keys x 256 bytes: lane l lands at LDS slot (key 4r + (l >> 4), chunk l & 15)
+  // and fetches the logical chunk (l & 15) ^ (key & 15), which realises the XOR
+  // swizzle. Keys at or past kend read row kend - 1 (masked later). The load is
+  // issued from inline asm so that the compiler, which cannot tell ring slots
+  // apart, does not drain every load in flight before each LDS read; the sweeps
+  // wait for exactly the tile they need with vmcnt and an LDS-only barrier.
   const uint16_t* kbase = p.k + (size_t)g * kHeadDim;
-  auto load_tile = [&](int kt, int kend, uint4 (&reg)[4]) {
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)&sm.u.ktile[0][0][0];
+  auto dma_tile = [&](int kt, int kend, int buf) HS2_INLINE {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int kk = (tid >> 4) + 16 * r;
-      const int j = kt * kKeyTile + kk;
-      reg[r] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < kend) reg[r] = ldg128(kbase + (size_t)(base + j) * Hkv * kHeadDim + (tid & 15) * 8);
+      const int key = 16 * w + 4 * r + (l >> 4);
+      const int j = min(kt * kKeyTile + key, kend - 1);
+      const int ch = (l & 15) ^ (key & 15);
+      const uint16_t* src = kbase + (size_t)(base + j) * Hkv * kHeadDim + ch * 8;
+      const uint32_t dst = lds_ring + (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
     }
   };
-  auto store_tile = [&](int buf, const uint4 (&reg)[4]) {
+  auto lds_barrier = [&]() HS2_INLINE {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // Wait until the oldest outstanding tile has landed while `younger` later tiles
+  // (4 loads each) may still be in flight, then the barrier. Loads complete in
+  // issue order, so vmcnt <= 4 * younger suffices; global stores issued in
+  // between only make the wait stricter.
+  auto ring_ready = [&](int younger) HS2_INLINE {
+    // s_waitcnt immediate: vmcnt in bits 3:0, expcnt 6:4 = 7 and lgkmcnt 11:8 = 15 (no wait)
+    if (younger >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);       // vmcnt(12)
+    else if (younger == 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+    lds_barrier();
+  };
+  // Streams tiles first, first + step, ... (n of them) of keys below kend through
+  // NS ring slots, NS - 1 tiles ahead; body(kt, slot). Ends with every load landed
+  // and every wave past its last LDS read.
+  auto sweep = [&](int n, int first, int step, int kend, auto NSc, auto&& body) HS2_INLINE {
+    constexpr int NS = decltype(NSc)::value;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int kk = (tid >> 4) + 16 * r;
-      sm.ktile[buf][kk][(tid & 15) ^ (kk & 15)] = reg[r];
+    for (int i = 0; i < NS - 1; i++)
+      if (i < n) dma_tile(first + i * step, kend, i);
+    for (int i = 0; i < n; i++) {
+      ring_ready(min(NS - 2, n - 1 - i));
+      // every wave is past tile i - 1, so its slot can take tile i + NS - 1
+      if (i + NS - 1 < n) dma_tile(first + (i + NS - 1) * step, kend, (i + NS - 1) % NS);
+      body(first + i * step, i % NS);
+    }
+    lds_barrier();
+  };
+  // acc = q . k - rref[row]: the MFMAs accumulate onto the row reference
+  f32x16 acc[RT][2];
+  auto compute = [&](int buf) HS2_INLINE {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float4 r4 = *reinterpret_cast<const float4*>(&sm.rref[w * ROWS_W + 32 * rt + 8 * i + 4 * h5]);
+        acc[rt][0][4 * i + 0] = -r4.x;
+        acc[rt][0][4 * i + 1] = -r4.y;
+        acc[rt][0][4 * i + 2] = -r4.z;
+        acc[rt][0][4 * i + 3] = -r4.w;
+      }
+      acc[rt][1] = acc[rt][0];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ct++) {
+      const int kk = 32 * ct + c5;
+#pragma unroll
+      for (int ks = 0; ks < 8; ks++) {
+        const bf16x8 b = as_bf16x8(to_u32x4(sm.u.ktile[buf][kk][(2 * ks + h5) ^ (kk & 15)]));
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) acc[rt][ct] = mfma32x32x16(qa[rt][ks], b, acc[rt][ct]);
+      }
     }
   };
-  f32x4 acc[RT][4];
-  auto compute = [&](int buf) {
+  // keys beyond a row's token are -inf (only tiles that reach past t0)
+  auto mask_causal = [&](int kt) HS2_INLINE {
+    if (kt * kKeyTile + kKeyTile - 1 <= t0) return;
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 16; r++) {
+        const int t = t0 + row_of(rt, r) / G;
 #pragma unroll
-    for (int ct = 0; ct < 4; ct++) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        const int kk = 16 * ct + lc;
-        const bf16x8 b = as_bf16x8(to_u32x4(sm.ktile[buf][kk][(4 * ks + lq) ^ lc]));
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++) acc[rt][ct] = mfma16x16x32(qa[rt][ks], b, acc[rt][ct]);
+        for (int ct = 0; ct < 2; ct++)
+          if (kt * kKeyTile + 32 * ct + c5 > t) acc[rt][ct][r] = -INFINITY;
       }
-    }
   };
+  using Ring = std::integral_constant<int, kRing>;
+  using Pair = std::integral_constant<int, 2>;
 
   // ======================= sweep 1: row statistics ==========================
-  float m_run[RT][4], l_run[RT][4];
+  // lsum = sum_j exp2(c (q . k_j - rref)) over the causal keys, with rref the
+  // Cauchy-Schwarz bound. If that bound is so loose that some row's sum falls
+  // below 2^-60, a max-only sweep first sets rref to each row's exact maximum
+  // and the sum is taken again.
+  const int kend1 = t0 + ntok;
+  const int n_kt1 = ceil_div(kend1, kKeyTile);
+  float lsum[RT][16];
+  auto sum_sweep = [&]() HS2_INLINE {
+    lds_barrier();  // rref
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) lsum[rt][r] = 0.f;
+    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) {
+      compute(buf);
+      mask_causal(kt);
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          lsum[rt][r] += fast_exp2(acc[rt][0][r] * c) + fast_exp2(acc[rt][1][r] * c);
+    });
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float s = lsum[rt][r];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) s += shfl_xor_f(s, off);
+        lsum[rt][r] = s;
+      }
+  };
+  sum_sweep();
+  {
+    bool bad = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) bad |= (row_of(rt, r) / G < ntok) && !(lsum[rt][r] >= 0x1p-60f);
+    if (tid == 0) sm.unsafe = 0;
+    __syncthreads();
+    if (bad) sm.unsafe = 1;
+    __syncthreads();
+  }
+  if (sm.unsafe) {
+    // max-only sweep: rref <- max_j q . k_j per row, then the sum again
+    float mx[RT][16];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) mx[rt][r] = -INFINITY;
+    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) {
+      compute(buf);
+      mask_causal(kt);
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) mx[rt][r] = fmaxf(mx[rt][r], fmaxf(acc[rt][0][r], acc[rt][1][r]));
+    });
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float m = mx[rt][r];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+        // acc held q . k - rref, so the new reference is rref + m
+        if (c5 == 0) sm.rref[row_of(rt, r)] += m;
+      }
+    sum_sweep();
+  }
+  // lse2 = c * rref + log2(lsum); from here on rref = lse2 / c, so that
+  // exp2(c * acc) is the full layer's probability
+  lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) { m_run[rt][i] = -1e30f; l_run[rt][i] = 0.f; }  // finite: no inf-inf
-
-  {
-    const int kend = t0 + ntok;
-    const int n_kt = ceil_div(kend, kKeyTile);
-    uint4 reg[4];
-    load_tile(0, kend, reg);
-    store_tile(0, reg);
-    __syncthreads();
-    constexpr float kSlack = 8.f;  // log2 units a score may exceed the row reference
-    for (int kt = 0; kt < n_kt; kt++) {
-      if (kt + 1 < n_kt) load_tile(kt + 1, kend, reg);
-      compute(kt & 1);
-      const bool diag = kt * kKeyTile + kKeyTile - 1 > t0;  // some key may lie beyond a token
-      if (diag) {
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int t = t0 + (w * ROWS_W + 16 * rt + 4 * lq + i) / G;
-#pragma unroll
-            for (int ct = 0; ct < 4; ct++)
-              if (kt * kKeyTile + 16 * ct + lc > t) acc[rt][ct][i] = -INFINITY;
-          }
-      }
-      // the row reference m only moves when a score passes it by the slack (so no
-      // term exceeds 2^slack); moving it rescales l. Raw accumulators compare
-      // directly since the scale c is positive.
-      bool move = false;
-      float mx[RT][4];
-#pragma unroll
-      for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          mx[rt][i] = fmaxf(fmaxf(acc[rt][0][i], acc[rt][1][i]), fmaxf(acc[rt][2][i], acc[rt][3][i])) * c;
-          move |= mx[rt][i] > m_run[rt][i] + kSlack;
-        }
-      if (__any(move)) {
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float mn = fmaxf(m_run[rt][i], mx[rt][i]);
-            l_run[rt][i] *= fast_exp2(m_run[rt][i] - mn);
-            m_run[rt][i] = mn;
-          }
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float mneg = -m_run[rt][i];
-          float sum = 0.f;
-#pragma unroll
-          for (int ct = 0; ct < 4; ct++) sum += fast_exp2(fmaf(acc[rt][ct][i], c, mneg));
-          l_run[rt][i] += sum;
-        }
-      if (kt + 1 < n_kt) store_tile((kt + 1) & 1, reg);
-      __syncthreads();
+    for (int r = 0; r < 16; r++) {
+      const int row = row_of(rt, r);
+      const float lse = fmaf(c, sm.rref[row], fast_log2(lsum[rt][r]));
+      lsum[rt][r] = lse;
     }
-  }
-
-  // combine the 16 lanes that share a row, then lse2 = m + log2(l)
-  float lse[RT][4];
+  lds_barrier();
 #pragma unroll
-  for (int rt = 0; rt < RT; rt++) {
+  for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      float m = m_run[rt][i], s = l_run[rt][i];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float mo = shfl_xor_f(m, off), so = shfl_xor_f(s, off);
-        const float mn = fmaxf(m, mo);
-        const float a = s * fast_exp2(m - mn);  // m, mo finite (>= -1e30)
-        const float b = so * fast_exp2(mo - mn);
-        s = a + b;
-        m = mn;
+    for (int r = 0; r < 16; r++) {
+      const int row = row_of(rt, r);
+      if (c5 == 0) {
+        sm.rref[row] = lsum[rt][r] / c;
+        if (row / G < ntok) p.lse2[(size_t)(base + t0 + row / G) * Hq + g * G + row % G] = lsum[rt][r];
       }
-      lse[rt][i] = m + fast_log2(s);
-      const int r = w * ROWS_W + 16 * rt + 4 * lq + i;
-      const int tl = r / G, hl = r % G;
-      if (lc == 0 && tl < ntok) p.lse2[(size_t)(base + t0 + tl) * Hq + g * G + hl] = lse[rt][i];
     }
-  }
 
   // ===================== per-token selection mode ===========================
   const int cand_end = t0 + ntok - W;  // candidates of the last token are [0, cand_end)
@@ -235,7 +401,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     sm.cnt[tid] = 0;
   }
   if (tid == 0) { sm.any_sample = 0; sm.any_emit = 0; }
-  for (int i = tid; i < 64 * (kBins / 2); i += kSelThreads) (&sm.hist[0][0])[i] = 0u;
+  for (int i = tid; i < TOK * (kBins / 2); i += kSelThreads) (&sm.u.s.hist[0][0])[i] = 0u;
   __syncthreads();
   if (tid < TOK) {
     if (sm.mode[tid] == kModeSample) atomicOr(&sm.any_sample, 1);
@@ -243,57 +409,63 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   }
   __syncthreads();
 
-  // group score of the lane's token(s) for accumulator (rt, ct); emits per token u
-  auto group_scores = [&](int rt, int ct, float (&S)[NT]) {
-    float e[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) e[i] = fast_exp2(fmaf(acc[rt][ct][i], c, -lse[rt][i]));
+  // group scores of accumulator tile (rt, ct): S[e] for the lane's elements
+  auto group_scores = [&](int rt, int ct, float (&S)[NE]) HS2_INLINE {
+    auto e = [&](int r) HS2_INLINE { return fast_exp2(acc[rt][ct][r] * c); };
     if constexpr (G == 1) {
 #pragma unroll
-      for (int u = 0; u < NT; u++) S[u] = e[u];
+      for (int i = 0; i < 16; i++) S[i] = e(i);
     } else if constexpr (G == 2) {
-      S[0] = e[0] + e[1];
-      S[1] = e[2] + e[3];
+#pragma unroll
+      for (int i = 0; i < 8; i++) S[i] = e(2 * i) + e(2 * i + 1);
+    } else if constexpr (G == 16) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; r++) s += e(8 * i + r);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
+                                                         false, false);
+        S[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
     } else {
-      float part = (e[0] + e[1]) + (e[2] + e[3]);
-      if constexpr (G >= 8) part += shfl_xor_f(part, 16);
-      if constexpr (G >= 16) part += shfl_xor_f(part, 32);
-      S[0] = part;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float s = (e(4 * i) + e(4 * i + 1)) + (e(4 * i + 2) + e(4 * i + 3));
+        if constexpr (G == 8) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s),
+                                                           __float_as_uint(s), false, false);
+          s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        S[i] = s;
+      }
     }
   };
-  // local token index of the lane's u-th token in row tile rt; owner lanes only
-  auto token_of = [&](int rt, int u) { return (w * ROWS_W + 16 * rt + 4 * lq) / G + u; };
-  const bool owner = (G <= 4) || (G == 8 ? ((lq & 1) == 0) : (lq == 0));
 
   // ========================= sweep 2: sample ================================
   if (sm.any_sample) {
-    for (int kt = 0; kt < n_kt2; kt += kSampleStride) {
-      uint4 reg[4];
-      load_tile(kt, cand_end, reg);
-      store_tile(0, reg);
-      __syncthreads();
-      compute(0);
+    sweep(ceil_div(n_kt2, kSampleStride), 0, kSampleStride, cand_end, Pair{}, [&](int kt, int buf) {
+      compute(buf);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ct++) {
-          float S[NT];
+        for (int ct = 0; ct < 2; ct++) {
+          float S[NE];
           group_scores(rt, ct, S);
-          const int j = kt * kKeyTile + 16 * ct + lc;
+          const int j = kt * kKeyTile + 32 * ct + c5;
 #pragma unroll
-          for (int u = 0; u < NT; u++) {
-            const int tl = token_of(rt, u);
+          for (int e = 0; e < NE; e++) {
+            const int tl = token_of(rt, e);
             if (owner && tl < TOK && sm.mode[tl] == kModeSample && j <= t0 + tl - W) {
-              int bin = (int)(__float_as_uint(S[u]) >> 20) - p.bin_base;
+              int bin = (int)(__float_as_uint(S[e]) >> 20) - p.bin_base;
               bin = min(max(bin, 0), kBins - 1);
-              atomicAdd(&sm.hist[tl][bin >> 1], (bin & 1) ? 65536u : 1u);
+              atomicAdd(&sm.u.s.hist[tl][bin >> 1], (bin & 1) ? 65536u : 1u);
             }
           }
         }
       }
-      __syncthreads();
-    }
-    // threshold: lower edge of the bin where the top count reaches r
+    });
+    // threshold: interpolated where the sample's top count reaches r
     if (tid < TOK && sm.mode[tid] == kModeSample) {
       const int t = t0 + tid, n_c = t - W + 1;
       int n_s = 0;
@@ -304,7 +476,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
       if (r <= n_s) {
         int cum = 0;
         for (int b = kBins - 1; b >= 1; b--) {
-          const uint32_t wd = sm.hist[tid][b >> 1];
+          const uint32_t wd = sm.u.s.hist[tid][b >> 1];
           const int h = (b & 1) ? (int)(wd >> 16) : (int)(wd & 0xFFFFu);
           cum += h;
           if (cum >= r) {
@@ -327,65 +499,58 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 
   // ========================= sweep 3: collect ===============================
   if (sm.any_emit) {
-    float tau_r[RT][NT];
-    int nc_r[RT][NT];
+    float tau_r[RT][NE];
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int u = 0; u < NT; u++) {
-        const int tl = token_of(rt, u);
+      for (int e = 0; e < NE; e++) {
+        const int tl = token_of(rt, e);
         const bool emit = owner && tl < TOK && sm.mode[tl] == kModeEmit;
-        tau_r[rt][u] = emit ? sm.tau[tl] : INFINITY;
-        nc_r[rt][u] = emit ? t0 + tl - W + 1 : 0;
+        tau_r[rt][e] = emit ? sm.tau[tl] : INFINITY;
       }
     uint64_t* cand = p.cand;
     const int C = p.cand_cap;
-    uint4 reg[4];
-    load_tile(0, cand_end, reg);
-    store_tile(0, reg);
-    __syncthreads();
-    for (int kt = 0; kt < n_kt2; kt++) {
-      if (kt + 1 < n_kt2) load_tile(kt + 1, cand_end, reg);
-      compute(kt & 1);
+    const int nc_min = t0 - W + 1;  // every token's candidates include [0, nc_min)
+    sweep(n_kt2, 0, 1, cand_end, Ring{}, [&](int kt, int buf) {
+      compute(buf);
+      const bool tail = kt * kKeyTile + kKeyTile > nc_min;  // some key may be past a token's range
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
-        float Sv[4][NT];
-        uint32_t pass[NT];
+        float Sv[2][NE];
+        uint32_t pass[NE];
 #pragma unroll
-        for (int u = 0; u < NT; u++) pass[u] = 0u;
+        for (int e = 0; e < NE; e++) pass[e] = 0u;
 #pragma unroll
-        for (int ct = 0; ct < 4; ct++) {
-          float S[NT];
-          group_scores(rt, ct, S);
-          const int j = kt * kKeyTile + 16 * ct + lc;
+        for (int ct = 0; ct < 2; ct++) {
+          group_scores(rt, ct, Sv[ct]);
+          const int j = kt * kKeyTile + 32 * ct + c5;
 #pragma unroll
-          for (int u = 0; u < NT; u++) {
-            Sv[ct][u] = S[u];
-            pass[u] |= (S[u] >= tau_r[rt][u] && j < nc_r[rt][u]) ? (1u << ct) : 0u;
+          for (int e = 0; e < NE; e++) {
+            bool ok = Sv[ct][e] >= tau_r[rt][e];
+            if (tail) ok = ok && j <= t0 + token_of(rt, e) - W;
+            pass[e] |= ok ? (1u << ct) : 0u;
           }
         }
-        // one LDS atomic per lane and token for its (up to 4) passing keys
+        // one LDS atomic per lane and token for its (up to 2) passing keys
 #pragma unroll
-        for (int u = 0; u < NT; u++) {
-          if (pass[u]) {
-            const int tl = token_of(rt, u);
-            int pos = atomicAdd(&sm.cnt[tl], __popc(pass[u]));
+        for (int e = 0; e < NE; e++) {
+          if (pass[e]) {
+            const int tl = token_of(rt, e);
+            int pos = atomicAdd(&sm.cnt[tl], __popc(pass[e]));
             uint64_t* dst = cand + (size_t)(slot0 + tl) * C;
 #pragma unroll
-            for (int ct = 0; ct < 4; ct++) {
-              if ((pass[u] >> ct) & 1u) {
+            for (int ct = 0; ct < 2; ct++) {
+              if ((pass[e] >> ct) & 1u) {
                 if (pos < C)
-                  dst[pos] = ((uint64_t)__float_as_uint(Sv[ct][u]) << 32) |
-                             (uint32_t)(kt * kKeyTile + 16 * ct + lc);
+                  dst[pos] = ((uint64_t)__float_as_uint(Sv[ct][e]) << 32) |
+                             (uint32_t)(kt * kKeyTile + 32 * ct + c5);
                 pos++;
               }
             }
           }
         }
       }
-      if (kt + 1 < n_kt2) store_tile((kt + 1) & 1, reg);
-      __syncthreads();
-    }
+    });
   }
 
   // ============================ row verdicts ================================
