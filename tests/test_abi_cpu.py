@@ -177,4 +177,4 @@ def test_planner_covers_every_tile_once_longest_first(lib, lengths, tok):
 
 
 def test_tokens_per_task_matches_kernel_geometry():
-    assert [hs2.tokens_per_task(g) for g in (1, 2, 4, 8, 16)] == [128, 64, 64, 32, 16]
+    assert [hs2.tokens_per_task(g) for g in (1, 2, 4, 8, 16)] == [64, 64, 64, 32, 16]

@@ -195,5 +195,5 @@ def hs2_version() -> int:
 
 def tokens_per_task(G: int) -> int:
     """Tokens of one selection task (workgroup) for group size G."""
-    rt = 2 if G >= 4 else 1
-    return 4 * 32 * rt // G
+    rt = 4 if G >= 4 else G
+    return 4 * 16 * rt // G

@@ -25,10 +25,10 @@ constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact
 constexpr float kTauAlpha = 1.2f;
 constexpr int kTauBeta = 24;
 
-// Scoring workgroups: 4 waves x 32 * score_row_tiles(G) MFMA rows (tokens x heads);
-// tokens per selection task (one workgroup): 128, 64, 64, 32, 16 for G = 1..16.
-__host__ __device__ constexpr int score_row_tiles(int G) { return G >= 4 ? 2 : 1; }
-__host__ __device__ constexpr int tokens_per_task(int G) { return 4 * 32 * score_row_tiles(G) / G; }
+// Scoring workgroups: 4 waves x 16 * score_row_tiles(G) MFMA rows (tokens x heads);
+// tokens per selection task (one workgroup): 64, 64, 64, 32, 16 for G = 1..16.
+__host__ __device__ constexpr int score_row_tiles(int G) { return G >= 4 ? 4 : G; }
+__host__ __device__ constexpr int tokens_per_task(int G) { return 4 * 16 * score_row_tiles(G) / G; }
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

@@ -1,19 +1,19 @@
 // select_scores.hip - the full-attention layer's scoring sweeps on gfx950.
 //
 // One workgroup owns TOK consecutive query tokens of one sequence and one KV
-// group g: all G query heads of the group, 4 * 32 * RT MFMA rows in token-major,
-// head-minor order, so the 32x32 accumulator rows a lane holds are the heads of
-// one or more whole tokens (or half a group, joined with the partner lane). It
-// sweeps the causal keys in 64-key tiles staged through LDS, with bf16
-// v_mfma_f32_32x32x16_bf16 and fp32 accumulation, three times:
+// group g: all G query heads of the group, 4 waves x 16 * RT MFMA rows in
+// token-major, head-minor order, so the 4 accumulator rows a lane holds are the
+// heads of whole tokens (G <= 4) or a share of one token (G = 8, 16; joined with
+// the partner lane groups). It sweeps the causal keys in 64-key tiles streamed
+// through an LDS ring, with bf16 v_mfma_f32_16x16x32_bf16 and fp32 accumulation:
 //
 //  1. row statistics: per (t, h) the log2-domain log-sum-exp lse2 of the full
 //     layer's softmax over all causal keys with scale 1/sqrt(d) (attention as in
 //     the SHARP walkthrough, section 1.1). The exponents are taken against a
 //     fixed per-row reference, the Cauchy-Schwarz bound c * |q| * max_j |k_j|,
-//     so the sweep needs no running maximum; if that bound is too loose for
-//     some row (sum below 2^-60) the workgroup redoes the sweep with a lazily
-//     moved running maximum.
+//     which the MFMAs subtract as their initial accumulator, so the sweep needs
+//     no running maximum; if that bound is too loose for some row (sum below
+//     2^-60) the workgroup first finds each row's exact maximum and sums again.
 //  2. sample: on every 8th key tile, the group score
 //       S[t,g,j] = sum_{h in g} exp2(z2[t,h,j] - lse2[t,h])
 //     (the full layer's probabilities, summed over the group whose KV cache
@@ -26,6 +26,8 @@
 //
 // A row whose candidates are too many (> C) or too few (< K) is sent to the
 // exact path (select_topk.hip), so the result never depends on the sample.
+#include <type_traits>
+
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -33,22 +35,13 @@ namespace hs2 {
 
 enum : int { kModeTrivial = 0, kModeEmit = 1, kModeExact = 2, kModeSample = 3 };
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// C[32x32] += A[32x16] * B[16x32], bf16 in, fp32 accumulate. Lane l supplies A row
-// (l & 31), k = 8*(l >> 5) .. +7 and B column (l & 31), same k; it receives C
-// column (l & 31), rows 8*(r >> 2) + 4*(l >> 5) + (r & 3) for register r.
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 template <int G>
 struct ScoreCfg {
-  static constexpr int RT = score_row_tiles(G);       // 32-row tiles per wave
-  static constexpr int ROWS_W = 32 * RT;              // MFMA rows per wave
-  static constexpr int TOK = tokens_per_task(G);      // tokens per workgroup
-  // group elements (token sums) per lane per 32x32 accumulator tile
-  static constexpr int NE = G == 1 ? 16 : G == 2 ? 8 : G == 16 ? 2 : 4;
+  static constexpr int RT = score_row_tiles(G);   // 16-row tiles per wave
+  static constexpr int ROWS_W = 16 * RT;          // MFMA rows per wave
+  static constexpr int TOK = tokens_per_task(G);  // tokens per workgroup
+  // tokens whose rows a lane holds per accumulator tile: 4 (G = 1), 2 (G = 2), else 1
+  static constexpr int NT = G >= 4 ? 1 : 4 / G;
 };
 
 constexpr int kRing = 4;  // K tiles in flight: compute tile kt while kt+1..kt+3 load
@@ -56,7 +49,7 @@ constexpr int kRing = 4;  // K tiles in flight: compute tile kt while kt+1..kt+3
 template <int TOK>
 struct ScoreSmem {
   // A ring of kRing 64-key x 256-byte K tiles (XOR-swizzled 16-byte chunks). The
-  // sample sweep uses tiles 0-1 only and keeps its histogram where tiles 2.. live.
+  // sample sweep uses tiles 0-1 only and keeps its histogram where tiles 2-3 live.
   union {
     uint4 ktile[kRing][kKeyTile][16];
     struct {
@@ -64,7 +57,7 @@ struct ScoreSmem {
       uint32_t hist[TOK][kBins / 2];  // two 16-bit bin counters per word
     } s;
   } u;
-  float rref[256];                   // per-MFMA-row reference subtracted from q . k
+  float nref[256];                   // minus the reference of each MFMA row
   float tau[TOK];
   int32_t cnt[TOK];
   int32_t mode[TOK];
@@ -137,11 +130,12 @@ hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv
 template <int G>
 __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   using Cfg = ScoreCfg<G>;
-  constexpr int RT = Cfg::RT, TOK = Cfg::TOK, ROWS_W = Cfg::ROWS_W, NE = Cfg::NE;
+  constexpr int RT = Cfg::RT, TOK = Cfg::TOK, ROWS_W = Cfg::ROWS_W, NT = Cfg::NT;
+  static_assert(TOK <= 64, "the histogram overlays two ring slots");
   __shared__ ScoreSmem<TOK> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int h5 = l >> 5, c5 = l & 31;
+  const int lq = l >> 4, lc = l & 15;
   const int g = blockIdx.x % p.Hkv;
   const int64_t task = p.task_begin + blockIdx.x / p.Hkv;
   int seq, tile;
@@ -154,31 +148,28 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   const int Hq = p.Hq, Hkv = p.Hkv, K = p.K, W = p.W;
   const float c = p.c;
 
-  // accumulator register r of row tile rt holds wave row 32 rt + 8 (r >> 2) + 4 h5 + (r & 3)
-  auto row_of = [&](int rt, int r) HS2_INLINE { return w * ROWS_W + 32 * rt + 8 * (r >> 2) + 4 * h5 + (r & 3); };
-  // first register of group element e (the heads of one token, or half of them)
-  auto first_reg = [&](int e) HS2_INLINE {
-    if constexpr (G == 1) return e;
-    else if constexpr (G == 2) return 4 * (e >> 1) + 2 * (e & 1);
-    else if constexpr (G == 16) return 8 * e;
-    else return 4 * e;
-  };
-  auto token_of = [&](int rt, int e) HS2_INLINE { return row_of(rt, first_reg(e)) / G; };
-  const bool owner = (G <= 4) || h5 == 0;  // for G >= 8 lanes l and l ^ 32 share a token
+  // accumulator element i of row tile rt: wave row 16 rt + 4 lq + i, key lc of its
+  // 16-key column tile
+  auto row_of = [&](int rt, int i) HS2_INLINE { return w * ROWS_W + 16 * rt + 4 * lq + i; };
+  // local token of the lane's u-th token in row tile rt
+  auto token_of = [&](int rt, int u) HS2_INLINE { return (w * ROWS_W + 16 * rt + 4 * lq) / G + u; };
+  // lanes holding a token's first rows (G = 8 and 16 spread a token over lane groups)
+  const bool owner = (G <= 4) || (G == 8 ? ((lq & 1) == 0) : (lq == 0));
 
-  // ---- Q operands (A): row ra (token-major, head-minor), d = 16 ks + 8 h5 .. +7 ----
-  bf16x8 qa[RT][8];
+  // ---- Q operands (A): row ra (token-major, head-minor), d = 32 ks + 8 lq .. +7 ----
+  bf16x8 qa[RT][4];
+  const float kmax = __uint_as_float(p.kmax[seq * Hkv + g]);
 #pragma unroll
   for (int rt = 0; rt < RT; rt++) {
-    const int ra = w * ROWS_W + 32 * rt + c5;
+    const int ra = w * ROWS_W + 16 * rt + lc;
     const int ta = ra / G, ha = ra % G;
     float qn2 = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ks++) {
+    for (int ks = 0; ks < 4; ks++) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ta < ntok)
         v = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
-                            16 * ks + 8 * h5));
+                            32 * ks + 8 * lq));
       qa[rt][ks] = as_bf16x8(v);
 #pragma unroll
       for (int u = 0; u < 4; u++) {
@@ -186,11 +177,10 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
         qn2 = fmaf(a, a, fmaf(b, b, qn2));
       }
     }
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(qn2), __float_as_uint(qn2),
-                                                     false, false);
-    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    qn2 += shfl_xor_f(qn2, 16);
+    qn2 += shfl_xor_f(qn2, 32);
     // reference of sweep 1: the Cauchy-Schwarz bound |q| * max_j |k_j| >= q . k_j
-    if (h5 == 0) sm.rref[ra] = sqrtf(tot) * __uint_as_float(p.kmax[seq * Hkv + g]);
+    if (lq == 0) sm.nref[ra] = -(sqrtf(qn2) * kmax);
   }
 
   // K tiles go global -> LDS directly (no staging registers). One load moves 4
@@ -206,9 +196,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   auto dma_tile = [&](int kt, int kend, int buf) HS2_INLINE {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int key = 16 * w + 4 * r + (l >> 4);
+      const int key = 16 * w + 4 * r + lq;
       const int j = min(kt * kKeyTile + key, kend - 1);
-      const int ch = (l & 15) ^ (key & 15);
+      const int ch = lc ^ (key & 15);
       const uint16_t* src = kbase + (size_t)(base + j) * Hkv * kHeadDim + ch * 8;
       const uint32_t dst = lds_ring + (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
       asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
@@ -247,29 +237,24 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     }
     lds_barrier();
   };
-  // acc = q . k - rref[row]: the MFMAs accumulate onto the row reference
-  f32x16 acc[RT][2];
+  // acc = q . k - rref[row]: the first MFMA of each chain starts from -rref
+  f32x4 acc[RT][4];
+  f32x4 nref4[RT];
+  auto load_nref = [&]() HS2_INLINE {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+      nref4[rt] = *reinterpret_cast<const f32x4*>(&sm.nref[w * ROWS_W + 16 * rt + 4 * lq]);
+  };
   auto compute = [&](int buf) HS2_INLINE {
 #pragma unroll
-    for (int rt = 0; rt < RT; rt++) {
+    for (int ct = 0; ct < 4; ct++) {
+      const int kk = 16 * ct + lc;  // kk & 15 == lc
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float4 r4 = *reinterpret_cast<const float4*>(&sm.rref[w * ROWS_W + 32 * rt + 8 * i + 4 * h5]);
-        acc[rt][0][4 * i + 0] = -r4.x;
-        acc[rt][0][4 * i + 1] = -r4.y;
-        acc[rt][0][4 * i + 2] = -r4.z;
-        acc[rt][0][4 * i + 3] = -r4.w;
-      }
-      acc[rt][1] = acc[rt][0];
-    }
+      for (int ks = 0; ks < 4; ks++) {
+        const bf16x8 b = as_bf16x8(to_u32x4(sm.u.ktile[buf][kk][(4 * ks + lq) ^ lc]));
 #pragma unroll
-    for (int ct = 0; ct < 2; ct++) {
-      const int kk = 32 * ct + c5;
-#pragma unroll
-      for (int ks = 0; ks < 8; ks++) {
-        const bf16x8 b = as_bf16x8(to_u32x4(sm.u.ktile[buf][kk][(2 * ks + h5) ^ (kk & 15)]));
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++) acc[rt][ct] = mfma32x32x16(qa[rt][ks], b, acc[rt][ct]);
+        for (int rt = 0; rt < RT; rt++)
+          acc[rt][ct] = mfma16x16x32(qa[rt][ks], b, ks == 0 ? nref4[rt] : acc[rt][ct]);
       }
     }
   };
@@ -279,47 +264,47 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int t = t0 + row_of(rt, r) / G;
+      for (int i = 0; i < 4; i++) {
+        const int t = t0 + row_of(rt, i) / G;
 #pragma unroll
-        for (int ct = 0; ct < 2; ct++)
-          if (kt * kKeyTile + 32 * ct + c5 > t) acc[rt][ct][r] = -INFINITY;
+        for (int ct = 0; ct < 4; ct++)
+          if (kt * kKeyTile + 16 * ct + lc > t) acc[rt][ct][i] = -INFINITY;
       }
   };
   using Ring = std::integral_constant<int, kRing>;
   using Pair = std::integral_constant<int, 2>;
 
   // ======================= sweep 1: row statistics ==========================
-  // lsum = sum_j exp2(c (q . k_j - rref)) over the causal keys, with rref the
-  // Cauchy-Schwarz bound. If that bound is so loose that some row's sum falls
-  // below 2^-60, a max-only sweep first sets rref to each row's exact maximum
-  // and the sum is taken again.
+  // lsum = sum_j exp2(c (q . k_j - rref)) over the causal keys; a row's 16 lanes
+  // (one per key column) are summed at the end.
   const int kend1 = t0 + ntok;
   const int n_kt1 = ceil_div(kend1, kKeyTile);
-  float lsum[RT][16];
+  float lsum[RT][4];
   auto sum_sweep = [&]() HS2_INLINE {
-    lds_barrier();  // rref
+    lds_barrier();  // nref
+    load_nref();
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) lsum[rt][r] = 0.f;
-    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) {
+      for (int i = 0; i < 4; i++) lsum[rt][i] = 0.f;
+    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) HS2_INLINE {
       compute(buf);
       mask_causal(kt);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++)
-          lsum[rt][r] += fast_exp2(acc[rt][0][r] * c) + fast_exp2(acc[rt][1][r] * c);
+        for (int i = 0; i < 4; i++)
+          lsum[rt][i] += (fast_exp2(acc[rt][0][i] * c) + fast_exp2(acc[rt][1][i] * c)) +
+                         (fast_exp2(acc[rt][2][i] * c) + fast_exp2(acc[rt][3][i] * c));
     });
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        float s = lsum[rt][r];
+      for (int i = 0; i < 4; i++) {
+        float s = lsum[rt][i];
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) s += shfl_xor_f(s, off);
-        lsum[rt][r] = s;
+        for (int off = 1; off < 16; off <<= 1) s += shfl_xor_f(s, off);
+        lsum[rt][i] = s;
       }
   };
   sum_sweep();
@@ -328,36 +313,39 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) bad |= (row_of(rt, r) / G < ntok) && !(lsum[rt][r] >= 0x1p-60f);
+      for (int i = 0; i < 4; i++) bad |= (row_of(rt, i) / G < ntok) && !(lsum[rt][i] >= 0x1p-60f);
     if (tid == 0) sm.unsafe = 0;
     __syncthreads();
     if (bad) sm.unsafe = 1;
     __syncthreads();
   }
   if (sm.unsafe) {
-    // max-only sweep: rref <- max_j q . k_j per row, then the sum again
-    float mx[RT][16];
+    // the bound is too loose for some row: rref <- the row's exact maximum of
+    // q . k_j, then the sum again
+    float mx[RT][4];
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) mx[rt][r] = -INFINITY;
-    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) {
+      for (int i = 0; i < 4; i++) mx[rt][i] = -INFINITY;
+    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) HS2_INLINE {
       compute(buf);
       mask_causal(kt);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) mx[rt][r] = fmaxf(mx[rt][r], fmaxf(acc[rt][0][r], acc[rt][1][r]));
+        for (int i = 0; i < 4; i++)
+          mx[rt][i] = fmaxf(mx[rt][i], fmaxf(fmaxf(acc[rt][0][i], acc[rt][1][i]),
+                                             fmaxf(acc[rt][2][i], acc[rt][3][i])));
     });
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        float m = mx[rt][r];
+      for (int i = 0; i < 4; i++) {
+        float m = mx[rt][i];
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
         // acc held q . k - rref, so the new reference is rref + m
-        if (c5 == 0) sm.rref[row_of(rt, r)] += m;
+        if (lc == 0) sm.nref[row_of(rt, i)] -= m;
       }
     sum_sweep();
   }
@@ -367,20 +355,16 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 #pragma unroll
   for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int row = row_of(rt, r);
-      const float lse = fmaf(c, sm.rref[row], fast_log2(lsum[rt][r]));
-      lsum[rt][r] = lse;
-    }
+    for (int i = 0; i < 4; i++) lsum[rt][i] = fmaf(-c, nref4[rt][i], fast_log2(lsum[rt][i]));
   lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int row = row_of(rt, r);
-      if (c5 == 0) {
-        sm.rref[row] = lsum[rt][r] / c;
-        if (row / G < ntok) p.lse2[(size_t)(base + t0 + row / G) * Hq + g * G + row % G] = lsum[rt][r];
+    for (int i = 0; i < 4; i++) {
+      const int row = row_of(rt, i);
+      if (lc == 0) {
+        sm.nref[row] = -lsum[rt][i] / c;
+        if (row / G < ntok) p.lse2[(size_t)(base + t0 + row / G) * Hq + g * G + row % G] = lsum[rt][i];
       }
     }
 
@@ -408,56 +392,52 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     if (sm.mode[tid] == kModeEmit) atomicOr(&sm.any_emit, 1);
   }
   __syncthreads();
+  load_nref();
 
-  // group scores of accumulator tile (rt, ct): S[e] for the lane's elements
-  auto group_scores = [&](int rt, int ct, float (&S)[NE]) HS2_INLINE {
-    auto e = [&](int r) HS2_INLINE { return fast_exp2(acc[rt][ct][r] * c); };
+  // group scores of accumulator tile (rt, ct): S[u] for the lane's tokens
+  auto group_scores = [&](int rt, int ct, float (&S)[NT]) HS2_INLINE {
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) e[i] = fast_exp2(acc[rt][ct][i] * c);
     if constexpr (G == 1) {
 #pragma unroll
-      for (int i = 0; i < 16; i++) S[i] = e(i);
+      for (int u = 0; u < 4; u++) S[u] = e[u];
     } else if constexpr (G == 2) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) S[i] = e(2 * i) + e(2 * i + 1);
-    } else if constexpr (G == 16) {
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; r++) s += e(8 * i + r);
+      S[0] = e[0] + e[1];
+      S[1] = e[2] + e[3];
+    } else {
+      float s = (e[0] + e[1]) + (e[2] + e[3]);
+      if constexpr (G >= 8) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s),
+                                                         false, false);
+        s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      if constexpr (G >= 16) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
                                                          false, false);
-        S[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float s = (e(4 * i) + e(4 * i + 1)) + (e(4 * i + 2) + e(4 * i + 3));
-        if constexpr (G == 8) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s),
-                                                           __float_as_uint(s), false, false);
-          s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        S[i] = s;
-      }
+      S[0] = s;
     }
   };
 
   // ========================= sweep 2: sample ================================
   if (sm.any_sample) {
-    sweep(ceil_div(n_kt2, kSampleStride), 0, kSampleStride, cand_end, Pair{}, [&](int kt, int buf) {
+    sweep(ceil_div(n_kt2, kSampleStride), 0, kSampleStride, cand_end, Pair{},
+          [&](int kt, int buf) HS2_INLINE {
       compute(buf);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ct++) {
-          float S[NE];
+        for (int ct = 0; ct < 4; ct++) {
+          float S[NT];
           group_scores(rt, ct, S);
-          const int j = kt * kKeyTile + 32 * ct + c5;
+          const int j = kt * kKeyTile + 16 * ct + lc;
 #pragma unroll
-          for (int e = 0; e < NE; e++) {
-            const int tl = token_of(rt, e);
+          for (int u = 0; u < NT; u++) {
+            const int tl = token_of(rt, u);
             if (owner && tl < TOK && sm.mode[tl] == kModeSample && j <= t0 + tl - W) {
-              int bin = (int)(__float_as_uint(S[e]) >> 20) - p.bin_base;
+              int bin = (int)(__float_as_uint(S[u]) >> 20) - p.bin_base;
               bin = min(max(bin, 0), kBins - 1);
               atomicAdd(&sm.u.s.hist[tl][bin >> 1], (bin & 1) ? 65536u : 1u);
             }
@@ -499,51 +479,51 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 
   // ========================= sweep 3: collect ===============================
   if (sm.any_emit) {
-    float tau_r[RT][NE];
+    float tau_r[RT][NT];
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int e = 0; e < NE; e++) {
-        const int tl = token_of(rt, e);
+      for (int u = 0; u < NT; u++) {
+        const int tl = token_of(rt, u);
         const bool emit = owner && tl < TOK && sm.mode[tl] == kModeEmit;
-        tau_r[rt][e] = emit ? sm.tau[tl] : INFINITY;
+        tau_r[rt][u] = emit ? sm.tau[tl] : INFINITY;
       }
     uint64_t* cand = p.cand;
     const int C = p.cand_cap;
     const int nc_min = t0 - W + 1;  // every token's candidates include [0, nc_min)
-    sweep(n_kt2, 0, 1, cand_end, Ring{}, [&](int kt, int buf) {
+    sweep(n_kt2, 0, 1, cand_end, Ring{}, [&](int kt, int buf) HS2_INLINE {
       compute(buf);
       const bool tail = kt * kKeyTile + kKeyTile > nc_min;  // some key may be past a token's range
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
-        float Sv[2][NE];
-        uint32_t pass[NE];
+        float Sv[4][NT];
+        uint32_t pass[NT];
 #pragma unroll
-        for (int e = 0; e < NE; e++) pass[e] = 0u;
+        for (int u = 0; u < NT; u++) pass[u] = 0u;
 #pragma unroll
-        for (int ct = 0; ct < 2; ct++) {
+        for (int ct = 0; ct < 4; ct++) {
           group_scores(rt, ct, Sv[ct]);
-          const int j = kt * kKeyTile + 32 * ct + c5;
+          const int j = kt * kKeyTile + 16 * ct + lc;
 #pragma unroll
-          for (int e = 0; e < NE; e++) {
-            bool ok = Sv[ct][e] >= tau_r[rt][e];
-            if (tail) ok = ok && j <= t0 + token_of(rt, e) - W;
-            pass[e] |= ok ? (1u << ct) : 0u;
+          for (int u = 0; u < NT; u++) {
+            bool ok = Sv[ct][u] >= tau_r[rt][u];
+            if (tail) ok = ok && j <= t0 + token_of(rt, u) - W;
+            pass[u] |= ok ? (1u << ct) : 0u;
           }
         }
-        // one LDS atomic per lane and token for its (up to 2) passing keys
+        // one LDS atomic per lane and token for its (up to 4) passing keys
 #pragma unroll
-        for (int e = 0; e < NE; e++) {
-          if (pass[e]) {
-            const int tl = token_of(rt, e);
-            int pos = atomicAdd(&sm.cnt[tl], __popc(pass[e]));
+        for (int u = 0; u < NT; u++) {
+          if (pass[u]) {
+            const int tl = token_of(rt, u);
+            int pos = atomicAdd(&sm.cnt[tl], __popc(pass[u]));
             uint64_t* dst = cand + (size_t)(slot0 + tl) * C;
 #pragma unroll
-            for (int ct = 0; ct < 2; ct++) {
-              if ((pass[e] >> ct) & 1u) {
+            for (int ct = 0; ct < 4; ct++) {
+              if ((pass[u] >> ct) & 1u) {
                 if (pos < C)
-                  dst[pos] = ((uint64_t)__float_as_uint(Sv[ct][e]) << 32) |
-                             (uint32_t)(kt * kKeyTile + 32 * ct + c5);
+                  dst[pos] = ((uint64_t)__float_as_uint(Sv[ct][u]) << 32) |
+                             (uint32_t)(kt * kKeyTile + 16 * ct + lc);
                 pos++;
               }
             }
