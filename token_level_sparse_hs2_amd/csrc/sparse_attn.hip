@@ -9,11 +9,11 @@
 //   o[t,h] = sum_{j in I_t} exp(y_j - mu) v[j,g] / sum_{j in I_t} exp(y_j - mu),
 //   y_j = scale * <q'[t,h], k[j,g]>, g = h / G.
 //
-// One wavefront per (token, KV group): the K rows of a 32-entry chunk of I_t
-// are gathered straight into MFMA A operands (S^T = K_sel Q'^T, keys x heads,
-// all G heads of the group share the gather); the V rows are staged in the
-// wave's LDS slice and read back transposed as the A operand of
-// O^T = V^T P^T. Online softmax in the log2 domain, fp32 accumulation. P enters
+// One wavefront per (token, KV group), 32 index entries per step: the step's K
+// and V rows are gathered with full-row coalesced loads (16 lanes per 256-byte
+// row) into registers one step ahead, staged in the wave's LDS slice, and read
+// back as the A operands of S^T = K_sel Q'^T (keys x heads; all G heads of the
+// group share the gather) and, transposed, of O^T = V^T P^T. Online softmax in the log2 domain, fp32 accumulation. P enters
 // the matrix product as a sum of bf16 parts (two parts: ~16 mantissa bits; three
 // in the precise mode: ~24 bits), so rounding P to bf16 adds no visible error.
 #include "hs2_device.h"
@@ -62,11 +62,19 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   const int n_chunks = (KW + kChunk - 1) / kChunk;
 
   // index entries of chunk c for the lane's two A rows (keys 16*mt + lc)
-  auto load_idx = [&](int c, int (&j)[2]) {
+  // Index entries of chunk c for the lane's two A rows (keys 16*mt + lc). The raw
+  // load is unconditional (clamped to a valid entry) and its value is only used
+  // two chunks later by valid_idx(); loads skipped on some path, or consumed at
+  // once, would make the compiler drain the gather in flight behind them.
+  auto load_raw = [&](int c, int (&r)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) r[mt] = irow[min(c * kChunk + 16 * mt + lc, KW - 1)];
+  };
+  auto valid_idx = [&](int c, const int (&r)[2], int (&j)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       const int e = c * kChunk + 16 * mt + lc;
-      j[mt] = (c < n_chunks && e < KW) ? irow[e] : -1;
+      j[mt] = (c < n_chunks && e < KW) ? r[mt] : -1;
     }
   };
   // gather the chunk's K and V rows, fully coalesced: load r covers keys
@@ -196,24 +204,32 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
     }
   };
 
-  // software pipeline: the gather of chunk c+1 is in flight while chunk c computes
-  int ja[2], jb[2], jn[2];
+  // software pipeline: while chunk c computes, the gather of chunk c+1 and the
+  // index entries of chunks c+2 and c+3 are in flight. Entries past the row are
+  // -1: their gathers read row 0 and are skipped.
+  int r1[2], r2[2], ja[2], jb[2];
   Gather ga, gb;
-  load_idx(0, ja);
-  load_idx(1, jb);
+  load_raw(0, ja);
+  load_raw(1, r1);
+  load_raw(2, r2);
+  // keep this issue order (as in the loop body: idx entries older than the gather
+  // behind them), so the loop's waits can leave the gather in flight
+  __builtin_amdgcn_sched_barrier(0);
+  valid_idx(0, ja, ja);
   gather(ja, ga);
   for (int c = 0; c < n_chunks; c += 2) {
-    if (c + 1 < n_chunks) gather(jb, gb);
-    load_idx(c + 2, jn);
+    valid_idx(c + 1, r1, jb);
+    gather(jb, gb);
+    load_raw(c + 3, r1);
     consume(ja, ga);
-    if (c + 1 >= n_chunks) break;
-    ja[0] = jn[0]; ja[1] = jn[1];
-    if (c + 2 < n_chunks) gather(ja, ga);
-    load_idx(c + 3, jn);
+    // no early exit here: a chunk past the row has no valid entry and is skipped
+    // by consume(), and one exit keeps every path through the loop issuing the
+    // same loads in the same order
+    valid_idx(c + 2, r2, ja);
+    gather(ja, ga);
+    load_raw(c + 4, r2);
     consume(jb, gb);
-    jb[0] = jn[0]; jb[1] = jn[1];
   }
-
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
   if (lc < G) {
