@@ -157,19 +157,29 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   const bool owner = (G <= 4) || (G == 8 ? ((lq & 1) == 0) : (lq == 0));
 
   // ---- Q operands (A): row ra (token-major, head-minor), d = 32 ks + 8 lq .. +7 ----
+  // all loads first (rows past the sequence read its last token and are zeroed
+  // afterwards), so their latencies overlap
   bf16x8 qa[RT][4];
+  u32x4 qv[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) {
+    const int ra = w * ROWS_W + 16 * rt + lc;
+    const int ta = min(ra / G, ntok - 1), ha = ra % G;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+      qv[rt][ks] = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
+                                   32 * ks + 8 * lq));
+  }
   const float kmax = __uint_as_float(p.kmax[seq * Hkv + g]);
 #pragma unroll
   for (int rt = 0; rt < RT; rt++) {
     const int ra = w * ROWS_W + 16 * rt + lc;
-    const int ta = ra / G, ha = ra % G;
+    const bool live = ra / G < ntok;
     float qn2 = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ta < ntok)
-        v = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
-                            32 * ks + 8 * lq));
+      u32x4 v = qv[rt][ks];
+      if (!live) v = u32x4{0u, 0u, 0u, 0u};
       qa[rt][ks] = as_bf16x8(v);
 #pragma unroll
       for (int u = 0; u < 4; u++) {

@@ -300,15 +300,21 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   const uint64_t* cand = p.cand + (size_t)slot * p.cand_cap;
   uint32_t key[NREG], pos[NREG];
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  // every load of the row is issued before the first use (a use right after each
+  // load would wait out one memory latency per load); the guard is wave-uniform
+  const int count_u = __builtin_amdgcn_readfirstlane(count);
+  uint64_t ev[NREG];
 #pragma unroll
   for (int s = 0; s < NREG; s++) {
-    const int i = l + 64 * s;
-    key[s] = 0u;
-    pos[s] = 0u;
-    if (i < count) {
-      const uint64_t e = cand[i];
-      key[s] = (uint32_t)(e >> 32);
-      pos[s] = (uint32_t)e;
+    ev[s] = 0u;
+    if (64 * s < count_u) ev[s] = cand[min(l + 64 * s, p.cand_cap - 1)];
+  }
+#pragma unroll
+  for (int s = 0; s < NREG; s++) {
+    const bool in = l + 64 * s < count_u;
+    key[s] = in ? (uint32_t)(ev[s] >> 32) : 0u;
+    pos[s] = in ? (uint32_t)ev[s] : 0u;
+    if (in) {
       mn = min(mn, key[s]);
       mx = max(mx, key[s]);
     }
