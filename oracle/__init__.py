@@ -49,6 +49,11 @@ def _load():
     lib.hs2o_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, vp, vp, i64,
                                      vp, vp, i32]
     lib.hs2o_sparse_attn.restype = i32
+    lib.hs2o_decode_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, vp, vp, i32]
+    lib.hs2o_decode_select.restype = i32
+    lib.hs2o_decode_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, vp, vp,
+                                            vp, i32]
+    lib.hs2o_decode_sparse_attn.restype = i32
     lib.hs2o_bf16_round.argtypes = [f64]
     lib.hs2o_bf16_round.restype = ctypes.c_uint16
     _lib = lib
@@ -150,6 +155,59 @@ def sparse_attn(q, k, v, cu_seqlens, Hq, Hkv, idx, scale=None, tokens=None, nthr
                              nthreads or default_threads())
     if r != 0:
         raise ValueError("hs2o_sparse_attn: bad arguments")
+    return o64, o16
+
+
+def decode_select(q_dec, k, cu_seqlens, Hq, Hkv, K, W, scale=None, nthreads=None):
+    """Decode-step selection: one query per sequence at its last cached position.
+
+    q_dec [B,Hq,d], k [T,Hkv,d] bf16 bits; cu_seqlens describes the cache (every
+    sequence holds >= 1 token). Returns (idx [B*Hkv, K+W] int32, kth [B*Hkv] float64),
+    row b*Hkv + g.
+    """
+    lib = _load()
+    q_dec, k, cu = _u16(q_dec), _u16(k), _cu(cu_seqlens)
+    d = q_dec.shape[-1]
+    B = len(cu) - 1
+    assert q_dec.size == B * Hq * d
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    idx = np.empty((B * Hkv, K + W), dtype=np.int32)
+    kth = np.empty(B * Hkv, dtype=np.float64)
+    if B == 0:
+        return idx, kth
+    r = lib.hs2o_decode_select(q_dec.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d,
+                               scale, K, W, idx.ctypes.data, kth.ctypes.data,
+                               nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_decode_select: bad arguments")
+    return idx, kth
+
+
+def decode_sparse_attn(q_dec, k, v, cu_seqlens, Hq, Hkv, idx, scale=None, nthreads=None,
+                       want_f64=True, want_bf16=True):
+    """Sparse attention of the decode queries q_dec [B,Hq,d] over idx [B,Hkv,KW].
+
+    Returns (o64 [B,Hq,d] float64 or None, o16 [B,Hq,d] bf16 bits or None).
+    """
+    lib = _load()
+    q_dec, k, v, cu = _u16(q_dec), _u16(k), _u16(v), _cu(cu_seqlens)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    d = q_dec.shape[-1]
+    B = len(cu) - 1
+    KW = idx.shape[-1]
+    assert idx.size == B * Hkv * KW and q_dec.size == B * Hq * d
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    o64 = np.empty((B, Hq, d), dtype=np.float64) if want_f64 else None
+    o16 = np.empty((B, Hq, d), dtype=np.uint16) if want_bf16 else None
+    if B == 0:
+        return o64, o16
+    r = lib.hs2o_decode_sparse_attn(q_dec.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                    cu.ctypes.data, B, Hq, Hkv, d, scale, KW, idx.ctypes.data,
+                                    o64.ctypes.data if o64 is not None else None,
+                                    o16.ctypes.data if o16 is not None else None,
+                                    nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_decode_sparse_attn: bad arguments")
     return o64, o16
 
 

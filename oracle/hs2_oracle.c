@@ -92,15 +92,17 @@ static int find_seq(const dims_t* D, int64_t t_global) {
 }
 
 /* ---- O1 + O2: per-head row statistics and the group score of one row ---- */
-/* S_out[j] for j in [0, t]; scratch z holds G*(t+1) doubles. */
-static void row_group_scores(const dims_t* D, const uint16_t* q, const uint16_t* k, int64_t base,
+/* Row (t, g) of the sequence starting at token `base`; qt holds the query
+ * token's Hq query rows [Hq, d]. S_out[j] for j in [0, t]; scratch z holds
+ * G*(t+1) doubles. */
+static void row_group_scores(const dims_t* D, const uint16_t* qt, const uint16_t* k, int64_t base,
                              int64_t t, int g, double* z, double* S_out, double* m_out,
                              double* l_out) {
   const int G = D->Hq / D->Hkv, d = D->d;
   const int64_t n = t + 1;
   for (int hh = 0; hh < G; hh++) {
     const int h = g * G + hh;
-    const uint16_t* qr = q + ((size_t)(base + t) * D->Hq + h) * d;
+    const uint16_t* qr = qt + (size_t)h * d;
     double qd[1024];
     for (int e = 0; e < d; e++) qd[e] = bf2d(qr[e]);
     double* zr = z + (size_t)hh * n;
@@ -175,6 +177,9 @@ typedef struct {
   int64_t next;
   pthread_mutex_t mu;
   int max_len;
+  /* decode: one query per sequence (q, idx and outputs indexed by sequence),
+     at the sequence's last position */
+  int decode;
 } job_t;
 
 static int64_t take(job_t* J, int64_t chunk, int64_t* end) {
@@ -199,12 +204,22 @@ static void* select_worker(void* arg) {
     int64_t e, s = take(J, 8, &e);
     if (s >= J->n_rows) break;
     for (int64_t r = s; r < e; r++) {
-      int64_t row = J->rows ? J->rows[r] : r; /* row = t_global * Hkv + g */
+      int64_t row = J->rows ? J->rows[r] : r; /* row = t_global * Hkv + g (decode: b * Hkv + g) */
       int64_t tg = row / D->Hkv;
       int g = (int)(row % D->Hkv);
-      int i = find_seq(D, tg);
-      int64_t base = D->cu[i], t = tg - base;
-      row_group_scores(D, J->q, J->k, base, t, g, z, S, NULL, NULL);
+      int64_t base, t;
+      const uint16_t* qt;
+      if (J->decode) {
+        base = D->cu[tg];
+        t = D->cu[tg + 1] - base - 1;
+        qt = J->q + (size_t)tg * D->Hq * D->d;
+      } else {
+        int i = find_seq(D, tg);
+        base = D->cu[i];
+        t = tg - base;
+        qt = J->q + (size_t)tg * D->Hq * D->d;
+      }
+      row_group_scores(D, qt, J->k, base, t, g, z, S, NULL, NULL);
       double kth;
       row_select(D, S, t, J->idx_out + (size_t)r * KW, &kth, cb, mark);
       if (J->kth_out) J->kth_out[r] = kth;
@@ -226,9 +241,16 @@ static void* sparse_worker(void* arg) {
     int64_t e, s = take(J, 16, &e);
     if (s >= J->n_rows) break;
     for (int64_t r = s; r < e; r++) {
-      int64_t tg = J->rows ? J->rows[r] : r;
-      int i = find_seq(D, tg);
-      int64_t base = D->cu[i], t = tg - base;
+      int64_t tg = J->rows ? J->rows[r] : r; /* decode: the sequence */
+      int64_t base, t;
+      if (J->decode) {
+        base = D->cu[tg];
+        t = D->cu[tg + 1] - base - 1;
+      } else {
+        int i = find_seq(D, tg);
+        base = D->cu[i];
+        t = tg - base;
+      }
       for (int h = 0; h < D->Hq; h++) {
         const int g = h / G;
         const int32_t* ir = J->idx_in + ((size_t)tg * D->Hkv + g) * KW;
@@ -334,7 +356,7 @@ int hs2o_group_scores(const uint16_t* q, const uint16_t* k, const int32_t* cu, i
   int64_t base = cu[i], t = t_global - base;
   double* z = (double*)malloc(sizeof(double) * (size_t)(Hq / Hkv) * (size_t)(t + 1));
   if (!z) return -1;
-  row_group_scores(&D, q, k, base, t, g, z, S_out, m_out, l_out);
+  row_group_scores(&D, q + (size_t)t_global * Hq * d, k, base, t, g, z, S_out, m_out, l_out);
   free(z);
   return 0;
 }
@@ -358,6 +380,42 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
   job_t J;
   memset(&J, 0, sizeof(J));
   J.D = &D; J.q = q; J.k = k; J.v = v; J.rows = tokens; J.n_rows = n_tokens;
+  J.idx_in = idx; J.o64 = o64; J.o16 = o16;
+  return run(&J, sparse_worker, nthreads);
+}
+
+/*
+ * Decode step (one new query per sequence). cu describes the cache: sequence b
+ * holds L_b >= 1 tokens and its query sits at its last position t = L_b - 1,
+ * so row (b, g) is exactly prefill row (t, g) with q_dec[b] as the query.
+ * q_dec [B, Hq, d]; idx_out [B*Hkv, K+W] (row b*Hkv + g); kth_out [B*Hkv] nullable.
+ */
+int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* cu, int B, int Hq,
+                       int Hkv, int d, double scale, int K, int W, int32_t* idx_out,
+                       double* kth_out, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu};
+  if (!q_dec || !k || !cu || !idx_out || check_dims(&D)) return -1;
+  for (int b = 0; b < B; b++)
+    if (cu[b + 1] - cu[b] < 1) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q_dec; J.k = k; J.n_rows = (int64_t)B * Hkv; J.decode = 1;
+  J.idx_out = idx_out; J.kth_out = kth_out; J.max_len = max_len(&D);
+  return run(&J, select_worker, nthreads);
+}
+
+/* Sparse attention of the decode queries q_dec [B, Hq, d] over idx [B, Hkv, KW];
+ * o64 / o16 [B, Hq, d] (nullable). */
+int hs2o_decode_sparse_attn(const uint16_t* q_dec, const uint16_t* k, const uint16_t* v,
+                            const int32_t* cu, int B, int Hq, int Hkv, int d, double scale, int KW,
+                            const int32_t* idx, double* o64, uint16_t* o16, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu};
+  if (!q_dec || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
+  for (int b = 0; b < B; b++)
+    if (cu[b + 1] - cu[b] < 1) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q_dec; J.k = k; J.v = v; J.n_rows = B; J.decode = 1;
   J.idx_in = idx; J.o64 = o64; J.o16 = o16;
   return run(&J, sparse_worker, nthreads);
 }

@@ -341,3 +341,37 @@ def test_bf16_rounding_of_oracle_and_generator():
             assert err <= abs(lo - x) + 0.0 and err <= abs(hi - x) + 0.0, (x, b)
             if err == abs(lo - x) and lo != val or err == abs(hi - x) and hi != val:
                 assert (b & 1) == 0  # tie -> even
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_rows_equal_the_last_prefill_rows(G):
+    """Decode step: the new token's query sits at the last cached position, so its
+    selection and sparse output must be exactly the prefill rows of that position
+    (pinned above). Checks the decode wrappers' indexing (query row, position,
+    index row) on ragged cache lengths, including a one-token cache."""
+    lengths = [1, 2, 7, 40, 300, 1100]
+    Hkv, d, K, W = 2, 128, 16, 4
+    Hq = G * Hkv
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=90 + G)
+    last = cu[1:] - 1
+    rows = (last[:, None] * Hkv + np.arange(Hkv)[None, :]).ravel()
+    o_idx, o_kth = oracle.select(q, k, cu, Hq, Hkv, K, W, rows=rows)
+    q_dec = np.ascontiguousarray(q[last])
+    d_idx, d_kth = oracle.decode_select(q_dec, k, cu, Hq, Hkv, K, W)
+    assert (d_idx == o_idx).all()
+    assert np.array_equal(d_kth, o_kth)
+    # sparse layer with a fresh query over those index rows
+    T = int(cu[-1])
+    qs = synthgen.normal_bf16(91, 10, (T, Hq, d))
+    full_idx = np.full((T, Hkv, K + W), -1, dtype=np.int32)
+    full_idx[last] = o_idx.reshape(len(lengths), Hkv, -1)
+    p64, p16 = oracle.sparse_attn(qs, k, v, cu, Hq, Hkv, full_idx, tokens=last)
+    d64, d16 = oracle.decode_sparse_attn(np.ascontiguousarray(qs[last]), k, v, cu, Hq, Hkv,
+                                         o_idx.reshape(len(lengths), Hkv, -1))
+    assert np.array_equal(d64, p64) and np.array_equal(d16, p16)
+
+
+def test_decode_rejects_empty_cache():
+    q, k, v, cu = rand_inputs([3, 0, 5], 4, 1, 128, seed=3)
+    with pytest.raises(ValueError):
+        oracle.decode_select(q[:3], k, cu, 4, 1, 4, 2)
