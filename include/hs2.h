@@ -72,7 +72,13 @@ enum {
 };
 
 /* Operation selector for hs2_workspace_size. */
-enum { HS2_OP_SELECT = 1, HS2_OP_SPARSE = 2, HS2_OP_PREFILL_BLOCK = 3 };
+enum {
+  HS2_OP_SELECT = 1,
+  HS2_OP_SPARSE = 2,
+  HS2_OP_PREFILL_BLOCK = 3,
+  HS2_OP_DECODE_SELECT = 4,
+  HS2_OP_DECODE_SPARSE = 5
+};
 
 /* Flags of hs2_dims.flags. */
 enum {
@@ -103,8 +109,10 @@ typedef struct {
 
 /*
  * Bytes of workspace an operation needs for these dimensions.
- * op: HS2_OP_SELECT, HS2_OP_SPARSE or HS2_OP_PREFILL_BLOCK (n_sparse is unused
- * by the size). Returns HS2_OK and writes *bytes_out, or a validation error.
+ * op: HS2_OP_SELECT, HS2_OP_SPARSE, HS2_OP_PREFILL_BLOCK, HS2_OP_DECODE_SELECT or
+ * HS2_OP_DECODE_SPARSE (for the decode ops `varlen` describes the cache;
+ * n_sparse is unused by the size). Returns HS2_OK and writes *bytes_out, or a
+ * validation error.
  */
 int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, int n_sparse,
                        size_t* bytes_out);
@@ -142,6 +150,33 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
                       const void* const* q_sparse_host_array, void* const* out_sparse_host_array,
                       int out_dtype, int32_t* idx_out, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * Decode step: one new token per sequence after the prompt (the cross-decoder
+ * work HySparse2 moves to generation: HySparse2 news summary, early-exit
+ * paragraph). `cache` describes the KV cache: sequence b holds L_b >= 1
+ * tokens, the newest (position L_b - 1) being the new token itself, whose K/V
+ * rows are already appended. q [B,Hq,128] bf16 are the full layer's queries of
+ * the new tokens (row b). The selection of row b is exactly the prefill rule
+ * for position t = L_b - 1: per-head softmax over all L_b cached keys, group
+ * score S, top-K of [0, t-W] (S desc, position asc), the window [t-W+1, t],
+ * ascending. idx_out [B,Hkv,K+W] int32 (row b*Hkv + g), kth_score_out nullable
+ * [B,Hkv]. Every row is ranked exactly over all its candidates (no sampled
+ * threshold). A sequence with L_b = 0 is an HS2_ERR_INVALID_ARG.
+ */
+int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
+                      int32_t* idx_out, float* kth_score_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * One sparse layer of the decode step: q [B,Hq,128] bf16 (the layer's own
+ * queries of the new tokens), k, v the cache, idx [B,Hkv,K+W] (positions are
+ * local to each sequence; entries outside [0, L_b - 1] are ignored); out
+ * [B,Hq,128] bf16 or float as in hs2_sparse_attn. Needs no workspace.
+ */
+int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                           const void* k, const void* v, const int32_t* idx, void* out,
+                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status; for HS2_ERR_HIP the last HIP error of this thread. */
 const char* hs2_status_string(int status);

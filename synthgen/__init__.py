@@ -223,3 +223,37 @@ def make_inputs(w: Workload) -> dict:
             k[a:b] = ks
         out["needle_pos"] = pos
     return out
+
+
+def decode_workload(name: str) -> Workload:
+    """Decode-step workloads (the lengths are the cache lengths; one new query per sequence)."""
+    if name == "decode-32k":
+        return Workload("decode-32k", [32768] * 8, 32, 8, 128, 1024, 128, 3, False, 1101)
+    if name == "decode-varlen":
+        L, s = varlen_lengths(1005)
+        return Workload("decode-varlen", L, 32, 8, 128, 1024, 128, 1, False, 1102,
+                        {"length_seed": s})
+    raise KeyError(name)
+
+
+def make_decode_inputs(w: Workload) -> dict:
+    """Decode step over a cache of w.lengths tokens per sequence: k/v [T,Hkv,d] (as in
+    make_inputs), q_dec [B,Hq,d] and q_sparse_dec list of [B,Hq,d] = the rows of the
+    q_full / q_sparse streams at each sequence's last position (generated directly, so a
+    decode step equals the last prefill row of the same inputs). No needles."""
+    assert not w.needles, "decode inputs carry no needles"
+    T = w.total
+    cu = w.cu_seqlens
+    last = [int(x) - 1 for x in cu[1:]]
+    assert all(cu[i + 1] > cu[i] for i in range(len(w.lengths))), "every cache holds >= 1 token"
+    row = w.Hq * w.d
+
+    def rows(tid):
+        return np.stack([normal_bf16(w.seed, tid, (w.Hq, w.d), start=t * row) for t in last])
+
+    return {"k": normal_bf16(w.seed, TID_K, (T, w.Hkv, w.d)),
+            "v": normal_bf16(w.seed, TID_V, (T, w.Hkv, w.d)),
+            "q_dec": rows(TID_Q_FULL),
+            "q_sparse_dec": [rows(TID_Q_SPARSE0 + l) for l in range(w.n_sparse)],
+            "cu_seqlens": cu}
+

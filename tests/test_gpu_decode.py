@@ -1,0 +1,129 @@
+"""GPU parity of the decode step (one new query per sequence against its cache)
+through the C ABI, against the CPU oracle's decode functions.
+
+Selection: structural invariants of every row, A1/A2 against the oracle on the
+same seeded inputs, kth score; every decode row is ranked exactly over all its
+candidates, so the rows are expected to be identical except for fp32-vs-fp64
+near-ties. Sparse layer: A4 (fp32 mode) and A3 (bf16) on the GPU's index rows.
+"""
+import numpy as np
+import pytest
+
+import synthgen
+from hs2_testlib import (A1_TOL, A2_MIN, A3_TOL, A4_TOL, _check_structure_rows, from_dev_bf16,
+                         log, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_level_sparse_hs2_amd as hs2
+    hs2.load_library()
+
+
+def exact_group_scores(q_dec_b, k, cu, b, g, Hq, Hkv, scale):
+    """fp64 S over the cached keys of sequence b for the query of row (b, g)."""
+    G = Hq // Hkv
+    a, e = int(cu[b]), int(cu[b + 1])
+    kk = synthgen.bf16_to_float(k[a:e, g]).astype(np.float64)
+    S = np.zeros(e - a)
+    for hh in range(G):
+        qv = synthgen.bf16_to_float(q_dec_b[g * G + hh]).astype(np.float64)
+        z = scale * (kk @ qv)
+        p = np.exp(z - z.max())
+        S += p / p.sum()
+    return S
+
+
+def run_decode(w, check_a3=True):
+    import oracle
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    log(f"decode {w.name}: lengths={w.lengths[:8]} Hq={w.Hq} Hkv={w.Hkv} K={w.K} W={w.W}")
+    inp = synthgen.make_decode_inputs(w)
+    cu = inp["cu_seqlens"]
+    B, Hq, Hkv, KW = len(w.lengths), w.Hq, w.Hkv, w.K + w.W
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    cache = hs2.VarlenArgs(cu_dev, [int(x) for x in cu])
+    dims = hs2.make_dims(Hq, Hkv, w.K, w.W, w.scale)
+    k, v = to_dev_bf16(inp["k"]), to_dev_bf16(inp["v"])
+    q = to_dev_bf16(inp["q_dec"])
+    nbytes = hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SELECT, 0)
+    ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
+    idx_t = torch.full((B, Hkv, KW), -7, dtype=torch.int32, device="cuda")
+    kth_t = torch.empty((B, Hkv), dtype=torch.float32, device="cuda")
+    hs2.hs2_decode_select(dims, cache, q, k, idx_t, kth_t, ws)
+    torch.cuda.synchronize()
+    idx = idx_t.cpu().numpy()
+    tloc = (cu[1:] - cu[:-1] - 1).astype(np.int64)
+    _check_structure_rows(idx, tloc, w.K, w.W)
+    o_idx, o_kth = oracle.decode_select(inp["q_dec"], inp["k"], cu, Hq, Hkv, w.K, w.W,
+                                        scale=w.scale)
+    o_idx = o_idx.reshape(B, Hkv, KW)
+    inter = tot = 0
+    worst = np.inf
+    same = 0
+    for b in range(B):
+        for g in range(Hkv):
+            a_, o_ = idx[b, g][idx[b, g] >= 0], o_idx[b, g][o_idx[b, g] >= 0]
+            inter += len(np.intersect1d(a_, o_))
+            tot += len(o_)
+            if len(a_) == len(o_) and (a_ == o_).all():
+                same += 1
+                continue
+            S = exact_group_scores(inp["q_dec"][b], inp["k"], cu, b, g, Hq, Hkv, w.scale)
+            glob = a_[a_ < tloc[b] - w.W + 1]
+            if len(glob):
+                worst = min(worst, S[glob].min() - o_kth[b * Hkv + g])
+    overlap = inter / max(1, tot)
+    log(f"  select: rows {B * Hkv} identical {same} overlap {overlap:.6f} A1 margin {worst:.3g}")
+    assert overlap >= A2_MIN and worst >= -A1_TOL
+    kth = kth_t.cpu().numpy().reshape(-1)
+    assert ((kth == -1.0) == (o_kth == -1.0)).all()
+    sel = o_kth > 0
+    if sel.any():
+        rel = np.abs(kth[sel] - o_kth[sel]) / o_kth[sel]
+        log(f"  kth relative diff: max {rel.max():.3g}")
+        assert rel.max() <= 1e-3
+    # sparse layers on the GPU's rows
+    for l, qs_np in enumerate(inp["q_sparse_dec"]):
+        qs = to_dev_bf16(qs_np)
+        o64, o16 = oracle.decode_sparse_attn(qs_np, inp["k"], inp["v"], cu, Hq, Hkv, idx,
+                                             scale=w.scale)
+        out32 = torch.empty((B, Hq, w.d), dtype=torch.float32, device="cuda")
+        hs2.hs2_decode_sparse_attn(dims, cache, qs, k, v, idx_t, out32, hs2.HS2_OUT_F32)
+        out16 = torch.empty((B, Hq, w.d), dtype=torch.bfloat16, device="cuda")
+        hs2.hs2_decode_sparse_attn(dims, cache, qs, k, v, idx_t, out16, hs2.HS2_OUT_BF16)
+        torch.cuda.synchronize()
+        err4 = np.abs(out32.cpu().numpy() - o64).max()
+        g16 = synthgen.bf16_to_float(from_dev_bf16(out16)).astype(np.float64)
+        err3 = np.abs(g16 - synthgen.bf16_to_float(o16).astype(np.float64)).max()
+        log(f"  layer {l}: A4 max-abs {err4:.3g} A3 max-abs {err3:.3g}")
+        assert err4 <= A4_TOL
+        if check_a3:
+            assert err3 <= A3_TOL
+    return idx
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_decode_ragged_caches_every_group_size(G):
+    w = synthgen.custom([1, 2, 33, 128, 129, 700, 2100, 4500], Hq=2 * G, Hkv=2, K=256, W=32,
+                        n_sparse=1, seed=60 + G)
+    run_decode(w)
+
+
+@pytest.mark.parametrize("K,W", [(0, 16), (64, 0), (1, 1)])
+def test_decode_budget_edges(K, W):
+    w = synthgen.custom([1, 16, 17, 64, 65, 81, 3000], Hq=8, Hkv=2, K=K, W=W, n_sparse=1, seed=71)
+    run_decode(w)
+
+
+def test_decode_long_caches():
+    """Eight caches of 32k-class lengths at the 32k workload's head shape."""
+    w = synthgen.custom([32768, 1, 5000, 70001, 32769, 1153, 1152, 20000], Hq=32, Hkv=8, K=1024,
+                        W=128, n_sparse=1, seed=1101)
+    run_decode(w)

@@ -62,3 +62,13 @@ def test_varlen_lengths_draw():
     assert len(L) == 8 and sum(L) <= 600 * 1024
     assert all(4096 <= x <= 196608 for x in L)
     assert synthgen.varlen_lengths(1005) == (L, s)
+
+
+def test_decode_inputs_are_the_last_prefill_rows():
+    w = synthgen.custom([1, 5, 300], 8, 2, 16, 4, n_sparse=2, seed=5)
+    a, b = synthgen.make_inputs(w), synthgen.make_decode_inputs(w)
+    last = w.cu_seqlens[1:] - 1
+    assert (a["q_full"][last] == b["q_dec"]).all()
+    assert (a["k"] == b["k"]).all() and (a["v"] == b["v"]).all()
+    for x, y in zip(a["q_sparse"], b["q_sparse_dec"]):
+        assert (x[last] == y).all()

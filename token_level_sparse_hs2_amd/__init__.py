@@ -7,7 +7,8 @@ is torch's current HIP stream unless one is given. Every step of the path runs
 in the library's kernels; there is no fallback. If the library is missing the
 import of any entry point raises.
 
-Layouts (token-major over a packed varlen batch, T tokens):
+Layouts (token-major over a packed varlen batch, T tokens; the decode calls take
+one query row per sequence, [B, ...], against the cache described by cu_seqlens):
   q, q_sparse, out  [T, Hq, 128]   bf16 (out: bf16 or float32)
   k, v              [T, Hkv, 128]  bf16
   idx               [T, Hkv, K+W]  int32, local positions ascending, -1 padded
@@ -32,6 +33,8 @@ HS2_OUT_F32 = 1
 HS2_OP_SELECT = 1
 HS2_OP_SPARSE = 2
 HS2_OP_PREFILL_BLOCK = 3
+HS2_OP_DECODE_SELECT = 4
+HS2_OP_DECODE_SPARSE = 5
 HS2_FLAG_EXACT_SELECT = 1
 HS2_MAX_SEQLEN = 262144
 
@@ -78,6 +81,10 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_prefill_block.argtypes = [D, V, vp, vp, vp, i32, ctypes.POINTER(vp),
                                       ctypes.POINTER(vp), i32, vp, vp, sz, vp]
     lib.hs2_prefill_block.restype = i32
+    lib.hs2_decode_select.argtypes = [D, V, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_decode_select.restype = i32
+    lib.hs2_decode_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.hs2_decode_sparse_attn.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_plan_task.argtypes = [ctypes.POINTER(ctypes.c_int32), i32, i32, i64,
@@ -176,6 +183,26 @@ def hs2_prefill_block(dims: Dims, varlen: VarlenArgs, q_full, k, v, q_sparse: Se
                                             _ptr(q_full), _ptr(k), _ptr(v), n, qa, oa, out_dtype,
                                             _ptr(idx_out), _ptr(workspace), ws_bytes,
                                             _stream(stream)))
+
+
+def hs2_decode_select(dims: Dims, cache: VarlenArgs, q, k, idx_out, kth_score_out=None,
+                      workspace=None, stream=None) -> None:
+    """Decode step selection: q [B,Hq,128] (row b = sequence b's newest token, at its
+    last cached position), k the cache described by `cache`; idx_out [B,Hkv,K+W]."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().hs2_decode_select(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q),
+                                            _ptr(k), _ptr(idx_out), _ptr(kth_score_out),
+                                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hs2_decode_sparse_attn(dims: Dims, cache: VarlenArgs, q, k, v, idx, out,
+                           out_dtype: int = HS2_OUT_BF16, workspace=None, stream=None) -> None:
+    """One sparse layer of the decode step: q, out [B,Hq,128], idx [B,Hkv,K+W]."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().hs2_decode_sparse_attn(ctypes.byref(dims), ctypes.byref(cache.struct),
+                                                 _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+                                                 out_dtype, _ptr(workspace), ws_bytes,
+                                                 _stream(stream)))
 
 
 def hs2_plan_task(cu_host: Sequence[int], rows_per_task: int, task: int):

@@ -124,6 +124,37 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   return HS2_OK;
 }
 
+// Decode step: the varlen struct describes the cache; every sequence holds >= 1 token.
+struct DecodeGeometry {
+  Geometry geo;
+  int n_split = 0, bitmap_words = 0;
+  size_t off_z2 = 0, off_part = 0, off_dense = 0, bytes = 0, lds = 0;
+};
+
+int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) {
+  int st = validate(d, v, &dg->geo);
+  if (st != HS2_OK) return st;
+  const Geometry& g = dg->geo;
+  if (g.B == 0) return HS2_OK;
+  for (int i = 0; i < v->batch; i++)
+    if (v->cu_seqlens_host[i + 1] - v->cu_seqlens_host[i] < 1) return HS2_ERR_INVALID_ARG;
+  if (v->batch > 65535 || d->num_kv_heads > 65535) return HS2_ERR_UNSUPPORTED;  // grid y/z
+  const int max_len = std::max(1, g.max_len);
+  dg->n_split = hs2::ceil_div(max_len, hs2::kDecodeSplit);
+  dg->bitmap_words = hs2::ceil_div(max_len, 32);
+  size_t off = 0;
+  dg->off_z2 = off;
+  off = align_up(off + (size_t)g.T * d->num_q_heads * sizeof(float));
+  dg->off_part = off;
+  off = align_up(off + (size_t)v->batch * d->num_kv_heads * dg->n_split * g.G * 2 * sizeof(float));
+  dg->off_dense = off;
+  off = align_up(off + (size_t)v->batch * d->num_kv_heads * max_len * sizeof(uint32_t));
+  dg->bytes = off;
+  // histogram, scratch words, two bitmaps of the row's candidates
+  dg->lds = (hs2::kTopkBins + 16 + 2 * (size_t)dg->bitmap_words) * sizeof(uint32_t);
+  return HS2_OK;
+}
+
 int check_workspace(const Geometry& geo, void* ws, size_t bytes) {
   if (geo.select_bytes == 0) return HS2_OK;
   if (!ws || bytes < geo.select_bytes) return HS2_ERR_WORKSPACE;
@@ -242,7 +273,7 @@ int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
 
 extern "C" {
 
-int hs2_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int hs2_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 const char* hs2_status_string(int status) {
   switch (status) {
@@ -259,6 +290,13 @@ int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, i
                        size_t* bytes_out) {
   (void)n_sparse;
   if (!bytes_out) return HS2_ERR_INVALID_ARG;
+  if (op == HS2_OP_DECODE_SELECT || op == HS2_OP_DECODE_SPARSE) {
+    DecodeGeometry dg;
+    int st = validate_decode(dims, varlen, &dg);
+    if (st != HS2_OK) return st;
+    *bytes_out = (op == HS2_OP_DECODE_SPARSE || dg.geo.B == 0) ? 0 : dg.bytes;
+    return HS2_OK;
+  }
   if (op != HS2_OP_SELECT && op != HS2_OP_SPARSE && op != HS2_OP_PREFILL_BLOCK)
     return HS2_ERR_INVALID_ARG;
   Geometry geo;
@@ -322,6 +360,72 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
                     out_sparse_host_array[i], out_dtype, s);
     if (st != HS2_OK) return st;
   }
+  return HS2_OK;
+}
+
+int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
+                      int32_t* idx_out, float* kth_score_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  DecodeGeometry dg;
+  int st = validate_decode(dims, cache, &dg);
+  if (st != HS2_OK) return st;
+  if (dg.geo.B == 0) return HS2_OK;
+  if (!q || !k || !idx_out) return HS2_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < dg.bytes) return HS2_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  hs2::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.cu = cache->cu_seqlens;
+  p.B = cache->batch;
+  p.Hq = dims->num_q_heads;
+  p.Hkv = dims->num_kv_heads;
+  p.K = dims->top_k;
+  p.W = dims->window;
+  p.max_seqlen = std::max(1, dg.geo.max_len);
+  p.n_split = dg.n_split;
+  p.bitmap_words = dg.bitmap_words;
+  p.c = scale_log2(dims);
+  p.z2 = reinterpret_cast<float*>(w + dg.off_z2);
+  p.part = reinterpret_cast<float2*>(w + dg.off_part);
+  p.dense = reinterpret_cast<uint32_t*>(w + dg.off_dense);
+  p.idx = idx_out;
+  p.kth = kth_score_out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hs2::launch_decode_logits(dg.geo.G, p, s);
+  if (e != hipSuccess) return hip_fail(e, "decode logits kernel");
+  e = hs2::launch_decode_select(dg.geo.G, p, dg.lds, s);
+  if (e != hipSuccess) return hip_fail(e, "decode select kernel");
+  return HS2_OK;
+}
+
+int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                           const void* k, const void* v, const int32_t* idx, void* out,
+                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  DecodeGeometry dg;
+  int st = validate_decode(dims, cache, &dg);
+  if (st != HS2_OK) return st;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (dg.geo.B == 0) return HS2_OK;
+  if (!q || !k || !v || !idx || !out) return HS2_ERR_INVALID_ARG;
+  hs2::SparseParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.idx = idx;
+  p.cu = cache->cu_seqlens;
+  p.B = cache->batch;
+  p.Hq = dims->num_q_heads;
+  p.Hkv = dims->num_kv_heads;
+  p.KW = dims->top_k + dims->window;
+  p.T = cache->batch;
+  p.c = scale_log2(dims);
+  p.out = out;
+  p.decode = 1;
+  hipError_t e = hs2::launch_sparse(dg.geo.G, out_dtype == HS2_OUT_F32, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode sparse attention kernel");
   return HS2_OK;
 }
 

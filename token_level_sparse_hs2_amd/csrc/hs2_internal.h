@@ -117,15 +117,35 @@ struct TopkParams {
 };
 
 struct SparseParams {
-  const uint16_t* q;    // [T, Hq, 128]
+  const uint16_t* q;    // [T, Hq, 128] (decode: [B, Hq, 128])
   const uint16_t* k;    // [T, Hkv, 128]
   const uint16_t* v;
-  const int32_t* idx;   // [T, Hkv, KW]
+  const int32_t* idx;   // [T, Hkv, KW] (decode: [B, Hkv, KW])
   const int32_t* cu;
   int B, Hq, Hkv, KW;
-  int64_t T;
+  int64_t T;            // query rows: tokens, or sequences when decoding
   float c;              // softmax_scale * log2(e)
   void* out;            // [T, Hq, 128] bf16 or f32
+  int decode;           // query row r is sequence r at its last position
+};
+
+// Decode step: one query per sequence at its last cached position.
+constexpr int kDecodeSplit = 1024;  // cached keys per logits workgroup
+
+struct DecodeParams {
+  const uint16_t* q;    // [B, Hq, 128]
+  const uint16_t* k;    // [T, Hkv, 128] cache
+  const int32_t* cu;    // [B+1] cache offsets
+  int B, Hq, Hkv, K, W;
+  int max_seqlen;
+  int n_split;          // ceil(max_seqlen / kDecodeSplit)
+  int bitmap_words;     // ceil(max_seqlen / 32)
+  float c;              // softmax_scale * log2(e)
+  float* z2;            // [T, Hq]: c * q.k of every cached key and query head
+  float2* part;         // [B, Hkv, n_split, G]: per split (max, sum of exp2(z2 - max))
+  uint32_t* dense;      // [B * Hkv, max_seqlen] S bits
+  int32_t* idx;         // [B, Hkv, K+W]
+  float* kth;           // [B, Hkv] or null
 };
 
 // launchers (defined in the .hip files)
@@ -136,5 +156,7 @@ hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t 
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_sparse(int G, bool precise, const SparseParams& p, hipStream_t s);
+hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_select(int G, const DecodeParams& p, size_t lds_bytes, hipStream_t s);
 
 }  // namespace hs2

@@ -561,6 +561,111 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode step, logits. Sequence b's query (its newest token, at position
+// L_b - 1) against every cached key: z2[j, h] = c * <q[b,h], k[j,g]> for the
+// group's heads, written to p.z2 in the [T, Hq] layout, and per split the
+// (max, sum of exp2(z2 - max)) of each head, from which the select kernel forms
+// the full layer's log-sum-exp. Grid (split, g, b): kDecodeSplit keys per
+// workgroup, 4 waves x 16 keys per step on v_mfma_f32_16x16x32_bf16 with the
+// group's G heads as the 16-row A operand (rows >= G are zero).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_max_sum(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  s = s * fast_exp2(m - mn) + s2 * fast_exp2(m2 - mn);
+  m = mn;
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
+  __shared__ float2 red[4][16];
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int base = p.cu[b], L = p.cu[b + 1] - base;
+  const int j0 = split * kDecodeSplit;
+  if (j0 >= L) return;  // the whole workgroup: this split is past the sequence
+  const int j1 = min(L, j0 + kDecodeSplit);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l >> 4, lc = l & 15;
+  const int Hq = p.Hq, Hkv = p.Hkv;
+  const float c = p.c;
+
+  // A operand: row lc = head lc of the group, d = 32 ks + 8 lq .. +7
+  bf16x8 qa[4];
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * Hq + g * G + min(lc, G - 1)) * kHeadDim;
+    u32x4 v[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) v[ks] = to_u32x4(ldg128(qrow + 32 * ks + 8 * lq));
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      if (lc >= G) v[ks] = u32x4{0u, 0u, 0u, 0u};
+      qa[ks] = as_bf16x8(v[ks]);
+    }
+  }
+  // running (max, sum) of rows (heads) 4 lq + i over the lane's keys
+  float m[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) { m[i] = -INFINITY; sm[i] = 0.f; }
+  const uint16_t* kg = p.k + ((size_t)base * Hkv + g) * kHeadDim;
+  const size_t kstride = (size_t)Hkv * kHeadDim;
+  for (int jt = j0 + 16 * w; jt < j1; jt += 64) {
+    // B operand: key jt + lc (clamped to the split; masked below), d = 32 ks + 8 lq
+    const int j = min(jt + lc, j1 - 1);
+    u32x4 kv[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) kv[ks] = to_u32x4(ldg128(kg + (size_t)j * kstride + 32 * ks + 8 * lq));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) acc = mfma16x16x32(qa[ks], as_bf16x8(kv[ks]), acc);
+    const bool kval = jt + lc < j1;
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) z[i] = kval ? acc[i] * c : -INFINITY;
+    if (kval && 4 * lq < G) {  // heads 4 lq .. of key jt + lc
+      float* dst = p.z2 + (size_t)(base + jt + lc) * Hq + g * G + 4 * lq;
+      if constexpr (G >= 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < G; i++) dst[i] = z[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) merge_max_sum(m[i], sm[i], z[i], kval ? 1.f : 0.f);
+  }
+  // the 16 lanes of a lane group hold the same heads: merge them, then the waves
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const float m2 = shfl_xor_f(m[i], off), s2 = shfl_xor_f(sm[i], off);
+      merge_max_sum(m[i], sm[i], m2, s2);
+    }
+    if (lc == 0) red[w][4 * lq + i] = make_float2(m[i], sm[i]);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mm = -INFINITY, ss = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ww++) merge_max_sum(mm, ss, red[ww][tid].x, red[ww][tid].y);
+    p.part[(((size_t)b * Hkv + g) * p.n_split + split) * G + tid] = make_float2(mm, ss);
+  }
+}
+
+hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s) {
+  if (p.B <= 0) return hipSuccess;
+  const dim3 grid(p.n_split, p.Hkv, p.B), block(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(decode_logits_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(decode_logits_kernel<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(decode_logits_kernel<4>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(decode_logits_kernel<8>, grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL(decode_logits_kernel<16>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   dim3 grid(n_blocks), block(kSelThreads);

@@ -481,6 +481,90 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode step, selection: one workgroup per (KV group, sequence). The split
+// partials give each head's log-sum-exp over all cached keys; S[j] for every
+// candidate j <= t - W (t = L_b - 1) goes to a scratch row, then the same exact
+// radix select and assembly as the exact path (no sampled threshold).
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void decode_select_kernel(DecodeParams p) {
+  extern __shared__ uint32_t smem[];
+  __shared__ float lse_s[16];
+  TopkShared sh;
+  sh.hist = smem;
+  sh.misc = reinterpret_cast<int32_t*>(smem + kTopkBins);
+  sh.sel = smem + kTopkBins + 16;
+  sh.tie = sh.sel + p.bitmap_words;
+  sh.keys = nullptr;
+  sh.qf = nullptr;
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int base = p.cu[b], L = p.cu[b + 1] - base;
+  const int t = L - 1, n_c = t - p.W + 1, KW = p.K + p.W;
+  int32_t* row = p.idx + ((size_t)b * p.Hkv + g) * KW;
+  float* kth_out = p.kth ? p.kth + (size_t)b * p.Hkv + g : nullptr;
+  if (p.K == 0 || n_c <= p.K) {  // nothing to rank: [0, t] or the window only
+    write_trivial_row(n_c, p.K, t, KW, row);
+    if (kth_out && tid == 0) *kth_out = -1.f;
+    return;
+  }
+  if (tid < G) {
+    const float2* pr = p.part + ((size_t)b * p.Hkv + g) * p.n_split * G + tid;
+    float m = -INFINITY, s = 0.f;
+    const int n_sp = ceil_div(L, kDecodeSplit);
+    for (int i = 0; i < n_sp; i++) {
+      const float2 v = pr[(size_t)i * G];
+      const float mn = fmaxf(m, v.x);
+      s = s * fast_exp2(m - mn) + v.y * fast_exp2(v.x - mn);
+      m = mn;
+    }
+    lse_s[tid] = m + fast_log2(s);
+  }
+  __syncthreads();
+  float lse[G];
+#pragma unroll
+  for (int h = 0; h < G; h++) lse[h] = lse_s[h];
+  uint32_t* dense = p.dense + ((size_t)b * p.Hkv + g) * p.max_seqlen;
+  for (int j = tid; j < n_c; j += kSelThreads) {
+    const float* zr = p.z2 + (size_t)(base + j) * p.Hq + g * G;
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; h++) sum += fast_exp2(zr[h] - lse[h]);
+    dense[j] = __float_as_uint(sum);
+  }
+  __syncthreads();
+  int krem;
+  const uint32_t kth = radix_kth([&](int i) { return dense[i]; }, n_c, p.K, sh, &krem);
+  const int nwords = ceil_div(n_c, 32);
+  mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth, krem,
+                nwords, sh);
+  write_selected_row(nwords, n_c, t, KW, row, sh);
+  if (kth_out && tid == 0) *kth_out = __uint_as_float(kth);
+}
+
+template <int G>
+static hipError_t launch_decode_select_g(const DecodeParams& p, size_t lds, hipStream_t s) {
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_select_kernel<G>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(decode_select_kernel<G>, dim3(p.Hkv, p.B), dim3(kSelThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_select(int G, const DecodeParams& p, size_t lds_bytes, hipStream_t s) {
+  if (p.B <= 0) return hipSuccess;
+  switch (G) {
+    case 1: return launch_decode_select_g<1>(p, lds_bytes, s);
+    case 2: return launch_decode_select_g<2>(p, lds_bytes, s);
+    case 4: return launch_decode_select_g<4>(p, lds_bytes, s);
+    case 8: return launch_decode_select_g<8>(p, lds_bytes, s);
+    case 16: return launch_decode_select_g<16>(p, lds_bytes, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s) {
   (void)G;
   if (n_rows <= 0) return hipSuccess;

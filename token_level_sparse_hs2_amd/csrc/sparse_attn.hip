@@ -33,9 +33,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   const int g = blockIdx.x % Hkv;
   const int64_t tg = (int64_t)(blockIdx.x / Hkv) * 4 + w;
   if (tg >= p.T) return;
-  const int seq = find_seq(p.cu, p.B, tg);
+  // query row tg: a token of the packed batch, or (decode) sequence tg at its
+  // last cached position
+  const int seq = p.decode ? (int)tg : find_seq(p.cu, p.B, tg);
   const int base = p.cu[seq];
-  const int t = (int)(tg - base);
+  const int t = p.decode ? p.cu[seq + 1] - base - 1 : (int)(tg - base);
   const int32_t* irow = p.idx + ((size_t)tg * Hkv + g) * KW;
   const float c = p.c;
 
