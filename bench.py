@@ -7,6 +7,10 @@ index rows. Inputs are seeded synthetic bf16 tensors already resident in HBM.
 
 Default workload: B=1, L=32768, Hq=32, Hkv=8, d=128, K=1024, W=128, needle keys,
 1 select + 3 sparse layers. Prints one JSON line.
+
+--decode NAME measures the decode step instead (one new token per sequence
+against its KV cache: hs2_decode_select + every sparse layer's
+hs2_decode_sparse_attn) and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -91,6 +95,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=640)  # about 10 s of oracle work at 32k
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--decode", default=None, choices=["decode-32k", "decode-varlen"],
+                    help="time the decode step on this cache workload instead of prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device-to-device copy (known bytes) for counter scaling")
     args = ap.parse_args()
@@ -99,6 +105,9 @@ def main():
               "(the work shards by KV group with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        return main_decode(args)
 
     import numpy as np
     import torch
@@ -201,6 +210,116 @@ def main():
         "roofline_tokens_per_s": round(T / (f_sel / (MFMA_BF16_PEAK_TFS * 1e12)
                                             + len(outs) * b_sp / (HBM_PEAK_GBS * 1e9)), 1),
         "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def decode_work(lengths, Hq, Hkv, d, K, W, n_sparse):
+    """Algorithmic HBM bytes of one decode step: the K cache read once and the logits
+    written and read once (selection), then per sparse layer the gathered K/V rows,
+    the index rows and the queries/outputs of the new tokens."""
+    KW, B, T = K + W, len(lengths), sum(lengths)
+    sel = T * Hkv * d * 2 + 2 * T * Hq * 4 + B * Hq * d * 2 + B * Hkv * KW * 4
+    n = sum(min(L, KW) for L in lengths)
+    sp = Hkv * n * 2 * d * 2 + B * Hkv * KW * 4 + 2 * B * Hq * d * 2
+    return sel, sp
+
+
+def main_decode(args):
+    import numpy as np
+    import torch
+    import synthgen
+    import token_level_sparse_hs2_amd as hs2
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from hs2_testlib import to_dev_bf16
+
+    w = synthgen.decode_workload(args.decode)
+    t_in = time.perf_counter()
+    inp = synthgen.make_decode_inputs(w)
+    gen_s = time.perf_counter() - t_in
+    B, T, Hq, Hkv, d, K, W = len(w.lengths), w.total, w.Hq, w.Hkv, w.d, w.K, w.W
+    cu = inp["cu_seqlens"]
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    cache = hs2.VarlenArgs(cu_dev, [int(x) for x in cu])
+    dims = hs2.make_dims(Hq, Hkv, K, W, w.scale)
+    k, v, q = to_dev_bf16(inp["k"]), to_dev_bf16(inp["v"]), to_dev_bf16(inp["q_dec"])
+    qs = [to_dev_bf16(x) for x in inp["q_sparse_dec"]]
+    ws = torch.empty(max(1, hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SELECT, 0)),
+                     dtype=torch.uint8, device="cuda")
+    ws_sp = torch.empty(max(1, hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SPARSE, 0)),
+                        dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Hkv, K + W), dtype=torch.int32, device="cuda")
+    outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in qs]
+    stream = torch.cuda.current_stream()
+
+    def select():
+        hs2.hs2_decode_select(dims, cache, q, k, idx, None, ws, stream=stream)
+
+    def sparse(i):
+        hs2.hs2_decode_sparse_attn(dims, cache, qs[i], k, v, idx, outs[i], hs2.HS2_OUT_BF16, ws_sp,
+                                   stream=stream)
+
+    def step():
+        select()
+        for i in range(len(qs)):
+            sparse(i)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    steps = max(args.steps, 20)
+    for _ in range(max(args.warmup, 3)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ms = timed(step, steps)
+    wall = time.perf_counter() - t0
+    sel_ms = timed(select, 20)
+    sp_ms = timed(lambda: sparse(0), 20)
+    b_sel, b_sp = decode_work(w.lengths, Hq, Hkv, d, K, W, len(qs))
+    b_step = b_sel + len(qs) * b_sp
+    gbs = b_step / (step_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        c0 = time.perf_counter()
+        o_idx, _ = oracle.decode_select(inp["q_dec"], inp["k"], cu, Hq, Hkv, K, W, scale=w.scale,
+                                        nthreads=threads)
+        for x in inp["q_sparse_dec"]:
+            oracle.decode_sparse_attn(x, inp["k"], inp["v"], cu, Hq, Hkv, o_idx.reshape(B, Hkv, -1),
+                                      scale=w.scale, nthreads=threads, want_bf16=False)
+        dt = time.perf_counter() - c0
+        cpu = {"value": B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole step ({B} sequences, every KV group, select + {len(qs)} sparse "
+                         f"layers), fp64 C oracle, {dt:.1f} s wall"}
+
+    out = {
+        "metric": "decode tokens/sec (select + sparse attn over the KV cache), one new token per "
+                  "sequence",
+        "value": round(B / (step_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "ms_per_step": round(step_ms, 5), "wall_s": round(wall, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded bf16 N(0,1) K/V cache and queries (SplitMix64 + Box-Muller)",
+        "config": {"workload": f"{args.decode}: B={B} caches of lengths {w.lengths[:8]} "
+                               f"Hq={Hq} Hkv={Hkv} d={d} K={K} W={W}, 1 select + {len(qs)} sparse "
+                               f"layers", "global_batch": B, "cache_tokens": T,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole decode step", "algorithmic_bytes_per_step": b_step},
+        "select_ms": round(sel_ms, 5), "sparse_layer_ms": round(sp_ms, 5),
+        "select_bytes": b_sel, "sparse_layer_bytes": b_sp,
+        "cpu_baseline": cpu, "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
 

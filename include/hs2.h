@@ -172,7 +172,10 @@ int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
  * One sparse layer of the decode step: q [B,Hq,128] bf16 (the layer's own
  * queries of the new tokens), k, v the cache, idx [B,Hkv,K+W] (positions are
  * local to each sequence; entries outside [0, L_b - 1] are ignored); out
- * [B,Hq,128] bf16 or float as in hs2_sparse_attn. Needs no workspace.
+ * [B,Hq,128] bf16 or float as in hs2_sparse_attn. The few rows of a decode
+ * step are split over several wavefronts whose partial results are merged, so
+ * it takes a workspace of hs2_workspace_size(HS2_OP_DECODE_SPARSE) bytes
+ * (0 when no split is needed; then workspace may be NULL).
  */
 int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
                            const void* k, const void* v, const int32_t* idx, void* out,

@@ -178,3 +178,29 @@ def test_planner_covers_every_tile_once_longest_first(lib, lengths, tok):
 
 def test_tokens_per_task_matches_kernel_geometry():
     assert [hs2.tokens_per_task(g) for g in (1, 2, 4, 8, 16)] == [64, 64, 64, 32, 16]
+
+
+def test_decode_validation_and_workspace(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    L = hs2.load_library()
+    v = varlen([100, 0, 50])  # a cache with no token has no decode query
+    assert L.hs2_decode_select(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, None, 1, 1 << 40,
+                               None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_decode_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, 1, 0, 1,
+                                    1 << 40, None) == hs2.HS2_ERR_INVALID_ARG
+    v = varlen([32768] * 8)
+    n_sel = hs2.hs2_workspace_size(d, v, hs2.HS2_OP_DECODE_SELECT)
+    n_sp = hs2.hs2_workspace_size(d, v, hs2.HS2_OP_DECODE_SPARSE)
+    # logits [T, Hq] fp32 + scores [B*Hkv, L] + partials; sparse partials for the split rows
+    assert 8 * 32768 * 32 * 4 < n_sel < 64 << 20
+    assert 0 < n_sp < 16 << 20
+    assert L.hs2_decode_select(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, None, 1, n_sel - 1,
+                               None) == hs2.HS2_ERR_WORKSPACE
+    assert L.hs2_decode_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, 1, 0, None,
+                                    0, None) == hs2.HS2_ERR_WORKSPACE
+    assert L.hs2_decode_select(ctypes.byref(d), ctypes.byref(v.struct), None, 1, 1, None, 1, n_sel,
+                               None) == hs2.HS2_ERR_INVALID_ARG
+    # a single sequence (8 rows) is split too
+    v1 = varlen([1000])
+    assert hs2.hs2_workspace_size(d, v1, hs2.HS2_OP_DECODE_SPARSE) > 0
+    assert hs2.hs2_workspace_size(d, hs2.VarlenArgs(FakeDev(0), [0]), hs2.HS2_OP_DECODE_SELECT) == 0

@@ -90,14 +90,17 @@ def run_decode(w, check_a3=True):
         log(f"  kth relative diff: max {rel.max():.3g}")
         assert rel.max() <= 1e-3
     # sparse layers on the GPU's rows
+    nsp = hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SPARSE, 0)
+    ws_sp = torch.empty(max(1, nsp), dtype=torch.uint8, device="cuda")
+    log(f"  sparse workspace {nsp} bytes")
     for l, qs_np in enumerate(inp["q_sparse_dec"]):
         qs = to_dev_bf16(qs_np)
         o64, o16 = oracle.decode_sparse_attn(qs_np, inp["k"], inp["v"], cu, Hq, Hkv, idx,
                                              scale=w.scale)
         out32 = torch.empty((B, Hq, w.d), dtype=torch.float32, device="cuda")
-        hs2.hs2_decode_sparse_attn(dims, cache, qs, k, v, idx_t, out32, hs2.HS2_OUT_F32)
+        hs2.hs2_decode_sparse_attn(dims, cache, qs, k, v, idx_t, out32, hs2.HS2_OUT_F32, ws_sp)
         out16 = torch.empty((B, Hq, w.d), dtype=torch.bfloat16, device="cuda")
-        hs2.hs2_decode_sparse_attn(dims, cache, qs, k, v, idx_t, out16, hs2.HS2_OUT_BF16)
+        hs2.hs2_decode_sparse_attn(dims, cache, qs, k, v, idx_t, out16, hs2.HS2_OUT_BF16, ws_sp)
         torch.cuda.synchronize()
         err4 = np.abs(out32.cpu().numpy() - o64).max()
         g16 = synthgen.bf16_to_float(from_dev_bf16(out16)).astype(np.float64)
@@ -127,3 +130,30 @@ def test_decode_long_caches():
     w = synthgen.custom([32768, 1, 5000, 70001, 32769, 1153, 1152, 20000], Hq=32, Hkv=8, K=1024,
                         W=128, n_sparse=1, seed=1101)
     run_decode(w)
+
+
+def test_decode_zero_queries_tie_rule_bit_exact():
+    """q = 0: every score ties, so the lowest positions win. The 9000-token cache
+    overflows the compacted candidate path (all scores reach the sampled
+    threshold) and takes the full-row path; the short caches take the compacted
+    path. Both must equal the oracle exactly."""
+    import oracle
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    w = synthgen.custom([9000, 700, 300, 5], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=13)
+    inp = synthgen.make_decode_inputs(w)
+    inp["q_dec"][:] = 0
+    cu = inp["cu_seqlens"]
+    B, KW = len(w.lengths), w.K + w.W
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    cache = hs2.VarlenArgs(cu_dev, [int(x) for x in cu])
+    dims = hs2.make_dims(w.Hq, w.Hkv, w.K, w.W, w.scale)
+    ws = torch.empty(hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SELECT, 0),
+                     dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, w.Hkv, KW), dtype=torch.int32, device="cuda")
+    hs2.hs2_decode_select(dims, cache, to_dev_bf16(inp["q_dec"]), to_dev_bf16(inp["k"]), idx, None,
+                          ws)
+    torch.cuda.synchronize()
+    o_idx, _ = oracle.decode_select(inp["q_dec"], inp["k"], cu, w.Hq, w.Hkv, w.K, w.W,
+                                    scale=w.scale)
+    assert (idx.cpu().numpy().reshape(o_idx.shape) == o_idx).all()

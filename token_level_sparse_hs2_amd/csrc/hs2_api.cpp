@@ -129,6 +129,9 @@ struct DecodeGeometry {
   Geometry geo;
   int n_split = 0, bitmap_words = 0;
   size_t off_z2 = 0, off_part = 0, off_dense = 0, bytes = 0, lds = 0;
+  // sparse layer: n_part waves per (sequence, group) row and their partials
+  int n_part = 1;
+  size_t off_po = 0, off_pml = 0, sparse_bytes = 0;
 };
 
 int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) {
@@ -150,8 +153,24 @@ int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) 
   dg->off_dense = off;
   off = align_up(off + (size_t)v->batch * d->num_kv_heads * max_len * sizeof(uint32_t));
   dg->bytes = off;
-  // histogram, scratch words, two bitmaps of the row's candidates
-  dg->lds = (hs2::kTopkBins + 16 + 2 * (size_t)dg->bitmap_words) * sizeof(uint32_t);
+  // histogram, scratch words, two bitmaps of the row's candidates, compacted candidates
+  dg->lds = (hs2::kTopkBins + 16 + 2 * (size_t)dg->bitmap_words + 2 * (size_t)hs2::kDecodeCandCap) *
+            sizeof(uint32_t);
+  // sparse layer: spread the B * Hkv rows over about 1024 waves, >= 4 index steps each
+  const int64_t rows = (int64_t)v->batch * d->num_kv_heads;
+  const int n_steps = hs2::ceil_div(d->top_k + d->window, 32);
+  const int64_t want = (1024 + rows - 1) / rows;
+  dg->n_part = (int)std::max<int64_t>(
+      1, std::min<int64_t>({want, (int64_t)hs2::ceil_div(n_steps, 4), (int64_t)32}));  // <= kMaxParts
+  if (dg->n_part > 1) {
+    const size_t slots = (size_t)rows * dg->n_part;
+    size_t o2 = 0;
+    dg->off_po = o2;
+    o2 = align_up(o2 + slots * g.G * hs2::kHeadDim * sizeof(float));
+    dg->off_pml = o2;
+    o2 = align_up(o2 + slots * g.G * 2 * sizeof(float));
+    dg->sparse_bytes = o2;
+  }
   return HS2_OK;
 }
 
@@ -264,6 +283,7 @@ int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   p.T = geo.T;
   p.c = scale_log2(d);
   p.out = out;
+  p.n_part = 1;
   hipError_t e = hs2::launch_sparse(geo.G, out_dtype == HS2_OUT_F32, p, s);
   if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
   return HS2_OK;
@@ -294,7 +314,7 @@ int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, i
     DecodeGeometry dg;
     int st = validate_decode(dims, varlen, &dg);
     if (st != HS2_OK) return st;
-    *bytes_out = (op == HS2_OP_DECODE_SPARSE || dg.geo.B == 0) ? 0 : dg.bytes;
+    *bytes_out = dg.geo.B == 0 ? 0 : (op == HS2_OP_DECODE_SPARSE ? dg.sparse_bytes : dg.bytes);
     return HS2_OK;
   }
   if (op != HS2_OP_SELECT && op != HS2_OP_SPARSE && op != HS2_OP_PREFILL_BLOCK)
@@ -383,6 +403,7 @@ int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
   p.K = dims->top_k;
   p.W = dims->window;
   p.max_seqlen = std::max(1, dg.geo.max_len);
+  p.T = dg.geo.T;
   p.n_split = dg.n_split;
   p.bitmap_words = dg.bitmap_words;
   p.c = scale_log2(dims);
@@ -402,14 +423,14 @@ int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
 int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
                            const void* k, const void* v, const int32_t* idx, void* out,
                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   DecodeGeometry dg;
   int st = validate_decode(dims, cache, &dg);
   if (st != HS2_OK) return st;
   if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
   if (dg.geo.B == 0) return HS2_OK;
   if (!q || !k || !v || !idx || !out) return HS2_ERR_INVALID_ARG;
+  if (dg.sparse_bytes > 0 && (!workspace || workspace_bytes < dg.sparse_bytes))
+    return HS2_ERR_WORKSPACE;
   hs2::SparseParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -424,6 +445,12 @@ int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const 
   p.c = scale_log2(dims);
   p.out = out;
   p.decode = 1;
+  p.n_part = dg.n_part;
+  if (dg.n_part > 1) {
+    char* w = static_cast<char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(w + dg.off_po);
+    p.part_ml = reinterpret_cast<float2*>(w + dg.off_pml);
+  }
   hipError_t e = hs2::launch_sparse(dg.geo.G, out_dtype == HS2_OUT_F32, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode sparse attention kernel");
   return HS2_OK;

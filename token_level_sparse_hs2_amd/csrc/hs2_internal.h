@@ -127,10 +127,16 @@ struct SparseParams {
   float c;              // softmax_scale * log2(e)
   void* out;            // [T, Hq, 128] bf16 or f32
   int decode;           // query row r is sequence r at its last position
+  // split rows (decode): n_part waves share a row's index entries, each writing
+  // an unnormalised partial that sparse_combine merges
+  int n_part;           // 1 = one wave per row, output written directly
+  float* part_o;        // [T * n_part * Hkv, G, 128] partial P.V (fp32)
+  float2* part_ml;      // [T * n_part * Hkv, G] (reference, sum) of each partial
 };
 
 // Decode step: one query per sequence at its last cached position.
-constexpr int kDecodeSplit = 1024;  // cached keys per logits workgroup
+constexpr int kDecodeSplit = 1024;    // cached keys per logits workgroup
+constexpr int kDecodeCandCap = 4096;  // candidates ranked in LDS per decode row
 
 struct DecodeParams {
   const uint16_t* q;    // [B, Hq, 128]
@@ -141,7 +147,8 @@ struct DecodeParams {
   int n_split;          // ceil(max_seqlen / kDecodeSplit)
   int bitmap_words;     // ceil(max_seqlen / 32)
   float c;              // softmax_scale * log2(e)
-  float* z2;            // [T, Hq]: c * q.k of every cached key and query head
+  int64_t T;            // cached tokens
+  float* z2;            // [Hkv, T, G]: c * q.k of every cached key and the group's heads
   float2* part;         // [B, Hkv, n_split, G]: per split (max, sum of exp2(z2 - max))
   uint32_t* dense;      // [B * Hkv, max_seqlen] S bits
   int32_t* idx;         // [B, Hkv, K+W]

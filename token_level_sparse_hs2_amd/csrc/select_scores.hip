@@ -564,7 +564,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 // ---------------------------------------------------------------------------
 // Decode step, logits. Sequence b's query (its newest token, at position
 // L_b - 1) against every cached key: z2[j, h] = c * <q[b,h], k[j,g]> for the
-// group's heads, written to p.z2 in the [T, Hq] layout, and per split the
+// group's heads, written to p.z2 in the [Hkv, T, G] layout (each group's run
+// is contiguous for the select kernel's reads), and per split the
 // (max, sum of exp2(z2 - max)) of each head, from which the select kernel forms
 // the full layer's log-sum-exp. Grid (split, g, b): kDecodeSplit keys per
 // workgroup, 4 waves x 16 keys per step on v_mfma_f32_16x16x32_bf16 with the
@@ -608,12 +609,21 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
   for (int i = 0; i < 4; i++) { m[i] = -INFINITY; sm[i] = 0.f; }
   const uint16_t* kg = p.k + ((size_t)base * Hkv + g) * kHeadDim;
   const size_t kstride = (size_t)Hkv * kHeadDim;
-  for (int jt = j0 + 16 * w; jt < j1; jt += 64) {
-    // B operand: key jt + lc (clamped to the split; masked below), d = 32 ks + 8 lq
+  // B operand: key jt + lc (clamped to the split; masked below), d = 32 ks + 8 lq.
+  // The next step's rows are in flight while this step computes (the loads are
+  // unconditional, clamped, so the compiler's wait leaves them in flight).
+  auto load_keys = [&](int jt, u32x4 (&kv)[4]) {
     const int j = min(jt + lc, j1 - 1);
-    u32x4 kv[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) kv[ks] = to_u32x4(ldg128(kg + (size_t)j * kstride + 32 * ks + 8 * lq));
+  };
+  u32x4 kn[4];
+  load_keys(j0 + 16 * w, kn);
+  for (int jt = j0 + 16 * w; jt < j1; jt += 64) {
+    u32x4 kv[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) kv[ks] = kn[ks];
+    load_keys(jt + 64, kn);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) acc = mfma16x16x32(qa[ks], as_bf16x8(kv[ks]), acc);
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; i++) z[i] = kval ? acc[i] * c : -INFINITY;
     if (kval && 4 * lq < G) {  // heads 4 lq .. of key jt + lc
-      float* dst = p.z2 + (size_t)(base + jt + lc) * Hq + g * G + 4 * lq;
+      float* dst = p.z2 + ((size_t)g * p.T + base + jt + lc) * G + 4 * lq;
       if constexpr (G >= 4) {
         *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
       } else {

@@ -484,9 +484,14 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
 // ---------------------------------------------------------------------------
 // Decode step, selection: one workgroup per (KV group, sequence). The split
 // partials give each head's log-sum-exp over all cached keys; S[j] for every
-// candidate j <= t - W (t = L_b - 1) goes to a scratch row, then the same exact
-// radix select and assembly as the exact path (no sampled threshold).
+// candidate j <= t - W (t = L_b - 1) goes to a scratch row. A threshold tau is
+// read off a 1-in-16 sample of the row (the sample's r-th largest value); if at
+// least K scores reach it, the top K all do, so only those (compacted into LDS)
+// go through the exact radix select; otherwise the whole row does. Either way
+// the result is the exact top K, ties to the lower position.
 // ---------------------------------------------------------------------------
+constexpr int kDecodeSampleStride = 16;
+
 template <int G>
 __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(DecodeParams p) {
   extern __shared__ uint32_t smem[];
@@ -496,7 +501,8 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(DecodeParams
   sh.misc = reinterpret_cast<int32_t*>(smem + kTopkBins);
   sh.sel = smem + kTopkBins + 16;
   sh.tie = sh.sel + p.bitmap_words;
-  sh.keys = nullptr;
+  sh.keys = sh.tie + p.bitmap_words;                   // [kDecodeCandCap] compacted S bits
+  uint32_t* cpos = sh.keys + kDecodeCandCap;           // [kDecodeCandCap] their positions
   sh.qf = nullptr;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int base = p.cu[b], L = p.cu[b + 1] - base;
@@ -525,20 +531,69 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(DecodeParams
 #pragma unroll
   for (int h = 0; h < G; h++) lse[h] = lse_s[h];
   uint32_t* dense = p.dense + ((size_t)b * p.Hkv + g) * p.max_seqlen;
-  for (int j = tid; j < n_c; j += kSelThreads) {
-    const float* zr = p.z2 + (size_t)(base + j) * p.Hq + g * G;
-    float sum = 0.f;
+  // the strided loops below take kBatch elements per thread per round, every load
+  // issued before the first use (one load in flight per thread would wait out a
+  // memory latency per element); indices past the end are clamped and discarded
+  constexpr int kBatch = 8;
+  const float* zg = p.z2 + ((size_t)g * p.T + base) * G;
+  for (int j0 = 0; j0 < n_c; j0 += kBatch * kSelThreads) {
+    float zb[kBatch][G];
 #pragma unroll
-    for (int h = 0; h < G; h++) sum += fast_exp2(zr[h] - lse[h]);
-    dense[j] = __float_as_uint(sum);
+    for (int u = 0; u < kBatch; u++) {
+      const int j = min(j0 + u * kSelThreads + tid, n_c - 1);
+#pragma unroll
+      for (int h = 0; h < G; h++) zb[u][h] = zg[(size_t)j * G + h];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int j = j0 + u * kSelThreads + tid;
+      float sum = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; h++) sum += fast_exp2(zb[u][h] - lse[h]);
+      if (j < n_c) dense[j] = __float_as_uint(sum);
+    }
   }
   __syncthreads();
+  auto batched = [&](auto&& fn) {  // fn(j, S bits) for every j < n_c, batched loads
+    for (int j0 = 0; j0 < n_c; j0 += kBatch * kSelThreads) {
+      uint32_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; u++) v[u] = dense[min(j0 + u * kSelThreads + tid, n_c - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; u++) {
+        const int j = j0 + u * kSelThreads + tid;
+        if (j < n_c) fn(j, v[u]);
+      }
+    }
+  };
+  // threshold from the sample: its r-th largest, r ~ 1.5 K n_s / n_c + 16
+  const int n_s = ceil_div(n_c, kDecodeSampleStride);
+  const int r = min(n_s, (int)ceilf(1.5f * (float)p.K * (float)n_s / (float)n_c) + 16);
+  int krem_s;
+  const uint32_t tau = radix_kth([&](int i) { return dense[i * kDecodeSampleStride]; }, n_s, r, sh,
+                                 &krem_s);
+  // how many reach tau (a plain block sum, no contended atomics)
+  int cnt = 0;
+  batched([&](int, uint32_t x) { cnt += x >= tau ? 1 : 0; });
+  int n_pass;
+  const int off = block_excl_scan(cnt, sh.misc, &n_pass);
   int krem;
-  const uint32_t kth = radix_kth([&](int i) { return dense[i]; }, n_c, p.K, sh, &krem);
-  const int nwords = ceil_div(n_c, 32);
-  mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth, krem,
-                nwords, sh);
-  write_selected_row(nwords, n_c, t, KW, row, sh);
+  uint32_t kth;
+  if (n_pass >= p.K && n_pass <= kDecodeCandCap) {
+    int o = off;  // compact the passing scores and positions (same order as the count)
+    batched([&](int j, uint32_t x) {
+      if (x >= tau) { sh.keys[o] = x; cpos[o] = (uint32_t)j; o++; }
+    });
+    __syncthreads();
+    kth = radix_kth([&](int i) { return sh.keys[i]; }, n_pass, p.K, sh, &krem);
+    mark_selected([&](int i) { return sh.keys[i]; }, [&](int i) { return cpos[i]; }, n_pass, kth,
+                  krem, ceil_div(n_c, 32), sh);
+  } else {  // the sample misled: rank the whole row
+    kth = radix_kth([&](int i) { return dense[i]; }, n_c, p.K, sh, &krem);
+    mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth,
+                  krem, ceil_div(n_c, 32), sh);
+  }
+  write_selected_row(ceil_div(n_c, 32), n_c, t, KW, row, sh);
   if (kth_out && tid == 0) *kth_out = __uint_as_float(kth);
 }
 

@@ -22,6 +22,7 @@
 namespace hs2 {
 
 constexpr int kChunk = 32;  // index entries per step
+constexpr int kMaxParts = 32;  // partials merged per row (split rows of a decode step)
 
 template <int G, bool PRECISE>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
@@ -31,8 +32,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   const int lq = l >> 4, lc = l & 15;
   const int Hkv = p.Hkv, Hq = p.Hq, KW = p.KW;
   const int g = blockIdx.x % Hkv;
-  const int64_t tg = (int64_t)(blockIdx.x / Hkv) * 4 + w;
-  if (tg >= p.T) return;
+  const int64_t vr = (int64_t)(blockIdx.x / Hkv) * 4 + w;  // row x part
+  if (vr >= p.T * p.n_part) return;
+  const int64_t tg = vr / p.n_part;
+  const int part = (int)(vr % p.n_part);
   // query row tg: a token of the packed batch, or (decode) sequence tg at its
   // last cached position
   const int seq = p.decode ? (int)tg : find_seq(p.cu, p.B, tg);
@@ -41,14 +44,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   const int32_t* irow = p.idx + ((size_t)tg * Hkv + g) * KW;
   const float c = p.c;
 
-  // Q'^T operand (B): column = head (lane & 15) < G, k = d slice
+  // Q'^T operand (B): column = head (lane & 15) < G, k = d slice (loads first,
+  // columns >= G zeroed afterwards)
   bf16x8 qb[4];
+  {
+    u32x4 v[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ks++) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (lc < G)
-      v = to_u32x4(ldg128(p.q + ((size_t)tg * Hq + g * G + lc) * kHeadDim + 32 * ks + 8 * lq));
-    qb[ks] = as_bf16x8(v);
+    for (int ks = 0; ks < 4; ks++)
+      v[ks] = to_u32x4(ldg128(p.q + ((size_t)tg * Hq + g * G + min(lc, G - 1)) * kHeadDim +
+                              32 * ks + 8 * lq));
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      if (lc >= G) v[ks] = u32x4{0u, 0u, 0u, 0u};
+      qb[ks] = as_bf16x8(v[ks]);
+    }
   }
 
   float m = -INFINITY, lsum = 0.f;
@@ -62,6 +71,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   const uint32_t row_stride = (uint32_t)Hkv * kHeadDim * 2;
   uint4(*vl)[16] = vlds[w];
   const int n_chunks = (KW + kChunk - 1) / kChunk;
+  // this wave's steps: all of them, or its part's share
+  const int per_part = (n_chunks + p.n_part - 1) / p.n_part;
+  const int c_begin = part * per_part, c_end = min(n_chunks, c_begin + per_part);
 
   // index entries of chunk c for the lane's two A rows (keys 16*mt + lc)
   // Index entries of chunk c for the lane's two A rows (keys 16*mt + lc). The raw
@@ -76,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       const int e = c * kChunk + 16 * mt + lc;
-      j[mt] = (c < n_chunks && e < KW) ? r[mt] : -1;
+      j[mt] = (c < c_end && e < KW) ? r[mt] : -1;
     }
   };
   // gather the chunk's K and V rows, fully coalesced: load r covers keys
@@ -211,15 +223,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   // -1: their gathers read row 0 and are skipped.
   int r1[2], r2[2], ja[2], jb[2];
   Gather ga, gb;
-  load_raw(0, ja);
-  load_raw(1, r1);
-  load_raw(2, r2);
+  load_raw(c_begin, ja);
+  load_raw(c_begin + 1, r1);
+  load_raw(c_begin + 2, r2);
   // keep this issue order (as in the loop body: idx entries older than the gather
   // behind them), so the loop's waits can leave the gather in flight
   __builtin_amdgcn_sched_barrier(0);
-  valid_idx(0, ja, ja);
+  valid_idx(c_begin, ja, ja);
   gather(ja, ga);
-  for (int c = 0; c < n_chunks; c += 2) {
+  for (int c = c_begin; c < c_end; c += 2) {
     valid_idx(c + 1, r1, jb);
     gather(jb, gb);
     load_raw(c + 3, r1);
@@ -234,6 +246,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   }
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
+  if (p.n_part > 1) {  // unnormalised partial of this part (m = -inf, sum 0 if it had none)
+    if (lc < G) {
+      const size_t slot = (size_t)vr * Hkv + g;
+      float* po = p.part_o + (slot * G + lc) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++)
+        *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lq) = o[dt];
+      if (lq == 0) p.part_ml[slot * G + lc] = make_float2(m, lsum);
+    }
+    return;
+  }
   if (lc < G) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const size_t ob = ((size_t)tg * Hq + g * G + lc) * kHeadDim;
@@ -252,15 +275,64 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   }
 }
 
+// Merges the n_part (<= kMaxParts) partials of each (row, group): per head and d,
+// o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s (0 if no part
+// saw a valid entry). One workgroup per (row, group): the parts' (m, l) go to LDS,
+// one thread per head turns them into weights, then every output element sums its
+// parts with all loads in flight.
+template <int G, bool PRECISE>
+__global__ __launch_bounds__(256) void sparse_combine_kernel(SparseParams p) {
+  __shared__ float2 ml[kMaxParts * G];
+  __shared__ float wgt[kMaxParts * G];
+  const int64_t tg = blockIdx.x / p.Hkv;
+  const int g = (int)(blockIdx.x % p.Hkv);
+  const int tid = threadIdx.x, np = p.n_part;
+  auto slot = [&](int s) { return (size_t)(tg * np + s) * p.Hkv + g; };
+  for (int i = tid; i < np * G; i += 256) ml[i] = p.part_ml[slot(i / G) * G + i % G];
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int s = 0; s < np; s++) M = fmaxf(M, ml[s * G + tid].x);
+    float den = 0.f;
+    if (M > -INFINITY)
+      for (int s = 0; s < np; s++) den += ml[s * G + tid].y * fast_exp2(ml[s * G + tid].x - M);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int s = 0; s < np; s++)
+      wgt[s * G + tid] = M > -INFINITY ? fast_exp2(ml[s * G + tid].x - M) * inv : 0.f;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * kHeadDim; i += 256) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float v[kMaxParts];
+#pragma unroll
+    for (int s = 0; s < kMaxParts; s++)
+      v[s] = s < np ? p.part_o[(slot(s) * G + h) * kHeadDim + d] : 0.f;
+    float val = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxParts; s++) val += s < np ? v[s] * wgt[s * G + h] : 0.f;
+    const size_t o = ((size_t)tg * p.Hq + g * G + h) * kHeadDim + d;
+    if constexpr (PRECISE) static_cast<float*>(p.out)[o] = val;
+    else static_cast<__bf16*>(p.out)[o] = (__bf16)val;
+  }
+}
+
 template <int G>
 static hipError_t launch_sparse_g(bool precise, const SparseParams& p, hipStream_t s) {
-  const int64_t blocks = ((p.T + 3) / 4) * p.Hkv;
+  const int64_t blocks = ((p.T * p.n_part + 3) / 4) * p.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (precise)
     hipLaunchKernelGGL((sparse_attn_kernel<G, true>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((sparse_attn_kernel<G, false>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_part <= 1) return e;
+  const int64_t rows = p.T * p.Hkv;
+  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (precise)
+    hipLaunchKernelGGL((sparse_combine_kernel<G, true>), dim3((unsigned)rows), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((sparse_combine_kernel<G, false>), dim3((unsigned)rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
