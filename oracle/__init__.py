@@ -49,6 +49,9 @@ def _load():
     lib.hs2o_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, vp, vp, i64,
                                      vp, vp, i32]
     lib.hs2o_sparse_attn.restype = i32
+    lib.hs2o_select_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, vp,
+                                       i64, vp, vp, i32]
+    lib.hs2o_select_blocks.restype = i32
     lib.hs2o_decode_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, vp, vp, i32]
     lib.hs2o_decode_select.restype = i32
     lib.hs2o_decode_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, vp, vp,
@@ -74,11 +77,13 @@ def _cu(cu):
     return np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
 
 
-def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None):
+def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None, block=0):
     """Index rows and K-th scores.
 
     q [T,Hq,d], k [T,Hkv,d] bf16 bits; rows: None (all T*Hkv rows, row id = t*Hkv+g)
-    or an int64 array of row ids. Returns (idx [n, K+W] int32, kth [n] float64).
+    or an int64 array of row ids. block > 0 selects aligned blocks of that many
+    candidate tokens (K a multiple of block) by the sum of S over the block; kth is
+    then the lowest selected block's score. Returns (idx [n, K+W] int32, kth [n] float64).
     """
     lib = _load()
     q, k, cu = _u16(q), _u16(k), _cu(cu_seqlens)
@@ -95,9 +100,9 @@ def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None
     kth = np.empty(n, dtype=np.float64)
     if n == 0:
         return idx, kth
-    r = lib.hs2o_select(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d, scale, K, W,
-                        rows.ctypes.data if rows is not None else None, n, idx.ctypes.data,
-                        kth.ctypes.data, nthreads or default_threads())
+    r = lib.hs2o_select_blocks(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d, scale,
+                               K, W, int(block), rows.ctypes.data if rows is not None else None, n,
+                               idx.ctypes.data, kth.ctypes.data, nthreads or default_threads())
     if r != 0:
         raise ValueError("hs2o_select: bad arguments")
     return idx, kth

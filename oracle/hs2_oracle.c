@@ -80,6 +80,7 @@ typedef struct {
   int B, Hq, Hkv, d, K, W;
   double scale;
   const int32_t* cu;
+  int block; /* 0: single-token selection; > 0: blocks of this many tokens (K a multiple) */
 } dims_t;
 
 static int find_seq(const dims_t* D, int64_t t_global) {
@@ -149,6 +150,25 @@ static void row_select(const dims_t* D, const double* S, int64_t t, int32_t* idx
     if (n_cand <= K)
       for (int64_t j = 0; j < n_cand; j++) mark[j] = 1;
     *kth = -1.0;
+  } else if (D->block > 0) {
+    /* block selection (the previous generation's granularity, HySparse2 news
+     * summary, block-vs-token paragraph and ablation): the candidates are cut
+     * into aligned blocks of D->block tokens; a block scores the sum of S over
+     * its candidate tokens; the K / block best blocks (score desc, block asc)
+     * are taken whole. */
+    const int bs = D->block;
+    const int64_t nb = (n_cand + bs - 1) / bs;
+    const int n_sel = K / bs;
+    for (int64_t b = 0; b < nb; b++) {
+      double sum = 0.0;
+      for (int64_t j = b * bs; j < (b + 1) * bs && j < n_cand; j++) sum += S[j];
+      cbuf[b].s = sum;
+      cbuf[b].j = b;
+    }
+    qsort(cbuf, (size_t)nb, sizeof(cand_t), cmp_cand);
+    for (int i = 0; i < n_sel; i++)
+      for (int64_t j = cbuf[i].j * bs; j < (cbuf[i].j + 1) * bs && j < n_cand; j++) mark[j] = 1;
+    *kth = n_sel > 0 ? cbuf[n_sel - 1].s : -1.0;
   } else {
     for (int64_t j = 0; j < n_cand; j++) { cbuf[j].s = S[j]; cbuf[j].j = j; }
     qsort(cbuf, (size_t)n_cand, sizeof(cand_t), cmp_cand);
@@ -293,6 +313,7 @@ static void* sparse_worker(void* arg) {
 static int check_dims(const dims_t* D) {
   if (D->B < 1 || D->Hq < 1 || D->Hkv < 1 || D->Hq % D->Hkv || D->d < 1 || D->d > 1024) return -1;
   if (D->K < 0 || D->W < 0 || D->K + D->W < 1) return -1;
+  if (D->block < 0 || (D->block > 0 && D->K % D->block)) return -1;
   if (D->cu[0] != 0) return -1;
   for (int i = 0; i < D->B; i++)
     if (D->cu[i + 1] < D->cu[i]) return -1;
@@ -332,7 +353,26 @@ static int max_len(const dims_t* D) {
 int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq, int Hkv,
                 int d, double scale, int K, int W, const int64_t* rows, int64_t n_rows,
                 int32_t* idx_out, double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0};
+  if (!q || !k || !cu || !idx_out || check_dims(&D)) return -1;
+  int64_t T = cu[B];
+  if (!rows) n_rows = T * Hkv;
+  for (int64_t r = 0; rows && r < n_rows; r++)
+    if (rows[r] < 0 || rows[r] >= T * Hkv) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q; J.k = k; J.rows = rows; J.n_rows = n_rows;
+  J.idx_out = idx_out; J.kth_out = kth_out; J.max_len = max_len(&D);
+  return run(&J, select_worker, nthreads);
+}
+
+/* hs2o_select with block selection: blocks of `block` tokens (K a multiple of
+ * it); kth_out is the score of the lowest-ranked selected block. block = 0 is
+ * hs2o_select. */
+int hs2o_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq,
+                       int Hkv, int d, double scale, int K, int W, int block, const int64_t* rows,
+                       int64_t n_rows, int32_t* idx_out, double* kth_out, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block};
   if (!q || !k || !cu || !idx_out || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!rows) n_rows = T * Hkv;
@@ -349,7 +389,7 @@ int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, 
 int hs2o_group_scores(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq,
                       int Hkv, int d, double scale, int64_t t_global, int g, double* S_out,
                       double* m_out, double* l_out) {
-  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu};
+  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0};
   if (!q || !k || !cu || !S_out || check_dims(&D) || g < 0 || g >= Hkv) return -1;
   if (t_global < 0 || t_global >= cu[B]) return -1;
   int i = find_seq(&D, t_global);
@@ -371,7 +411,7 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      int B, int Hq, int Hkv, int d, double scale, int KW, const int32_t* idx,
                      const int64_t* tokens, int64_t n_tokens, double* o64, uint16_t* o16,
                      int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu};
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0};
   if (!q || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
   int64_t T = cu[B];
   if (!tokens) n_tokens = T;
@@ -393,7 +433,7 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* cu, int B, int Hq,
                        int Hkv, int d, double scale, int K, int W, int32_t* idx_out,
                        double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0};
   if (!q_dec || !k || !cu || !idx_out || check_dims(&D)) return -1;
   for (int b = 0; b < B; b++)
     if (cu[b + 1] - cu[b] < 1) return -1;
@@ -409,7 +449,7 @@ int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* 
 int hs2o_decode_sparse_attn(const uint16_t* q_dec, const uint16_t* k, const uint16_t* v,
                             const int32_t* cu, int B, int Hq, int Hkv, int d, double scale, int KW,
                             const int32_t* idx, double* o64, uint16_t* o16, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu};
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0};
   if (!q_dec || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
   for (int b = 0; b < B; b++)
     if (cu[b + 1] - cu[b] < 1) return -1;

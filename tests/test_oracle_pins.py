@@ -375,3 +375,42 @@ def test_decode_rejects_empty_cache():
     q, k, v, cu = rand_inputs([3, 0, 5], 4, 1, 128, seed=3)
     with pytest.raises(ValueError):
         oracle.decode_select(q[:3], k, cu, 4, 1, 4, 2)
+
+
+def test_block_size_one_is_token_selection():
+    q, k, v, cu = rand_inputs([1, 30, 90, 200], 8, 2, 128, seed=21)
+    a_idx, a_kth = oracle.select(q, k, cu, 8, 2, 16, 4)
+    b_idx, b_kth = oracle.select(q, k, cu, 8, 2, 16, 4, block=1)
+    assert (a_idx == b_idx).all() and np.array_equal(a_kth, b_kth)
+
+
+@pytest.mark.parametrize("bs,K,W", [(4, 8, 3), (4, 12, 0), (5, 10, 2)])
+def test_block_selection_bruteforce(bs, K, W):
+    """Block mode against a brute force over block subsets: the chosen blocks are
+    the subset of K/bs blocks with the largest total score (blocks cut from the
+    candidates [0, t-W], scored by the sum of the pinned group score S)."""
+    lengths = [3, 17, 40, 41]
+    Hq, Hkv, d = 4, 2, 128
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=22 + bs + K)
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W, block=bs)
+    T = int(cu[-1])
+    for r in range(T * Hkv):
+        tg, g = divmod(r, Hkv)
+        i = int(np.searchsorted(cu, tg, side="right") - 1)
+        t = tg - int(cu[i])
+        n_c = max(0, t - W + 1)
+        window = set(range(max(0, t - W + 1), t + 1))
+        if n_c <= K:
+            want = set(range(n_c)) | window
+            assert kth[r] == -1.0
+        else:
+            S, _, _ = oracle.group_scores(q, k, cu, Hq, Hkv, tg, g)
+            nb = -(-n_c // bs)
+            score = [S[b * bs:min((b + 1) * bs, n_c)].sum() for b in range(nb)]
+            best = max(itertools.combinations(range(nb), K // bs),
+                       key=lambda c: sum(score[b] for b in c))
+            want = {j for b in best for j in range(b * bs, min((b + 1) * bs, n_c))} | window
+            assert abs(kth[r] - min(score[b] for b in best)) <= 1e-12
+        got = idx[r][idx[r] >= 0]
+        assert list(got) == sorted(want), (r, t)
+        assert (idx[r][len(got):] == -1).all()
