@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=640)  # about 10 s of oracle work at 32k
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--block", action="store_true",
+                    help="64-token block selection (the pages' ablation baseline) instead of tokens")
     ap.add_argument("--decode", default=None, choices=["decode-32k", "decode-varlen"],
                     help="time the decode step on this cache workload instead of prefill")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -119,7 +121,7 @@ def main():
     w = synthgen.workload(args.workload)
     t_in = time.perf_counter()
     inp = synthgen.make_inputs(w)
-    case = GpuCase(w, inp)
+    case = GpuCase(w, inp, flags=hs2.HS2_FLAG_BLOCK_SELECT if args.block else 0)
     gen_s = time.perf_counter() - t_in
     T, Hq, Hkv, d, K, W = w.total, w.Hq, w.Hkv, w.d, w.K, w.W
     outs = [torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in case.q_sparse]
@@ -201,7 +203,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded bf16 N(0,1) Q/K/V (SplitMix64 + Box-Muller)"
                 + (", needle keys" if w.needles else ""),
-        "config": {"workload": f"{args.workload}: {wl[args.workload]}", "global_batch": len(w.lengths),
+        "config": {"workload": f"{args.workload}: {wl[args.workload]}"
+                               + (", 64-token block selection" if args.block else ""),
+                   "global_batch": len(w.lengths),
                    "seq_len": max(w.lengths), "tokens": T, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -84,7 +84,16 @@ enum {
 enum {
   /* Skip the sampled threshold: every row with more than top_k candidates is
      selected by the exact full-row path (slow; results obey the same rule). */
-  HS2_FLAG_EXACT_SELECT = 1u
+  HS2_FLAG_EXACT_SELECT = 1u,
+  /* Select aligned 64-token blocks instead of single tokens (the previous
+     generation's granularity, the baseline of the pages' block-vs-token
+     ablation: HySparse2 news summary, ablation paragraph): the candidates
+     [0, t-W] are cut into blocks [64i, 64i+63]; a block scores the sum of S over
+     its candidate tokens; the top_k/64 best blocks (score desc, block asc) are
+     taken whole, then the window. top_k must be a multiple of 64; kth_score is
+     the lowest selected block's score. Prefill only (hs2_select,
+     hs2_prefill_block); every block row is ranked exactly. */
+  HS2_FLAG_BLOCK_SELECT = 2u
 };
 
 typedef struct {

@@ -204,3 +204,14 @@ def test_decode_validation_and_workspace(lib):
     v1 = varlen([1000])
     assert hs2.hs2_workspace_size(d, v1, hs2.HS2_OP_DECODE_SPARSE) > 0
     assert hs2.hs2_workspace_size(d, hs2.VarlenArgs(FakeDev(0), [0]), hs2.HS2_OP_DECODE_SELECT) == 0
+
+
+def test_block_flag_validation(lib):
+    d = hs2.make_dims(32, 8, 1000, 128, flags=hs2.HS2_FLAG_BLOCK_SELECT)  # K not a multiple of 64
+    assert call_select(d, varlen([5000])) == hs2.HS2_ERR_INVALID_ARG
+    d = hs2.make_dims(32, 8, 1024, 128, flags=hs2.HS2_FLAG_BLOCK_SELECT)
+    v = varlen([5000])
+    assert hs2.hs2_workspace_size(d, v, hs2.HS2_OP_SELECT) > 0
+    L = hs2.load_library()
+    r = L.hs2_decode_select(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, None, 1, 1 << 40, None)
+    assert r == hs2.HS2_ERR_UNSUPPORTED  # decode selects single tokens

@@ -36,6 +36,7 @@ HS2_OP_PREFILL_BLOCK = 3
 HS2_OP_DECODE_SELECT = 4
 HS2_OP_DECODE_SPARSE = 5
 HS2_FLAG_EXACT_SELECT = 1
+HS2_FLAG_BLOCK_SELECT = 2
 HS2_MAX_SEQLEN = 262144
 
 

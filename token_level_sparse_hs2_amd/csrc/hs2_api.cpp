@@ -40,6 +40,7 @@ struct Geometry {
   size_t exact_lds = 0;
   int topk_rows_per_block = 4;
   bool exact_only = false;  // K above the register-ranked limit: every row takes the exact path
+  int block = 0;            // block selection: tokens per block
 };
 
 bool g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
@@ -52,7 +53,8 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
       (int64_t)d->top_k + d->window > (1 << 24))
     return HS2_ERR_INVALID_ARG;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return HS2_ERR_INVALID_ARG;
-  if (d->flags & ~(uint32_t)HS2_FLAG_EXACT_SELECT) return HS2_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(HS2_FLAG_EXACT_SELECT | HS2_FLAG_BLOCK_SELECT)) return HS2_ERR_INVALID_ARG;
+  if ((d->flags & HS2_FLAG_BLOCK_SELECT) && d->top_k % hs2::kBlockTokens) return HS2_ERR_INVALID_ARG;
   if (v->batch < 0) return HS2_ERR_INVALID_ARG;
   if (d->head_dim != hs2::kHeadDim) return HS2_ERR_UNSUPPORTED;
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -87,8 +89,11 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
 
   // candidate rows: C slots each; chunks of whole tasks under the byte budget
   const int K = d->top_k;
-  geo->exact_only = K > hs2::kMaxRankedK;
+  geo->block = (d->flags & HS2_FLAG_BLOCK_SELECT) ? hs2::kBlockTokens : 0;
+  geo->exact_only = !geo->block && K > hs2::kMaxRankedK;
   int64_t cap = geo->exact_only ? 64 : std::max<int64_t>(hs2::kMinCandCap, 2LL * K);
+  if (geo->block)  // one entry per candidate block of the longest row (<= 4096, ranked in registers)
+    cap = std::max<int64_t>(64, hs2::ceil_div(std::max(1, max_len), hs2::kBlockTokens));
   cap = (cap + 63) / 64 * 64;
   geo->cand_cap = (int)cap;
   const int64_t rows_per_task = (int64_t)d->num_kv_heads * geo->tok;
@@ -137,6 +142,7 @@ struct DecodeGeometry {
 int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) {
   int st = validate(d, v, &dg->geo);
   if (st != HS2_OK) return st;
+  if (d->flags & HS2_FLAG_BLOCK_SELECT) return HS2_ERR_UNSUPPORTED;  // decode selects tokens
   const Geometry& g = dg->geo;
   if (g.B == 0) return HS2_OK;
   for (int i = 0; i < v->batch; i++)
@@ -213,6 +219,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.bin_base = (int)(gk_bits >> 20) - (hs2::kBins - 1);
   sp.cand_cap = geo.cand_cap;
   sp.flags = d->flags | (geo.exact_only ? (uint32_t)HS2_FLAG_EXACT_SELECT : 0u);
+  sp.block = geo.block;
   sp.lse2 = lse2;
   sp.cand = cand;
   sp.cand_count = count;
@@ -229,6 +236,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.W = d->window;
   tp.max_tiles = geo.max_tiles;
   tp.tok = geo.tok;
+  tp.block = geo.block;
   tp.cand_cap = geo.cand_cap;
   tp.bitmap_words = geo.bitmap_words;
   tp.c = sp.c;

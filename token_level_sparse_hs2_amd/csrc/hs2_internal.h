@@ -21,6 +21,7 @@ constexpr int kMaxRankedK = 2048;  // ... held in registers by the top-K wave (<
                                    // a larger K sends every row to the exact path
 constexpr int64_t kCandBudgetBytes = 4LL << 30;  // candidate buffer cap per chunk
 constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact path
+constexpr int kBlockTokens = 64;                 // tokens per block in block selection (= kKeyTile)
 // sampled threshold: rank r = ceil(kTauAlpha * K * n_sample / n_cand) + kTauBeta
 constexpr float kTauAlpha = 1.2f;
 constexpr int kTauBeta = 24;
@@ -84,6 +85,7 @@ struct ScoreParams {
   const uint32_t* kmax; // [B * Hkv] largest key norm of each (sequence, group), float bits
   int cand_cap;         // C
   uint32_t flags;
+  int block;            // 0, or kBlockTokens: block selection (candidates are block scores)
   float* lse2;          // [T, Hq] log2-domain log-sum-exp of each full-layer row
   uint64_t* cand;       // [chunk rows, C]: (S bits << 32) | position
   int32_t* cand_count;  // [chunk rows]: count, or -1 = exact path
@@ -98,6 +100,7 @@ struct TopkParams {
   int max_tiles;
   int64_t task_begin;
   int tok;              // tokens per task
+  int block;            // 0, or kBlockTokens: candidates are (block score, block index)
   int cand_cap;
   int bitmap_words;     // words per bitmap in LDS (covers max_seqlen)
   float c;

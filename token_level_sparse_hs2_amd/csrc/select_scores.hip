@@ -386,7 +386,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     const int n_c = t - W + 1;
     int mode = kModeTrivial;
     if (tid < ntok && K > 0 && n_c > K) {
-      if (p.flags & 1u) mode = kModeExact;
+      if (p.block) mode = kModeEmit;  // block scores: one entry per candidate block, no sample
+      else if (p.flags & 1u) mode = kModeExact;
       else if (n_c <= p.cand_cap) mode = kModeEmit;
       else mode = kModeSample;
     }
@@ -487,8 +488,47 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     __syncthreads();
   }
 
+  // ================= block mode: the score of every candidate block =========
+  // Block kt (keys 64 kt .. 64 kt + 63, one key tile) of token t scores the sum
+  // of S over its candidate keys j <= t - W; every token with n_c > K gets one
+  // entry (score bits << 32 | kt) per candidate block, ranked by the top-K kernel.
+  if (p.block && sm.any_emit) {
+    uint64_t* cand = p.cand;
+    const int C = p.cand_cap;
+    sweep(n_kt2, 0, 1, cand_end, Ring{}, [&](int kt, int buf) HS2_INLINE {
+      compute(buf);
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++) {
+        float bsum[NT];
+#pragma unroll
+        for (int u = 0; u < NT; u++) bsum[u] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ct++) {
+          float S[NT];
+          group_scores(rt, ct, S);
+          const int j = kt * kKeyTile + 16 * ct + lc;
+#pragma unroll
+          for (int u = 0; u < NT; u++)
+            if (j <= t0 + token_of(rt, u) - W) bsum[u] += S[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NT; u++) {
+          float b = bsum[u];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) b += shfl_xor_f(b, off);  // the token's 16 key lanes
+          const int tl = token_of(rt, u);
+          if (owner && lc == 0 && tl < TOK && sm.mode[tl] == kModeEmit &&
+              kt * kKeyTile <= t0 + tl - W)
+            cand[(size_t)(slot0 + tl) * C + kt] = ((uint64_t)__float_as_uint(b) << 32) | (uint32_t)kt;
+        }
+      }
+    });
+    if (tid < TOK && sm.mode[tid] == kModeEmit) sm.cnt[tid] = ceil_div(t0 + tid - W + 1, kKeyTile);
+    __syncthreads();
+  }
+
   // ========================= sweep 3: collect ===============================
-  if (sm.any_emit) {
+  if (!p.block && sm.any_emit) {
     float tau_r[RT][NT];
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
@@ -551,7 +591,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
       count = -1;
     } else if (mode == kModeEmit) {
       count = sm.cnt[tid];
-      if (count > p.cand_cap || count < K) count = -1;
+      // block mode: ceil(n_c / 64) > K / 64 block entries, always within C
+      if (!p.block && (count > p.cand_cap || count < K)) count = -1;
     }
     p.cand_count[slot0 + tid] = count;
     if (count < 0) {

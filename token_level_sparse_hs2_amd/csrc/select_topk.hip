@@ -322,8 +322,10 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   // radix select of the K-th largest key below the common prefix, 8 bits per pass
+  // (block mode: the (K / 64)-th largest block score)
+  const int k_sel = p.block ? p.K / p.block : p.K;
   uint32_t prefix = mx, mask = 0xFFFFFFFFu;
-  int kr = p.K;
+  int kr = k_sel;
   if (mn != mx) {
     int hi = 31 - __clz(mn ^ mx);
     mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
@@ -375,7 +377,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   n_eq = wave_sum_u32(n_eq);
   uint32_t pos_cut = 0xFFFFFFFFu;  // ties with pos <= pos_cut are taken
   if (n_eq != (uint32_t)kr) {
-    uint32_t lo = 0, hi = (uint32_t)n_c - 1;  // smallest cut with >= kr ties at or below it
+    // smallest cut with >= kr ties at or below it (positions, or block indices)
+    uint32_t lo = 0, hi = (uint32_t)(p.block ? count : n_c) - 1;
     while (lo < hi) {
       const uint32_t mid = (lo + hi) >> 1;
       uint32_t c = 0;
@@ -393,8 +396,18 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   wave_lds_fence();
 #pragma unroll
   for (int s = 0; s < NREG; s++) {
-    if (l + 64 * s < count && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut)))
-      atomicOr(&bm[pos[s] >> 5], 1u << (pos[s] & 31));
+    if (l + 64 * s < count && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut))) {
+      if (p.block) {  // the block's candidate tokens [64 b, min(64 b + 64, n_c)): its own two words
+        const int j0 = p.block * (int)pos[s], j1 = min(j0 + p.block, n_c);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int nbits = min(max(j1 - (j0 + 32 * h), 0), 32);
+          if (nbits > 0) bm[(j0 >> 5) + h] = nbits == 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
+        }
+      } else {
+        atomicOr(&bm[pos[s] >> 5], 1u << (pos[s] & 31));
+      }
+    }
   }
   wave_lds_fence();
   // lane l compacts words [l * per, (l + 1) * per): count, one wave scan, write
