@@ -52,6 +52,8 @@ def _load():
     lib.hs2o_select_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, vp,
                                        i64, vp, vp, i32]
     lib.hs2o_select_blocks.restype = i32
+    lib.hs2o_full_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64, vp, vp, i32]
+    lib.hs2o_full_attn.restype = i32
     lib.hs2o_decode_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, vp, vp, i32]
     lib.hs2o_decode_select.restype = i32
     lib.hs2o_decode_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, vp, vp,
@@ -160,6 +162,35 @@ def sparse_attn(q, k, v, cu_seqlens, Hq, Hkv, idx, scale=None, tokens=None, nthr
                              nthreads or default_threads())
     if r != 0:
         raise ValueError("hs2o_sparse_attn: bad arguments")
+    return o64, o16
+
+
+def full_attn(q, k, v, cu_seqlens, Hq, Hkv, scale=None, tokens=None, nthreads=None,
+              want_f64=True, want_bf16=True):
+    """The full layer's dense causal attention output over [0, t] for `tokens`
+    (None = all T). Returns (o64 [n,Hq,d] float64 or None, o16 [n,Hq,d] bf16 bits or None)."""
+    lib = _load()
+    q, k, v, cu = _u16(q), _u16(k), _u16(v), _cu(cu_seqlens)
+    d = q.shape[-1]
+    B = len(cu) - 1
+    T = int(cu[-1])
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    if tokens is not None:
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        n = len(tokens)
+    else:
+        n = T
+    o64 = np.empty((n, Hq, d), dtype=np.float64) if want_f64 else None
+    o16 = np.empty((n, Hq, d), dtype=np.uint16) if want_bf16 else None
+    if n == 0:
+        return o64, o16
+    r = lib.hs2o_full_attn(q.ctypes.data, k.ctypes.data, v.ctypes.data, cu.ctypes.data, B, Hq, Hkv,
+                           d, scale, tokens.ctypes.data if tokens is not None else None, n,
+                           o64.ctypes.data if o64 is not None else None,
+                           o16.ctypes.data if o16 is not None else None,
+                           nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_full_attn: bad arguments")
     return o64, o16
 
 

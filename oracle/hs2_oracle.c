@@ -460,5 +460,74 @@ int hs2o_decode_sparse_attn(const uint16_t* q_dec, const uint16_t* k, const uint
   return run(&J, sparse_worker, nthreads);
 }
 
+/*
+ * The full layer's own attention output (dense causal softmax attention over
+ * [0, t] with the full layer's queries; SHARP walkthrough, section 1.1):
+ * o[t,h] = sum_{j <= t} softmax_j(scale <q[t,h], k[j,g]>) v[j,g]. tokens: global
+ * token ids or NULL for all T; o64 / o16 [n, Hq, d] (nullable).
+ */
+static void* full_worker(void* arg) {
+  job_t* J = (job_t*)arg;
+  const dims_t* D = J->D;
+  const int G = D->Hq / D->Hkv, d = D->d;
+  double* y = (double*)malloc(sizeof(double) * (size_t)J->max_len);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  double qd[1024];
+  for (;;) {
+    int64_t e, s = take(J, 4, &e);
+    if (s >= J->n_rows) break;
+    for (int64_t r = s; r < e; r++) {
+      int64_t tg = J->rows ? J->rows[r] : r;
+      int i = find_seq(D, tg);
+      int64_t base = D->cu[i], t = tg - base;
+      for (int h = 0; h < D->Hq; h++) {
+        const int g = h / G;
+        const uint16_t* qr = J->q + ((size_t)tg * D->Hq + h) * d;
+        for (int c = 0; c < d; c++) qd[c] = bf2d(qr[c]);
+        double mu = -INFINITY;
+        for (int64_t j = 0; j <= t; j++) {
+          const uint16_t* kr = J->k + ((size_t)(base + j) * D->Hkv + g) * d;
+          double dot = 0.0;
+          for (int c = 0; c < d; c++) dot += qd[c] * bf2d(kr[c]);
+          y[j] = D->scale * dot;
+          if (y[j] > mu) mu = y[j];
+        }
+        double den = 0.0;
+        for (int c = 0; c < d; c++) acc[c] = 0.0;
+        for (int64_t j = 0; j <= t; j++) {
+          double w = exp(y[j] - mu);
+          den += w;
+          const uint16_t* vr = J->v + ((size_t)(base + j) * D->Hkv + g) * d;
+          for (int c = 0; c < d; c++) acc[c] += w * bf2d(vr[c]);
+        }
+        size_t o = ((size_t)r * D->Hq + h) * d;
+        for (int c = 0; c < d; c++) {
+          double val = acc[c] / den;
+          if (J->o64) J->o64[o + c] = val;
+          if (J->o16) J->o16[o + c] = d2bf(val);
+        }
+      }
+    }
+  }
+  free(y); free(acc);
+  return NULL;
+}
+
+int hs2o_full_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                   int B, int Hq, int Hkv, int d, double scale, const int64_t* tokens,
+                   int64_t n_tokens, double* o64, uint16_t* o16, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0};
+  if (!q || !k || !v || !cu || check_dims(&D)) return -1;
+  int64_t T = cu[B];
+  if (!tokens) n_tokens = T;
+  for (int64_t r = 0; tokens && r < n_tokens; r++)
+    if (tokens[r] < 0 || tokens[r] >= T) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q; J.k = k; J.v = v; J.rows = tokens; J.n_rows = n_tokens;
+  J.o64 = o64; J.o16 = o16; J.max_len = max_len(&D);
+  return run(&J, full_worker, nthreads);
+}
+
 /* double -> bf16 RNE, exported for tests of the rounding itself. */
 uint16_t hs2o_bf16_round(double x) { return d2bf(x); }

@@ -414,3 +414,22 @@ def test_block_selection_bruteforce(bs, K, W):
         got = idx[r][idx[r] >= 0]
         assert list(got) == sorted(want), (r, t)
         assert (idx[r][len(got):] == -1).all()
+
+
+def test_full_attn_against_sdpa():
+    """The full layer's dense causal output equals torch SDPA (fp64, causal, GQA)
+    per sequence, on the whole batch and on a token subset."""
+    lengths, Hq, Hkv, d = [37, 1, 90], 8, 2, 128
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=31)
+    o64, o16 = oracle.full_attn(q, k, v, cu, Hq, Hkv)
+    G = Hq // Hkv
+    for i in range(len(lengths)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        Q = torch.from_numpy(bf(q[a:b])).permute(1, 0, 2)[None]
+        Kt = torch.from_numpy(bf(k[a:b])).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        Vt = torch.from_numpy(bf(v[a:b])).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, is_causal=True)
+        np.testing.assert_allclose(o64[a:b], ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    toks = np.array([0, 36, 37, 38, 127])
+    s64, s16 = oracle.full_attn(q, k, v, cu, Hq, Hkv, tokens=toks)
+    assert np.array_equal(s64, o64[toks]) and np.array_equal(s16, o16[toks])
