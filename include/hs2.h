@@ -161,6 +161,19 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
                       void* stream);
 
 /*
+ * hs2_select plus the full layer's own attention output (the full layer is a
+ * real layer of the module; its softmax is the one whose scores select):
+ *   out_full[t,h] = sum_{j <= t} softmax_j(softmax_scale <q[t,h], k[j,g]>) v[j,g]
+ * q, k, v [T,*,128] bf16; out_full [T,Hq,128] bf16 (HS2_OUT_BF16, P as one bf16
+ * part) or float (HS2_OUT_F32, P as three parts). The output sweep reuses the
+ * selection's per-row log-sum-exp, so it needs no running maximum (it divides by
+ * the sum of the P it accumulated). Workspace as for HS2_OP_SELECT.
+ */
+int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                    const void* v, int32_t* idx_out, float* kth_score_out, void* out_full,
+                    int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode step: one new token per sequence after the prompt (the cross-decoder
  * work HySparse2 moves to generation: HySparse2 news summary, early-exit
  * paragraph). `cache` describes the KV cache: sequence b holds L_b >= 1

@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_prefill_block.argtypes = [D, V, vp, vp, vp, i32, ctypes.POINTER(vp),
                                       ctypes.POINTER(vp), i32, vp, vp, sz, vp]
     lib.hs2_prefill_block.restype = i32
+    lib.hs2_select_full.argtypes = [D, V, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.hs2_select_full.restype = i32
     lib.hs2_decode_select.argtypes = [D, V, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_decode_select.restype = i32
     lib.hs2_decode_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp, sz, vp]
@@ -184,6 +186,17 @@ def hs2_prefill_block(dims: Dims, varlen: VarlenArgs, q_full, k, v, q_sparse: Se
                                             _ptr(q_full), _ptr(k), _ptr(v), n, qa, oa, out_dtype,
                                             _ptr(idx_out), _ptr(workspace), ws_bytes,
                                             _stream(stream)))
+
+
+def hs2_select_full(dims: Dims, varlen: VarlenArgs, q, k, v, idx_out, out_full,
+                    out_dtype: int = HS2_OUT_BF16, kth_score_out=None, workspace=None,
+                    stream=None) -> None:
+    """hs2_select plus the full layer's own attention output out_full [T,Hq,128]."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().hs2_select_full(ctypes.byref(dims), ctypes.byref(varlen.struct), _ptr(q),
+                                          _ptr(k), _ptr(v), _ptr(idx_out), _ptr(kth_score_out),
+                                          _ptr(out_full), out_dtype, _ptr(workspace), ws_bytes,
+                                          _stream(stream)))
 
 
 def hs2_decode_select(dims: Dims, cache: VarlenArgs, q, k, idx_out, kth_score_out=None,

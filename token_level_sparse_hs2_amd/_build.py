@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libhs2.so")
 
-SOURCES = ["select_scores.hip", "select_topk.hip", "sparse_attn.hip", "hs2_api.cpp"]
+SOURCES = ["select_scores.hip", "select_topk.hip", "sparse_attn.hip", "full_out.hip", "hs2_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

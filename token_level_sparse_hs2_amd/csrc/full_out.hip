@@ -1,0 +1,241 @@
+// full_out.hip - the full-attention layer's own output on gfx950.
+//
+// The full layer of a hybrid module is a real attention layer (HySparse2 news
+// summary, two-level KV sharing paragraph: the full-attention layers keep their
+// own projections and outputs; its scores also pick the sparse layers' tokens):
+//   o[t,h] = sum_{j <= t} P[t,h,j] v[j,g],  P = softmax_j(scale <q[t,h], k[j,g]>)
+// (attention as in the SHARP walkthrough, section 1.1). The selection's first
+// sweep already produced each row's log2-domain log-sum-exp lse2, so here
+// P = exp2(c q.k - lse2) is known outright: a single sweep over the causal keys
+// with no running maximum and no rescaling. The output is still divided by the
+// sum of the P values it accumulated (~1), which cancels the fp32 rounding of
+// lse2 itself.
+//
+// One workgroup owns TOK tokens of one sequence and one KV group: 4 wavefronts
+// x 32 MFMA rows (token-major, head-minor). Each 64-key tile of K and of V
+// streams into a 2-slot LDS ring with global_load_lds (16-byte chunks
+// XOR-swizzled by which chunk each lane fetches). Per wave and tile:
+//   S^T = K Q^T (keys x rows), v_mfma_f32_16x16x32_bf16, A = K from LDS, B = Q
+//   in registers;
+//   P^T = exp2(c S^T - lse2) in the accumulator layout, which is the B-operand
+//   layout of v_mfma_f32_16x16x16_bf16;
+//   O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16).
+// P enters as one bf16 part for bf16 output and three (~24 bits) for fp32.
+#include <type_traits>
+
+#include "hs2_device.h"
+#include "hs2_internal.h"
+
+namespace hs2 {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kOutRT = 2;                  // 16-row tiles per wave
+constexpr int kOutRowsW = 16 * kOutRT;     // MFMA rows per wave
+constexpr int kOutSlots = 2;               // ring depth (K and V each)
+
+__device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+struct OutSmem {
+  uint4 k[kOutSlots][kKeyTile][16];  // K rows: chunk c of key r at c ^ (r & 15)
+  uint4 v[kOutSlots][kKeyTile][16];  // V rows: chunk c of key r at c ^ (2 (r & 7))
+};
+
+}  // namespace
+
+template <int G, bool PRECISE>
+__global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
+  constexpr int TOK = full_out_tokens(G);
+  constexpr int NSPLIT = PRECISE ? 3 : 1;
+  __shared__ OutSmem sm;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int lq = l >> 4, lc = l & 15;
+  const int g = blockIdx.x % p.Hkv;
+  int seq, tile;
+  plan_decode(p.cu, p.B, TOK, p.max_tiles, blockIdx.x / p.Hkv, &seq, &tile);
+  const int base = p.cu[seq];
+  const int L = p.cu[seq + 1] - base;
+  const int t0 = tile * TOK;
+  const int ntok = min(TOK, L - t0);
+  const int Hq = p.Hq, Hkv = p.Hkv;
+  const float c = p.c;
+
+  // B operand Q^T: column = row (lc) of row tile rt, k = d chunk 4 ks + lq; and the
+  // row's lse2 (+inf for rows past the sequence: P = 0 there)
+  bf16x8 qb[kOutRT][4];
+  float lse[kOutRT];
+  {
+    u32x4 v[kOutRT][4];
+#pragma unroll
+    for (int rt = 0; rt < kOutRT; rt++) {
+      const int row = w * kOutRowsW + 16 * rt + lc;
+      const int ta = min(row / G, ntok - 1), ha = row % G;
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++)
+        v[rt][ks] = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
+                                    32 * ks + 8 * lq));
+      lse[rt] = p.lse2[(size_t)(base + t0 + ta) * Hq + g * G + ha];
+    }
+#pragma unroll
+    for (int rt = 0; rt < kOutRT; rt++) {
+      const bool live = (w * kOutRowsW + 16 * rt + lc) / G < ntok;
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) qb[rt][ks] = as_bf16x8(live ? v[rt][ks] : u32x4{0u, 0u, 0u, 0u});
+      if (!live) lse[rt] = INFINITY;
+    }
+  }
+
+  // ---- K / V tiles: global -> LDS ring, waits by vmcnt (loads complete in order) ----
+  const size_t row_elems = (size_t)Hkv * kHeadDim;
+  const uint16_t* kbase = p.k + (size_t)base * row_elems + (size_t)g * kHeadDim;
+  const uint16_t* vbase = p.v + (size_t)base * row_elems + (size_t)g * kHeadDim;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t lds_k = (uint32_t)(uintptr_t)&sm.k[0][0][0];
+  const uint32_t lds_v = (uint32_t)(uintptr_t)&sm.v[0][0][0];
+  const int kend = t0 + ntok;  // keys [0, kend) cover every row's causal range
+  auto dma_tile = [&](int kt, int buf) HS2_INLINE {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int key = 16 * w + 4 * r + lq;
+      const int j = min(kt * kKeyTile + key, kend - 1);
+      const uint16_t* ks = kbase + (size_t)j * row_elems + 8 * (lc ^ (key & 15));
+      const uint16_t* vs = vbase + (size_t)j * row_elems + 8 * (lc ^ (2 * (key & 7)));
+      const uint32_t off = (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(ks), "{m0}"(lds_k + off) : "memory");
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vs), "{m0}"(lds_v + off) : "memory");
+    }
+  };
+  auto lds_barrier = [&]() HS2_INLINE {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  f32x4 o[8][kOutRT];
+  float lsum[kOutRT] = {};
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+    for (int rt = 0; rt < kOutRT; rt++) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_kt = ceil_div(kend, kKeyTile);
+  dma_tile(0, 0);
+  for (int kt = 0; kt < n_kt; kt++) {
+    const int buf = kt & 1;
+    // tile kt landed (the 8 loads of tile kt + 1, issued below, may stay in flight)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only tile kt is outstanding here
+    lds_barrier();
+    if (kt + 1 < n_kt) dma_tile(kt + 1, buf ^ 1);
+    const bool diag = kt * kKeyTile + kKeyTile - 1 > t0;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {  // 16-key subtiles
+      // S^T for keys 16 kk + 4 lq + i, rows lc of each row tile
+      const int kr = 16 * kk + lc;     // A operand row (key) of this lane
+      bf16x8 ka[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) ka[ks] = as_bf16x8(to_u32x4(sm.k[buf][kr][(4 * ks + lq) ^ (kr & 15)]));
+      s16x4 pb[kOutRT][NSPLIT];
+#pragma unroll
+      for (int rt = 0; rt < kOutRT; rt++) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) s = mfma16x16x32(ka[ks], qb[rt][ks], s);
+        const int t = t0 + (w * kOutRowsW + 16 * rt + lc) / G;
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          pv[i] = fast_exp2(fmaf(s[i], c, -lse[rt]));
+          if (diag && kt * kKeyTile + 16 * kk + 4 * lq + i > t) pv[i] = 0.f;
+        }
+        lsum[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+        for (int part = 0; part < NSPLIT; part++) {
+          const uint32_t lo = pack_bf16x2(pv[0], pv[1]), hi = pack_bf16x2(pv[2], pv[3]);
+          pb[rt][part] = __builtin_bit_cast(s16x4, make_uint2(lo, hi));
+          if (part + 1 < NSPLIT) {
+            pv[0] -= bf16_bits_to_f32(lo & 0xFFFFu);
+            pv[1] -= __uint_as_float(lo & 0xFFFF0000u);
+            pv[2] -= bf16_bits_to_f32(hi & 0xFFFFu);
+            pv[3] -= __uint_as_float(hi & 0xFFFF0000u);
+          }
+        }
+      }
+      // O^T += V^T P^T: lane reads V[16 kk + 4 lq + e][16 dt + lc] (e = 0..3) via one
+      // transposing read; lane j of the group addresses key 16 kk + 4 lq + (j >> 2),
+      // d = 16 dt + 4 (j & 3)
+      const int key = 16 * kk + 4 * lq + (lc >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const int d0 = 16 * dt + 4 * (lc & 3);
+        const int phys = (d0 >> 3) ^ (2 * (key & 7));
+        const short* src = reinterpret_cast<const short*>(&sm.v[buf][key][phys]) + (d0 & 7);
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(src));
+#pragma unroll
+        for (int rt = 0; rt < kOutRT; rt++)
+#pragma unroll
+          for (int part = 0; part < NSPLIT; part++) o[dt][rt] = mfma16x16x16(va, pb[rt][part], o[dt][rt]);
+      }
+    }
+  }
+
+  // lane holds O^T[d = 16 dt + 4 lq + i][row lc of each row tile]; a row's keys
+  // are spread over the 4 lane groups
+#pragma unroll
+  for (int rt = 0; rt < kOutRT; rt++) {
+    float ls = lsum[rt];
+    ls += shfl_xor_f(ls, 16);
+    ls += shfl_xor_f(ls, 32);
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt][rt] *= inv;
+  }
+#pragma unroll
+  for (int rt = 0; rt < kOutRT; rt++) {
+    const int row = w * kOutRowsW + 16 * rt + lc;
+    if (row / G >= ntok) continue;
+    const size_t ob = ((size_t)(base + t0 + row / G) * Hq + g * G + row % G) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+      const int d0 = 16 * dt + 4 * lq;
+      if constexpr (PRECISE) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + ob + d0) =
+            make_float4(o[dt][rt][0], o[dt][rt][1], o[dt][rt][2], o[dt][rt][3]);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + ob + d0) =
+            make_uint2(pack_bf16x2(o[dt][rt][0], o[dt][rt][1]), pack_bf16x2(o[dt][rt][2], o[dt][rt][3]));
+      }
+    }
+  }
+}
+
+template <int G>
+static hipError_t launch_full_out_g(bool precise, const FullOutParams& p, int64_t blocks,
+                                    hipStream_t s) {
+  if (precise)
+    hipLaunchKernelGGL((full_out_kernel<G, true>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((full_out_kernel<G, false>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_full_out(int G, bool precise, const FullOutParams& p, int64_t n_tasks,
+                           hipStream_t s) {
+  const int64_t blocks = n_tasks * p.Hkv;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (G) {
+    case 1: return launch_full_out_g<1>(precise, p, blocks, s);
+    case 2: return launch_full_out_g<2>(precise, p, blocks, s);
+    case 4: return launch_full_out_g<4>(precise, p, blocks, s);
+    case 8: return launch_full_out_g<8>(precise, p, blocks, s);
+    case 16: return launch_full_out_g<16>(precise, p, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hs2

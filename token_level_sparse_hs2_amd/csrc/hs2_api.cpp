@@ -391,6 +391,41 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
   return HS2_OK;
 }
 
+int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                    const void* v, int32_t* idx_out, float* kth_score_out, void* out_full,
+                    int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (geo.T == 0) return HS2_OK;
+  if (!q || !k || !v || !idx_out || !out_full) return HS2_ERR_INVALID_ARG;
+  st = check_workspace(geo, workspace, workspace_bytes);
+  if (st != HS2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace, s);
+  if (st != HS2_OK) return st;
+  const int tok = hs2::full_out_tokens(geo.G);
+  int64_t n_tasks = 0;
+  for (int i = 0; i < varlen->batch; i++)
+    n_tasks += hs2::ceil_div(varlen->cu_seqlens_host[i + 1] - varlen->cu_seqlens_host[i], tok);
+  hs2::FullOutParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.cu = varlen->cu_seqlens;
+  p.B = varlen->batch;
+  p.Hq = dims->num_q_heads;
+  p.Hkv = dims->num_kv_heads;
+  p.max_tiles = std::max(1, hs2::ceil_div(geo.max_len, tok));
+  p.c = scale_log2(dims);
+  p.lse2 = reinterpret_cast<const float*>(static_cast<char*>(workspace) + geo.off_lse);
+  p.out = out_full;
+  hipError_t e = hs2::launch_full_out(geo.G, out_dtype == HS2_OUT_F32, p, n_tasks, s);
+  if (e != hipSuccess) return hip_fail(e, "full-layer output kernel");
+  return HS2_OK;
+}
+
 int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
                       int32_t* idx_out, float* kth_score_out, void* workspace,
                       size_t workspace_bytes, void* stream) {

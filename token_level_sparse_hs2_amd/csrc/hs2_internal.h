@@ -158,6 +158,21 @@ struct DecodeParams {
   float* kth;           // [B, Hkv] or null
 };
 
+// The full layer's output sweep: 4 waves x 32 MFMA rows per workgroup.
+__host__ __device__ constexpr int full_out_tokens(int G) { return 4 * 32 / G; }
+
+struct FullOutParams {
+  const uint16_t* q;    // [T, Hq, 128] the full layer's queries
+  const uint16_t* k;    // [T, Hkv, 128]
+  const uint16_t* v;
+  const int32_t* cu;
+  int B, Hq, Hkv;
+  int max_tiles;        // tiles of full_out_tokens(G) tokens in the longest sequence
+  float c;              // softmax_scale * log2(e)
+  const float* lse2;    // [T, Hq] from the selection's statistics sweep
+  void* out;            // [T, Hq, 128] bf16 or f32
+};
+
 // launchers (defined in the .hip files)
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv, int64_t T,
@@ -167,6 +182,8 @@ hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_bloc
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_sparse(int G, bool precise, const SparseParams& p, hipStream_t s);
 hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s);
+hipError_t launch_full_out(int G, bool precise, const FullOutParams& p, int64_t n_tasks,
+                           hipStream_t s);
 hipError_t launch_decode_select(int G, const DecodeParams& p, size_t lds_bytes, hipStream_t s);
 
 }  // namespace hs2
