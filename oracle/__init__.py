@@ -52,6 +52,9 @@ def _load():
     lib.hs2o_select_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, vp,
                                        i64, vp, vp, i32]
     lib.hs2o_select_blocks.restype = i32
+    lib.hs2o_select_oam.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, f64,
+                                    vp, i64, vp, vp, i32]
+    lib.hs2o_select_oam.restype = i32
     lib.hs2o_full_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64, vp, vp, i32]
     lib.hs2o_full_attn.restype = i32
     lib.hs2o_decode_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, vp, vp, i32]
@@ -79,13 +82,16 @@ def _cu(cu):
     return np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
 
 
-def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None, block=0):
+def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None, block=0,
+           v=None, oam_beta=0.0):
     """Index rows and K-th scores.
 
     q [T,Hq,d], k [T,Hkv,d] bf16 bits; rows: None (all T*Hkv rows, row id = t*Hkv+g)
     or an int64 array of row ids. block > 0 selects aligned blocks of that many
     candidate tokens (K a multiple of block) by the sum of S over the block; kth is
-    then the lowest selected block's score. Returns (idx [n, K+W] int32, kth [n] float64).
+    then the lowest selected block's score. oam_beta > 0 (needs v [T,Hkv,d]) ranks by the
+    output-aware metric S_j * max(1, |v_j|_2)^oam_beta. Returns (idx [n, K+W] int32,
+    kth [n] float64).
     """
     lib = _load()
     q, k, cu = _u16(q), _u16(k), _cu(cu_seqlens)
@@ -102,9 +108,17 @@ def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None
     kth = np.empty(n, dtype=np.float64)
     if n == 0:
         return idx, kth
-    r = lib.hs2o_select_blocks(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d, scale,
-                               K, W, int(block), rows.ctypes.data if rows is not None else None, n,
-                               idx.ctypes.data, kth.ctypes.data, nthreads or default_threads())
+    if oam_beta:
+        v = _u16(v)
+        r = lib.hs2o_select_oam(q.ctypes.data, k.ctypes.data, v.ctypes.data, cu.ctypes.data, B, Hq,
+                                Hkv, d, scale, K, W, int(block), float(oam_beta),
+                                rows.ctypes.data if rows is not None else None, n, idx.ctypes.data,
+                                kth.ctypes.data, nthreads or default_threads())
+    else:
+        r = lib.hs2o_select_blocks(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d,
+                                   scale, K, W, int(block),
+                                   rows.ctypes.data if rows is not None else None, n,
+                                   idx.ctypes.data, kth.ctypes.data, nthreads or default_threads())
     if r != 0:
         raise ValueError("hs2o_select: bad arguments")
     return idx, kth

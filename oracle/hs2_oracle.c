@@ -81,6 +81,7 @@ typedef struct {
   double scale;
   const int32_t* cu;
   int block; /* 0: single-token selection; > 0: blocks of this many tokens (K a multiple) */
+  double oam_beta; /* > 0: S_j is weighted by max(1, |v_j|_2)^beta (needs v) */
 } dims_t;
 
 static int find_seq(const dims_t* D, int64_t t_global) {
@@ -240,6 +241,18 @@ static void* select_worker(void* arg) {
         qt = J->q + (size_t)tg * D->Hq * D->d;
       }
       row_group_scores(D, qt, J->k, base, t, g, z, S, NULL, NULL);
+      if (D->oam_beta > 0.0) {
+        /* output-aware metric (Stem page, OAM paragraph): the logit term
+         * beta * max(0, log |v_j|_2) multiplies key j's probability, and so its
+         * group score, by max(1, |v_j|_2)^beta */
+        for (int64_t j = 0; j <= t; j++) {
+          const uint16_t* vr = J->v + ((size_t)(base + j) * D->Hkv + g) * D->d;
+          double n2 = 0.0;
+          for (int c = 0; c < D->d; c++) n2 += bf2d(vr[c]) * bf2d(vr[c]);
+          const double nv = sqrt(n2);
+          S[j] *= pow(nv > 1.0 ? nv : 1.0, D->oam_beta);
+        }
+      }
       double kth;
       row_select(D, S, t, J->idx_out + (size_t)r * KW, &kth, cb, mark);
       if (J->kth_out) J->kth_out[r] = kth;
@@ -353,7 +366,7 @@ static int max_len(const dims_t* D) {
 int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq, int Hkv,
                 int d, double scale, int K, int W, const int64_t* rows, int64_t n_rows,
                 int32_t* idx_out, double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0};
   if (!q || !k || !cu || !idx_out || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!rows) n_rows = T * Hkv;
@@ -372,7 +385,7 @@ int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, 
 int hs2o_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq,
                        int Hkv, int d, double scale, int K, int W, int block, const int64_t* rows,
                        int64_t n_rows, int32_t* idx_out, double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block, 0.0};
   if (!q || !k || !cu || !idx_out || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!rows) n_rows = T * Hkv;
@@ -385,11 +398,31 @@ int hs2o_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* cu, 
   return run(&J, select_worker, nthreads);
 }
 
+/* Selection with the output-aware metric: S'_j = S_j * max(1, |v_j|_2)^beta
+ * (beta >= 0; v [T, Hkv, d]); optional block selection as in hs2o_select_blocks.
+ * kth_out is the S' of the lowest-ranked selected candidate (or block). */
+int hs2o_select_oam(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                    int B, int Hq, int Hkv, int d, double scale, int K, int W, int block,
+                    double beta, const int64_t* rows, int64_t n_rows, int32_t* idx_out,
+                    double* kth_out, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block, beta};
+  if (!q || !k || !v || !cu || !idx_out || check_dims(&D) || !(beta >= 0.0)) return -1;
+  int64_t T = cu[B];
+  if (!rows) n_rows = T * Hkv;
+  for (int64_t r = 0; rows && r < n_rows; r++)
+    if (rows[r] < 0 || rows[r] >= T * Hkv) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q; J.k = k; J.v = v; J.rows = rows; J.n_rows = n_rows;
+  J.idx_out = idx_out; J.kth_out = kth_out; J.max_len = max_len(&D);
+  return run(&J, select_worker, nthreads);
+}
+
 /* The group score row S[t,g,0..t] (O1+O2) of one row, plus per-head m and l (nullable, [G]). */
 int hs2o_group_scores(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq,
                       int Hkv, int d, double scale, int64_t t_global, int g, double* S_out,
                       double* m_out, double* l_out) {
-  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0};
+  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0, 0.0};
   if (!q || !k || !cu || !S_out || check_dims(&D) || g < 0 || g >= Hkv) return -1;
   if (t_global < 0 || t_global >= cu[B]) return -1;
   int i = find_seq(&D, t_global);
@@ -411,7 +444,7 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      int B, int Hq, int Hkv, int d, double scale, int KW, const int32_t* idx,
                      const int64_t* tokens, int64_t n_tokens, double* o64, uint16_t* o16,
                      int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0};
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0};
   if (!q || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
   int64_t T = cu[B];
   if (!tokens) n_tokens = T;
@@ -433,7 +466,7 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* cu, int B, int Hq,
                        int Hkv, int d, double scale, int K, int W, int32_t* idx_out,
                        double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0};
   if (!q_dec || !k || !cu || !idx_out || check_dims(&D)) return -1;
   for (int b = 0; b < B; b++)
     if (cu[b + 1] - cu[b] < 1) return -1;
@@ -449,7 +482,7 @@ int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* 
 int hs2o_decode_sparse_attn(const uint16_t* q_dec, const uint16_t* k, const uint16_t* v,
                             const int32_t* cu, int B, int Hq, int Hkv, int d, double scale, int KW,
                             const int32_t* idx, double* o64, uint16_t* o16, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0};
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0};
   if (!q_dec || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
   for (int b = 0; b < B; b++)
     if (cu[b + 1] - cu[b] < 1) return -1;
@@ -516,7 +549,7 @@ static void* full_worker(void* arg) {
 int hs2o_full_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
                    int B, int Hq, int Hkv, int d, double scale, const int64_t* tokens,
                    int64_t n_tokens, double* o64, uint16_t* o16, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0};
+  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0, 0.0};
   if (!q || !k || !v || !cu || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!tokens) n_tokens = T;

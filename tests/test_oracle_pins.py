@@ -433,3 +433,46 @@ def test_full_attn_against_sdpa():
     toks = np.array([0, 36, 37, 38, 127])
     s64, s16 = oracle.full_attn(q, k, v, cu, Hq, Hkv, tokens=toks)
     assert np.array_equal(s64, o64[toks]) and np.array_equal(s16, o16[toks])
+
+
+@pytest.mark.parametrize("block", [0, 4])
+def test_oam_selection_against_numpy_ranking(block):
+    """Output-aware metric: the selection equals a numpy ranking of the pinned
+    group score S times max(1, |v_j|)^beta (token mode: K best by value desc,
+    position asc; block mode: blocks by summed weighted score). beta = 0 is the
+    plain selection. V rows are scaled so that norms straddle 1."""
+    lengths, Hq, Hkv, d, K, W, beta = [40, 90], 4, 2, 128, 8, 3, 0.7
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=41)
+    T = int(cu[-1])
+    scale_rows = np.exp(synthgen.normal_f64(41, 50, T * Hkv)).reshape(T, Hkv, 1) * 0.1
+    v = synthgen.float_to_bf16(bf(v) * scale_rows)
+    a0, k0 = oracle.select(q, k, cu, Hq, Hkv, K, W, block=block)
+    b0, kb0 = oracle.select(q, k, cu, Hq, Hkv, K, W, block=block, v=v, oam_beta=0.0)
+    assert (a0 == b0).all() and np.array_equal(k0, kb0)
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W, block=block, v=v, oam_beta=beta)
+    wv = np.maximum(1.0, np.linalg.norm(bf(v), axis=2)) ** beta  # [T, Hkv]
+    changed = 0
+    for r in range(T * Hkv):
+        tg, g = divmod(r, Hkv)
+        i = int(np.searchsorted(cu, tg, side="right") - 1)
+        t = tg - int(cu[i])
+        n_c = max(0, t - W + 1)
+        if n_c <= K:
+            continue
+        S, _, _ = oracle.group_scores(q, k, cu, Hq, Hkv, tg, g)
+        Sw = S[:n_c] * wv[int(cu[i]):int(cu[i]) + n_c, g]
+        if block:
+            nb = -(-n_c // block)
+            bs = np.array([Sw[b * block:(b + 1) * block].sum() for b in range(nb)])
+            order = sorted(range(nb), key=lambda b: (-bs[b], b))[:K // block]
+            glob = sorted(j for b in order for j in range(b * block, min((b + 1) * block, n_c)))
+            ref_kth = bs[order[-1]]
+        else:
+            order = sorted(range(n_c), key=lambda j: (-Sw[j], j))[:K]
+            glob = sorted(order)
+            ref_kth = Sw[order[-1]]
+        got = idx[r][(idx[r] >= 0) & (idx[r] < n_c)]
+        assert list(got) == glob, r
+        assert abs(kth[r] - ref_kth) <= 1e-12 * max(1.0, abs(ref_kth))
+        changed += not np.array_equal(idx[r], a0[r])
+    assert changed > 0  # the metric changes some selections
