@@ -160,6 +160,26 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
                       int out_dtype, int32_t* idx_out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Selection variants for hs2_select_ex. */
+typedef struct {
+  /* Output-aware metric (Stem page, OAM paragraph: add beta * max(0, log |v_j|_2)
+     to the selection logit): key j's group score is weighted,
+       S'[t,g,j] = S[t,g,j] * max(1, |v[j,g]|_2)^oam_beta,
+     and S' replaces S in the selection (tokens or blocks) and in kth_score.
+     Finite, >= 0; 0 = the plain score. */
+  float oam_beta;
+  float reserved[3]; /* must be 0 */
+} hs2_select_options;
+
+/*
+ * hs2_select with the options above (opts NULL = hs2_select). v [T,Hkv,128]
+ * bf16 is read when oam_beta > 0 (may be NULL otherwise). Workspace as for
+ * HS2_OP_SELECT.
+ */
+int hs2_select_ex(const hs2_dims* dims, const hs2_varlen* varlen, const hs2_select_options* opts,
+                  const void* q, const void* k, const void* v, int32_t* idx_out,
+                  float* kth_score_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * hs2_select plus the full layer's own attention output (the full layer is a
  * real layer of the module; its softmax is the one whose scores select):

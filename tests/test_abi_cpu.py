@@ -215,3 +215,29 @@ def test_block_flag_validation(lib):
     L = hs2.load_library()
     r = L.hs2_decode_select(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, None, 1, 1 << 40, None)
     assert r == hs2.HS2_ERR_UNSUPPORTED  # decode selects single tokens
+
+
+def test_select_ex_option_validation(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    v = varlen([5000])
+    L = hs2.load_library()
+
+    def call(opts, vv=FakeDev()):
+        return L.hs2_select_ex(ctypes.byref(d), ctypes.byref(v.struct),
+                               ctypes.byref(opts) if opts is not None else None, 1, 1,
+                               hs2._ptr(vv), 1, None, 1, 1 << 40, None)
+
+    assert call(hs2.SelectOptions(-0.5)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(hs2.SelectOptions(float("inf"))) == hs2.HS2_ERR_INVALID_ARG
+    assert call(hs2.SelectOptions(float("nan"))) == hs2.HS2_ERR_INVALID_ARG
+    o = hs2.SelectOptions(0.5)
+    o.reserved[1] = 1.0
+    assert call(o) == hs2.HS2_ERR_INVALID_ARG
+    assert call(hs2.SelectOptions(0.5), vv=None) == hs2.HS2_ERR_INVALID_ARG  # the metric needs V
+    small = FakeDev()
+    small.numel = lambda: 16
+    assert L.hs2_select_ex(ctypes.byref(d), ctypes.byref(v.struct), ctypes.byref(hs2.SelectOptions(0.5)),
+                           1, 1, 1, 1, None, hs2._ptr(small), 16, None) == hs2.HS2_ERR_WORKSPACE
+    e = hs2.VarlenArgs(FakeDev(0), [0])  # nothing to select: no pointer is needed
+    assert L.hs2_select_ex(ctypes.byref(d), ctypes.byref(e.struct), ctypes.byref(hs2.SelectOptions(0.5)),
+                           None, None, None, None, None, None, 0, None) == hs2.HS2_OK

@@ -53,6 +53,10 @@ class Dims(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 
+class SelectOptions(ctypes.Structure):
+    _fields_ = [("oam_beta", ctypes.c_float), ("reserved", ctypes.c_float * 3)]
+
+
 class Varlen(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
                 ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
@@ -82,6 +86,9 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_prefill_block.argtypes = [D, V, vp, vp, vp, i32, ctypes.POINTER(vp),
                                       ctypes.POINTER(vp), i32, vp, vp, sz, vp]
     lib.hs2_prefill_block.restype = i32
+    lib.hs2_select_ex.argtypes = [D, V, ctypes.POINTER(SelectOptions), vp, vp, vp, vp, vp, vp, sz,
+                                  vp]
+    lib.hs2_select_ex.restype = i32
     lib.hs2_select_full.argtypes = [D, V, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.hs2_select_full.restype = i32
     lib.hs2_decode_select.argtypes = [D, V, vp, vp, vp, vp, vp, sz, vp]
@@ -186,6 +193,18 @@ def hs2_prefill_block(dims: Dims, varlen: VarlenArgs, q_full, k, v, q_sparse: Se
                                             _ptr(q_full), _ptr(k), _ptr(v), n, qa, oa, out_dtype,
                                             _ptr(idx_out), _ptr(workspace), ws_bytes,
                                             _stream(stream)))
+
+
+def hs2_select_ex(dims: Dims, varlen: VarlenArgs, q, k, idx_out, kth_score_out=None, v=None,
+                  oam_beta: float = 0.0, workspace=None, stream=None) -> None:
+    """hs2_select with the output-aware metric: key j's group score weighted by
+    max(1, |v_j|_2)^oam_beta (v [T,Hkv,128] needed when oam_beta > 0)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    opts = SelectOptions(float(oam_beta))
+    _check(load_library().hs2_select_ex(ctypes.byref(dims), ctypes.byref(varlen.struct),
+                                        ctypes.byref(opts), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(idx_out), _ptr(kth_score_out), _ptr(workspace),
+                                        ws_bytes, _stream(stream)))
 
 
 def hs2_select_full(dims: Dims, varlen: VarlenArgs, q, k, v, idx_out, out_full,

@@ -35,7 +35,7 @@ struct Geometry {
   int bitmap_words = 0;
   // workspace offsets
   size_t off_lse = 0, off_cand = 0, off_count = 0, off_flags = 0, off_nflag = 0, off_dense = 0,
-         off_kmax = 0;
+         off_kmax = 0, off_vw = 0, off_vwmax = 0;
   size_t select_bytes = 0;
   size_t exact_lds = 0;
   int topk_rows_per_block = 4;
@@ -119,6 +119,10 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   off = align_up(off + (size_t)hs2::kFallbackBlocks * std::max(1, max_len) * sizeof(uint32_t));
   geo->off_kmax = off;
   off = align_up(off + (size_t)v->batch * d->num_kv_heads * sizeof(uint32_t));
+  geo->off_vw = off;  // output-aware metric: key weights and their maxima
+  off = align_up(off + (size_t)geo->T * d->num_kv_heads * sizeof(float));
+  geo->off_vwmax = off;
+  off = align_up(off + (size_t)v->batch * d->num_kv_heads * sizeof(uint32_t));
   geo->select_bytes = off;
   // exact path: histogram, scratch words, two bitmaps, G query rows in fp32
   geo->exact_lds =
@@ -189,7 +193,8 @@ int check_workspace(const Geometry& geo, void* ws, size_t bytes) {
 float scale_log2(const hs2_dims* d) { return d->softmax_scale * 1.4426950408889634f; }
 
 int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
-               const void* k, int32_t* idx_out, float* kth_out, void* ws, hipStream_t s) {
+               const void* k, int32_t* idx_out, float* kth_out, void* ws, hipStream_t s,
+               const void* vv = nullptr, float oam_beta = 0.f) {
   if (geo.T == 0) return HS2_OK;
   char* w = static_cast<char*>(ws);
   float* lse2 = reinterpret_cast<float*>(w + geo.off_lse);
@@ -254,6 +259,16 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
 
   hipError_t ek = hs2::launch_key_norms(sp.k, v->cu_seqlens, v->batch, d->num_kv_heads, geo.T, kmax, s);
   if (ek != hipSuccess) return hip_fail(ek, "key norm kernel");
+  if (oam_beta > 0.f) {
+    float* vw = reinterpret_cast<float*>(w + geo.off_vw);
+    uint32_t* vwmax = reinterpret_cast<uint32_t*>(w + geo.off_vwmax);
+    ek = hs2::launch_value_weights(static_cast<const uint16_t*>(vv), v->cu_seqlens, v->batch,
+                                   d->num_kv_heads, geo.T, oam_beta, vw, vwmax, s);
+    if (ek != hipSuccess) return hip_fail(ek, "value weight kernel");
+    sp.vw = vw;
+    sp.vwmax = vwmax;
+    tp.vw = vw;
+  }
   for (int64_t t0 = 0; t0 < geo.n_tasks; t0 += geo.tasks_per_chunk) {
     const int64_t nt = std::min(geo.tasks_per_chunk, geo.n_tasks - t0);
     const int64_t blocks = nt * d->num_kv_heads;
@@ -389,6 +404,27 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
     if (st != HS2_OK) return st;
   }
   return HS2_OK;
+}
+
+int hs2_select_ex(const hs2_dims* dims, const hs2_varlen* varlen, const hs2_select_options* opts,
+                  const void* q, const void* k, const void* v, int32_t* idx_out,
+                  float* kth_score_out, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  float beta = 0.f;
+  if (opts) {
+    beta = opts->oam_beta;
+    if (!(std::isfinite(beta) && beta >= 0.f)) return HS2_ERR_INVALID_ARG;
+    for (float r : opts->reserved)
+      if (r != 0.f) return HS2_ERR_INVALID_ARG;
+  }
+  if (geo.T == 0) return HS2_OK;
+  if (!q || !k || !idx_out || (beta > 0.f && !v)) return HS2_ERR_INVALID_ARG;
+  st = check_workspace(geo, workspace, workspace_bytes);
+  if (st != HS2_OK) return st;
+  return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace,
+                    static_cast<hipStream_t>(stream), v, beta);
 }
 
 int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,

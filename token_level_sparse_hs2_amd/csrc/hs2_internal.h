@@ -86,6 +86,8 @@ struct ScoreParams {
   int cand_cap;         // C
   uint32_t flags;
   int block;            // 0, or kBlockTokens: block selection (candidates are block scores)
+  const float* vw;      // [T, Hkv] log2 key weights beta * max(0, log2 |v|), or null (plain score)
+  const uint32_t* vwmax;  // [B * Hkv] largest weight of each (sequence, group), float bits
   float* lse2;          // [T, Hq] log2-domain log-sum-exp of each full-layer row
   uint64_t* cand;       // [chunk rows, C]: (S bits << 32) | position
   int32_t* cand_count;  // [chunk rows]: count, or -1 = exact path
@@ -114,6 +116,7 @@ struct TopkParams {
   const float* lse2;
   uint32_t* dense;      // [kFallbackBlocks, max_seqlen] S bits
   int max_seqlen;
+  const float* vw;      // [T, Hkv] log2 key weights, or null
   // outputs
   int32_t* idx;         // [T, Hkv, K+W]
   float* kth;           // [T, Hkv] or null
@@ -177,6 +180,8 @@ struct FullOutParams {
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv, int64_t T,
                             uint32_t* kmax, hipStream_t s);
+hipError_t launch_value_weights(const uint16_t* v, const int32_t* cu, int B, int Hkv, int64_t T,
+                                float beta, float* vw, uint32_t* vwmax, hipStream_t s);
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);

@@ -58,6 +58,8 @@ struct ScoreSmem {
     } s;
   } u;
   float nref[256];                   // minus the reference of each MFMA row
+  // output-aware metric: log2 key weights of each ring slot's tile, one copy per wave
+  float lw[kRing][kSelThreads / 64][kKeyTile];
   float tau[TOK];
   int32_t cnt[TOK];
   int32_t mode[TOK];
@@ -124,6 +126,62 @@ hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)((T + 255) / 256), (unsigned)Hkv), dim3(256), 0,
                      s, k, cu, B, Hkv, T, kmax);
+  return hipGetLastError();
+}
+
+// Key weights of the output-aware metric, max(1, |v[j,g]|_2)^beta: vw[j, g] holds
+// their log2, beta * max(0, log2 |v|), and vwmax the largest weight of each
+// (sequence, group) itself, as float bits (weights are >= 1; vwmax zeroed first).
+// Same geometry and single-sequence reduction as key_norm_kernel.
+__global__ __launch_bounds__(256) void value_weight_kernel(const uint16_t* v, const int32_t* cu,
+                                                           int B, int Hkv, int64_t T, float beta,
+                                                           float* vw, uint32_t* vwmax) {
+  __shared__ float wmax[4];
+  const int g = blockIdx.y, tid = threadIdx.x, lane16 = tid & 15, sub = tid >> 4;
+  const int64_t t_first = (int64_t)blockIdx.x * 256;
+  const int64_t t_last = min(T, t_first + 256) - 1;
+  const int s_first = find_seq(cu, B, t_first), s_last = find_seq(cu, B, t_last);
+  const bool one_seq = s_first == s_last;
+  float m = 1.f;
+  for (int it = 0; it < 16; it++) {
+    const int64_t tok = t_first + 16 * it + sub;
+    float n2 = 0.f;
+    if (tok <= t_last) {
+      const uint4 x = ldg128(v + ((size_t)tok * Hkv + g) * kHeadDim + 8 * lane16);
+      const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const float a = __uint_as_float(wv[u] << 16), b = __uint_as_float(wv[u] & 0xFFFF0000u);
+        n2 = fmaf(a, a, fmaf(b, b, n2));
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) n2 += shfl_xor_f(n2, off);
+    // n2 <= 1 gives weight 1
+    const float lw = n2 > 1.f ? beta * 0.5f * fast_log2(n2) : 0.f;
+    const float wgt = fast_exp2(lw);
+    if (lane16 == 0 && tok <= t_last) {
+      vw[(size_t)tok * Hkv + g] = lw;
+      if (!one_seq) atomicMax(&vwmax[find_seq(cu, B, tok) * Hkv + g], __float_as_uint(wgt));
+    }
+    if (tok <= t_last) m = fmaxf(m, wgt);
+  }
+  if (!one_seq) return;  // uniform over the workgroup
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0)
+    atomicMax(&vwmax[s_first * Hkv + g],
+              __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+}
+
+hipError_t launch_value_weights(const uint16_t* v, const int32_t* cu, int B, int Hkv, int64_t T,
+                                float beta, float* vw, uint32_t* vwmax, hipStream_t s) {
+  hipError_t e = launch_zero_i32(reinterpret_cast<int32_t*>(vwmax), B * Hkv, s);
+  if (e != hipSuccess || T <= 0) return e;
+  hipLaunchKernelGGL(value_weight_kernel, dim3((unsigned)((T + 255) / 256), (unsigned)Hkv), dim3(256),
+                     0, s, v, cu, B, Hkv, T, beta, vw, vwmax);
   return hipGetLastError();
 }
 
@@ -203,7 +261,10 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   const uint16_t* kbase = p.k + (size_t)g * kHeadDim;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t lds_ring = (uint32_t)(uintptr_t)&sm.u.ktile[0][0][0];
-  auto dma_tile = [&](int kt, int kend, int buf) HS2_INLINE {
+  const uint32_t lds_lw = (uint32_t)(uintptr_t)&sm.lw[0][0][0];
+  // With wts (the output-aware metric) a fifth load per wave brings the tile's 64
+  // log2 key weights into the wave's own copy, so the ring waits cover them too.
+  auto dma_tile = [&](int kt, int kend, int buf, bool wts) HS2_INLINE {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int key = 16 * w + 4 * r + lq;
@@ -213,6 +274,11 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
       const uint32_t dst = lds_ring + (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
       asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
     }
+    if (wts) {
+      const float* src = p.vw + (size_t)(base + min(kt * kKeyTile + l, kend - 1)) * Hkv + g;
+      const uint32_t dst = lds_lw + (uint32_t)(buf * (kSelThreads / 64) + wu) * (kKeyTile * 4u);
+      asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+    }
   };
   auto lds_barrier = [&]() HS2_INLINE {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -220,29 +286,36 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
   // Wait until the oldest outstanding tile has landed while `younger` later tiles
-  // (4 loads each) may still be in flight, then the barrier. Loads complete in
-  // issue order, so vmcnt <= 4 * younger suffices; global stores issued in
-  // between only make the wait stricter.
-  auto ring_ready = [&](int younger) HS2_INLINE {
+  // (4 loads each, 5 with weights; at most 2 of them) may still be in flight, then
+  // the barrier. Loads complete in issue order, so vmcnt <= loads * younger
+  // suffices; global stores issued in between only make the wait stricter.
+  auto ring_ready = [&](int younger, bool wts) HS2_INLINE {
     // s_waitcnt immediate: vmcnt in bits 3:0, expcnt 6:4 = 7 and lgkmcnt 11:8 = 15 (no wait)
-    if (younger >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);       // vmcnt(12)
-    else if (younger == 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+    if (younger >= 2) {
+      if (wts) __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+      else __builtin_amdgcn_s_waitcnt(0x0F78);      // vmcnt(8)
+    } else if (younger == 1) {
+      if (wts) __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);      // vmcnt(4)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
     lds_barrier();
   };
   // Streams tiles first, first + step, ... (n of them) of keys below kend through
   // NS ring slots, NS - 1 tiles ahead; body(kt, slot). Ends with every load landed
   // and every wave past its last LDS read.
-  auto sweep = [&](int n, int first, int step, int kend, auto NSc, auto&& body) HS2_INLINE {
+  auto sweep = [&](int n, int first, int step, int kend, auto NSc, bool wts,
+                   auto&& body) HS2_INLINE {
     constexpr int NS = decltype(NSc)::value;
+    static_assert(NS <= 4, "ring_ready waits for at most 2 younger tiles");
 #pragma unroll
     for (int i = 0; i < NS - 1; i++)
-      if (i < n) dma_tile(first + i * step, kend, i);
+      if (i < n) dma_tile(first + i * step, kend, i, wts);
     for (int i = 0; i < n; i++) {
-      ring_ready(min(NS - 2, n - 1 - i));
+      ring_ready(min(NS - 2, n - 1 - i), wts);
       // every wave is past tile i - 1, so its slot can take tile i + NS - 1
-      if (i + NS - 1 < n) dma_tile(first + (i + NS - 1) * step, kend, (i + NS - 1) % NS);
+      if (i + NS - 1 < n) dma_tile(first + (i + NS - 1) * step, kend, (i + NS - 1) % NS, wts);
       body(first + i * step, i % NS);
     }
     lds_barrier();
@@ -297,7 +370,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) lsum[rt][i] = 0.f;
-    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) HS2_INLINE {
+    sweep(n_kt1, 0, 1, kend1, Ring{}, false, [&](int kt, int buf) HS2_INLINE {
       compute(buf);
       mask_causal(kt);
 #pragma unroll
@@ -337,7 +410,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) mx[rt][i] = -INFINITY;
-    sweep(n_kt1, 0, 1, kend1, Ring{}, [&](int kt, int buf) HS2_INLINE {
+    sweep(n_kt1, 0, 1, kend1, Ring{}, false, [&](int kt, int buf) HS2_INLINE {
       compute(buf);
       mask_causal(kt);
 #pragma unroll
@@ -405,11 +478,28 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   __syncthreads();
   load_nref();
 
+  // Histogram range: 8 bins per octave below G/K (the largest a K-th score can
+  // be); with key weights, below G * max weight / K.
+  int bin_base = p.bin_base;
+  if (p.vw) {
+    const float top = (float)G * __uint_as_float(p.vwmax[seq * Hkv + g]) / (float)max(1, K);
+    bin_base = (int)(__float_as_uint(top) >> 20) - (kBins - 1);
+  }
+  // output-aware metric: the log2 weight of the lane's key (column lc of tile ct)
+  // enters every head's exponent, so S comes out multiplied by the key's weight
+  const bool wts = p.vw != nullptr;
+  float lw[4] = {0.f, 0.f, 0.f, 0.f};
+  auto read_weights = [&](int buf) HS2_INLINE {
+    if (!wts) return;
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++) lw[ct] = sm.lw[buf][w][16 * ct + lc];
+  };
+
   // group scores of accumulator tile (rt, ct): S[u] for the lane's tokens
   auto group_scores = [&](int rt, int ct, float (&S)[NT]) HS2_INLINE {
     float e[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) e[i] = fast_exp2(acc[rt][ct][i] * c);
+    for (int i = 0; i < 4; i++) e[i] = fast_exp2(fmaf(acc[rt][ct][i], c, lw[ct]));
     if constexpr (G == 1) {
 #pragma unroll
       for (int u = 0; u < 4; u++) S[u] = e[u];
@@ -434,8 +524,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 
   // ========================= sweep 2: sample ================================
   if (sm.any_sample) {
-    sweep(ceil_div(n_kt2, kSampleStride), 0, kSampleStride, cand_end, Pair{},
+    sweep(ceil_div(n_kt2, kSampleStride), 0, kSampleStride, cand_end, Pair{}, wts,
           [&](int kt, int buf) HS2_INLINE {
+      read_weights(buf);
       compute(buf);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
@@ -448,7 +539,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
           for (int u = 0; u < NT; u++) {
             const int tl = token_of(rt, u);
             if (owner && tl < TOK && sm.mode[tl] == kModeSample && j <= t0 + tl - W) {
-              int bin = (int)(__float_as_uint(S[u]) >> 20) - p.bin_base;
+              int bin = (int)(__float_as_uint(S[u]) >> 20) - bin_base;
               bin = min(max(bin, 0), kBins - 1);
               atomicAdd(&sm.u.s.hist[tl][bin >> 1], (bin & 1) ? 65536u : 1u);
             }
@@ -474,7 +565,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
             // the r-th sample lies (r - (cum - h)) / h deep into bin b from its top;
             // interpolate linearly in the bit pattern (bins are 1/8 octave)
             const float depth = (float)(r - (cum - h)) / (float)h;
-            const uint32_t lo_bits = (uint32_t)(b + p.bin_base) << 20;
+            const uint32_t lo_bits = (uint32_t)(b + bin_base) << 20;
             tau = __uint_as_float(lo_bits + (uint32_t)((1.f - depth) * (float)(1u << 20)));
             mode = kModeEmit;
             break;
@@ -495,7 +586,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   if (p.block && sm.any_emit) {
     uint64_t* cand = p.cand;
     const int C = p.cand_cap;
-    sweep(n_kt2, 0, 1, cand_end, Ring{}, [&](int kt, int buf) HS2_INLINE {
+    sweep(n_kt2, 0, 1, cand_end, Ring{}, wts, [&](int kt, int buf) HS2_INLINE {
+      read_weights(buf);
       compute(buf);
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
@@ -541,7 +633,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     uint64_t* cand = p.cand;
     const int C = p.cand_cap;
     const int nc_min = t0 - W + 1;  // every token's candidates include [0, nc_min)
-    sweep(n_kt2, 0, 1, cand_end, Ring{}, [&](int kt, int buf) HS2_INLINE {
+    sweep(n_kt2, 0, 1, cand_end, Ring{}, wts, [&](int kt, int buf) HS2_INLINE {
+      read_weights(buf);
       compute(buf);
       const bool tail = kt * kKeyTile + kKeyTile > nc_min;  // some key may be past a token's range
 #pragma unroll

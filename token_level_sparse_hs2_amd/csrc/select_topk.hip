@@ -476,9 +476,11 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
           }
         }
       }
+      // output-aware metric: the key's log2 weight joins every head's exponent
+      const float lwj = p.vw ? p.vw[(size_t)(r.base + j) * p.Hkv + r.g] : 0.f;
       float s = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < G; hh++) s += fast_exp2(dot[hh] * p.c - lse[hh]);
+      for (int hh = 0; hh < G; hh++) s += fast_exp2(fmaf(dot[hh], p.c, lwj - lse[hh]));
       dense[j] = __float_as_uint(s);
     }
     __syncthreads();
