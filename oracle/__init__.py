@@ -13,6 +13,7 @@ pages are silent.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -52,9 +53,9 @@ def _load():
     lib.hs2o_select_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, vp,
                                        i64, vp, vp, i32]
     lib.hs2o_select_blocks.restype = i32
-    lib.hs2o_select_oam.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, f64,
+    lib.hs2o_select_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, i32, f64, i32,
                                     vp, i64, vp, vp, i32]
-    lib.hs2o_select_oam.restype = i32
+    lib.hs2o_select_ex.restype = i32
     lib.hs2o_full_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64, vp, vp, i32]
     lib.hs2o_full_attn.restype = i32
     lib.hs2o_decode_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, i32, i32, vp, vp, i32]
@@ -82,16 +83,30 @@ def _cu(cu):
     return np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
 
 
+def decay_k_end(K, decay_mu):
+    """Budget at a sequence's last position for the position-decaying budget:
+    k_end = floor(mu * K + 0.5), mu taken as a 32-bit float (as callers pass it);
+    mu = 0 means no decay (k_end = K)."""
+    if not decay_mu:
+        return K
+    mu = float(np.float32(decay_mu))
+    if not 0.0 < mu <= 1.0:
+        raise ValueError("decay_mu must lie in (0, 1]")
+    return int(math.floor(mu * K + 0.5))
+
+
 def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None, block=0,
-           v=None, oam_beta=0.0):
+           v=None, oam_beta=0.0, decay_mu=0.0):
     """Index rows and K-th scores.
 
     q [T,Hq,d], k [T,Hkv,d] bf16 bits; rows: None (all T*Hkv rows, row id = t*Hkv+g)
     or an int64 array of row ids. block > 0 selects aligned blocks of that many
     candidate tokens (K a multiple of block) by the sum of S over the block; kth is
     then the lowest selected block's score. oam_beta > 0 (needs v [T,Hkv,d]) ranks by the
-    output-aware metric S_j * max(1, |v_j|_2)^oam_beta. Returns (idx [n, K+W] int32,
-    kth [n] float64).
+    output-aware metric S_j * max(1, |v_j|_2)^oam_beta. decay_mu in (0, 1] gives the
+    position-decaying budget: position t of a sequence of L tokens keeps
+    K - floor((K - k_end) t / (L - 1)) candidates, k_end = decay_k_end(K, decay_mu)
+    (token selection only). Returns (idx [n, K+W] int32, kth [n] float64).
     """
     lib = _load()
     q, k, cu = _u16(q), _u16(k), _cu(cu_seqlens)
@@ -108,12 +123,13 @@ def select(q, k, cu_seqlens, Hq, Hkv, K, W, scale=None, rows=None, nthreads=None
     kth = np.empty(n, dtype=np.float64)
     if n == 0:
         return idx, kth
-    if oam_beta:
-        v = _u16(v)
-        r = lib.hs2o_select_oam(q.ctypes.data, k.ctypes.data, v.ctypes.data, cu.ctypes.data, B, Hq,
-                                Hkv, d, scale, K, W, int(block), float(oam_beta),
-                                rows.ctypes.data if rows is not None else None, n, idx.ctypes.data,
-                                kth.ctypes.data, nthreads or default_threads())
+    if oam_beta or decay_mu:
+        v = _u16(v) if oam_beta else None
+        r = lib.hs2o_select_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data if v is not None else None,
+                               cu.ctypes.data, B, Hq, Hkv, d, scale, K, W, int(block),
+                               float(oam_beta), decay_k_end(K, decay_mu),
+                               rows.ctypes.data if rows is not None else None, n, idx.ctypes.data,
+                               kth.ctypes.data, nthreads or default_threads())
     else:
         r = lib.hs2o_select_blocks(q.ctypes.data, k.ctypes.data, cu.ctypes.data, B, Hq, Hkv, d,
                                    scale, K, W, int(block),

@@ -82,7 +82,17 @@ typedef struct {
   const int32_t* cu;
   int block; /* 0: single-token selection; > 0: blocks of this many tokens (K a multiple) */
   double oam_beta; /* > 0: S_j is weighted by max(1, |v_j|_2)^beta (needs v) */
+  int k_end;       /* budget at a sequence's last position (K: no decay) */
 } dims_t;
+
+/* Position-decaying budget (Stem page, Token Position-Decay paragraph): the
+ * top-k budget of query position t falls linearly from K at the first position
+ * of its sequence to k_end at the last one (L tokens). Reading: the decrement
+ * (K - k_end) * t / (L - 1) is rounded down, so K_t is exact in integers. */
+static int row_budget(const dims_t* D, int64_t t, int64_t L) {
+  if (L <= 1 || D->k_end == D->K) return D->K;
+  return D->K - (int)(((int64_t)(D->K - D->k_end) * t) / (L - 1));
+}
 
 static int find_seq(const dims_t* D, int64_t t_global) {
   int lo = 0, hi = D->B - 1;
@@ -140,9 +150,9 @@ static int cmp_cand(const void* a, const void* b) {
 }
 
 /* ---- O3..O6 for one row: window, candidates, top-K, ascending index row ---- */
-static void row_select(const dims_t* D, const double* S, int64_t t, int32_t* idx_row, double* kth,
-                       cand_t* cbuf, uint8_t* mark) {
-  const int K = D->K, W = D->W, KW = D->K + D->W;
+static void row_select(const dims_t* D, const double* S, int64_t t, int64_t L, int32_t* idx_row,
+                       double* kth, cand_t* cbuf, uint8_t* mark) {
+  const int K = row_budget(D, t, L), W = D->W, KW = D->K + D->W;
   const int64_t n_cand = t - W + 1 > 0 ? t - W + 1 : 0; /* C_t = [0, t-W] */
   memset(mark, 0, (size_t)(t + 1));
   for (int64_t j = (t - W + 1 > 0 ? t - W + 1 : 0); j <= t; j++) mark[j] = 1; /* W_t */
@@ -228,15 +238,17 @@ static void* select_worker(void* arg) {
       int64_t row = J->rows ? J->rows[r] : r; /* row = t_global * Hkv + g (decode: b * Hkv + g) */
       int64_t tg = row / D->Hkv;
       int g = (int)(row % D->Hkv);
-      int64_t base, t;
+      int64_t base, t, L;
       const uint16_t* qt;
       if (J->decode) {
         base = D->cu[tg];
-        t = D->cu[tg + 1] - base - 1;
+        L = D->cu[tg + 1] - base;
+        t = L - 1;
         qt = J->q + (size_t)tg * D->Hq * D->d;
       } else {
         int i = find_seq(D, tg);
         base = D->cu[i];
+        L = D->cu[i + 1] - base;
         t = tg - base;
         qt = J->q + (size_t)tg * D->Hq * D->d;
       }
@@ -254,7 +266,7 @@ static void* select_worker(void* arg) {
         }
       }
       double kth;
-      row_select(D, S, t, J->idx_out + (size_t)r * KW, &kth, cb, mark);
+      row_select(D, S, t, L, J->idx_out + (size_t)r * KW, &kth, cb, mark);
       if (J->kth_out) J->kth_out[r] = kth;
     }
   }
@@ -327,6 +339,7 @@ static int check_dims(const dims_t* D) {
   if (D->B < 1 || D->Hq < 1 || D->Hkv < 1 || D->Hq % D->Hkv || D->d < 1 || D->d > 1024) return -1;
   if (D->K < 0 || D->W < 0 || D->K + D->W < 1) return -1;
   if (D->block < 0 || (D->block > 0 && D->K % D->block)) return -1;
+  if (D->k_end < 0 || D->k_end > D->K || (D->block > 0 && D->k_end != D->K)) return -1;
   if (D->cu[0] != 0) return -1;
   for (int i = 0; i < D->B; i++)
     if (D->cu[i + 1] < D->cu[i]) return -1;
@@ -366,7 +379,7 @@ static int max_len(const dims_t* D) {
 int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq, int Hkv,
                 int d, double scale, int K, int W, const int64_t* rows, int64_t n_rows,
                 int32_t* idx_out, double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0, K};
   if (!q || !k || !cu || !idx_out || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!rows) n_rows = T * Hkv;
@@ -385,7 +398,7 @@ int hs2o_select(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, 
 int hs2o_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq,
                        int Hkv, int d, double scale, int K, int W, int block, const int64_t* rows,
                        int64_t n_rows, int32_t* idx_out, double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block, 0.0};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block, 0.0, K};
   if (!q || !k || !cu || !idx_out || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!rows) n_rows = T * Hkv;
@@ -398,15 +411,20 @@ int hs2o_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* cu, 
   return run(&J, select_worker, nthreads);
 }
 
-/* Selection with the output-aware metric: S'_j = S_j * max(1, |v_j|_2)^beta
- * (beta >= 0; v [T, Hkv, d]); optional block selection as in hs2o_select_blocks.
- * kth_out is the S' of the lowest-ranked selected candidate (or block). */
-int hs2o_select_oam(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
-                    int B, int Hq, int Hkv, int d, double scale, int K, int W, int block,
-                    double beta, const int64_t* rows, int64_t n_rows, int32_t* idx_out,
-                    double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block, beta};
-  if (!q || !k || !v || !cu || !idx_out || check_dims(&D) || !(beta >= 0.0)) return -1;
+/* Selection with the variants: the output-aware metric S'_j = S_j *
+ * max(1, |v_j|_2)^beta (beta >= 0; v [T, Hkv, d], may be NULL when beta = 0),
+ * the position-decaying budget from K down to k_end (0 <= k_end <= K; k_end = K
+ * is no decay; token selection only), and block selection as in
+ * hs2o_select_blocks. kth_out is the score (S' with beta > 0) of the
+ * lowest-ranked selected candidate (or block). Rows are K + W wide; a row with
+ * a smaller budget holds fewer entries and more -1 padding. */
+int hs2o_select_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                   int B, int Hq, int Hkv, int d, double scale, int K, int W, int block,
+                   double beta, int k_end, const int64_t* rows, int64_t n_rows, int32_t* idx_out,
+                   double* kth_out, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, block, beta, k_end};
+  if (!q || !k || !cu || !idx_out || check_dims(&D) || !(beta >= 0.0)) return -1;
+  if (beta > 0.0 && !v) return -1;
   int64_t T = cu[B];
   if (!rows) n_rows = T * Hkv;
   for (int64_t r = 0; rows && r < n_rows; r++)
@@ -422,7 +440,7 @@ int hs2o_select_oam(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
 int hs2o_group_scores(const uint16_t* q, const uint16_t* k, const int32_t* cu, int B, int Hq,
                       int Hkv, int d, double scale, int64_t t_global, int g, double* S_out,
                       double* m_out, double* l_out) {
-  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0, 0.0};
+  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0, 0.0, 1};
   if (!q || !k || !cu || !S_out || check_dims(&D) || g < 0 || g >= Hkv) return -1;
   if (t_global < 0 || t_global >= cu[B]) return -1;
   int i = find_seq(&D, t_global);
@@ -444,7 +462,7 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      int B, int Hq, int Hkv, int d, double scale, int KW, const int32_t* idx,
                      const int64_t* tokens, int64_t n_tokens, double* o64, uint16_t* o16,
                      int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0};
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0, KW};
   if (!q || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
   int64_t T = cu[B];
   if (!tokens) n_tokens = T;
@@ -466,7 +484,7 @@ int hs2o_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* cu, int B, int Hq,
                        int Hkv, int d, double scale, int K, int W, int32_t* idx_out,
                        double* kth_out, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0};
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0, K};
   if (!q_dec || !k || !cu || !idx_out || check_dims(&D)) return -1;
   for (int b = 0; b < B; b++)
     if (cu[b + 1] - cu[b] < 1) return -1;
@@ -482,7 +500,7 @@ int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* 
 int hs2o_decode_sparse_attn(const uint16_t* q_dec, const uint16_t* k, const uint16_t* v,
                             const int32_t* cu, int B, int Hq, int Hkv, int d, double scale, int KW,
                             const int32_t* idx, double* o64, uint16_t* o16, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0};
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0, KW};
   if (!q_dec || !k || !v || !cu || !idx || check_dims(&D) || KW < 1) return -1;
   for (int b = 0; b < B; b++)
     if (cu[b + 1] - cu[b] < 1) return -1;
@@ -549,7 +567,7 @@ static void* full_worker(void* arg) {
 int hs2o_full_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
                    int B, int Hq, int Hkv, int d, double scale, const int64_t* tokens,
                    int64_t n_tokens, double* o64, uint16_t* o16, int nthreads) {
-  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0, 0.0};
+  dims_t D = {B, Hq, Hkv, d, 1, 0, scale, cu, 0, 0.0, 1};
   if (!q || !k || !v || !cu || check_dims(&D)) return -1;
   int64_t T = cu[B];
   if (!tokens) n_tokens = T;

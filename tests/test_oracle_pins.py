@@ -476,3 +476,81 @@ def test_oam_selection_against_numpy_ranking(block):
         assert abs(kth[r] - ref_kth) <= 1e-12 * max(1.0, abs(ref_kth))
         changed += not np.array_equal(idx[r], a0[r])
     assert changed > 0  # the metric changes some selections
+
+
+def _row_positions(cu, Hkv):
+    """(t, L) of every row t_global * Hkv + g."""
+    T = int(cu[-1])
+    tg = np.arange(T * Hkv) // Hkv
+    seq = np.searchsorted(cu, tg, side="right") - 1
+    return tg - cu[seq], cu[seq + 1] - cu[seq]
+
+
+@pytest.mark.parametrize("mu,beta", [(0.25, 0.0), (0.5, 0.0), (0.6, 0.7)])
+def test_position_decay_rows_are_plain_rows_with_the_row_budget(mu, beta):
+    """Position-decaying budget: the budget K_t of each row, read off its index row
+    (entries below t - W + 1 are the chosen candidates, min(n_c, K_t) of them), starts
+    at K on the first position of a sequence, ends at k_end = floor(mu K + 0.5) on the
+    last, never grows, and stays within one token of the straight line between them;
+    and every row equals the row the already pinned plain selection (or the
+    output-aware one) gives with top_k = K_t, index for index and in kth."""
+    lengths, Hq, Hkv, d, K, W = [300, 1, 45, 700], 4, 2, 64, 64, 16
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=43)
+    T = int(cu[-1])
+    v = synthgen.float_to_bf16(bf(v) * np.exp(synthgen.normal_f64(43, 50, T * Hkv)).reshape(T, Hkv, 1) * 0.1)
+    k_end = oracle.decay_k_end(K, mu)
+    assert k_end == math.floor(mu * K + 0.5)
+    idx, kth = oracle.select(q, k, cu, Hq, Hkv, K, W, v=v, oam_beta=beta, decay_mu=mu)
+    t, L = _row_positions(cu, Hkv)
+    n_c = np.maximum(0, t - W + 1)
+    chosen = ((idx >= 0) & (idx < n_c[:, None])).sum(axis=1)
+    # rows with more candidates than budget reveal K_t exactly
+    lin = K - (K - k_end) * t / np.maximum(1, L - 1)
+    full = n_c > K
+    assert (chosen[full] <= np.ceil(lin[full] + 1e-9)).all() and (chosen[full] >= np.floor(lin[full])).all()
+    long = (L == 700) & full
+    for s in (0, 1):  # non-increasing along the sequence
+        c = chosen[long][s::Hkv]
+        assert (np.diff(c) <= 0).all()
+    last = (L == 700) & (t == 699)
+    assert (chosen[last] == k_end).all()
+    # every row equals the plain selection with its own budget
+    budgets = {}
+    for r in np.nonzero(full)[0]:
+        budgets.setdefault(int(chosen[r]), []).append(r)
+    assert len(budgets) > 10
+    for Kt, rows in sorted(budgets.items())[:: max(1, len(budgets) // 12)]:
+        rows = np.array(rows, dtype=np.int64)
+        ref, ref_kth = oracle.select(q, k, cu, Hq, Hkv, Kt, W, rows=rows, v=v, oam_beta=beta)
+        got = idx[rows]
+        assert (got[:, :Kt + W] == ref).all() and (got[:, Kt + W:] == -1).all()
+        assert np.array_equal(kth[rows], ref_kth)
+    # rows with no more candidates than the budget take them all, as in plain selection
+    plain, _ = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    few = n_c <= k_end
+    assert (idx[few] == plain[few]).all()
+
+
+def test_position_decay_mu_one_is_plain_and_budget_mean():
+    """mu = 1 leaves the budget at K everywhere (the plain selection); the pages keep
+    the total budget of a uniform K0 when the budget decays from k_start =
+    2 K0 / (1 + mu): the mean of K_t over a long sequence is then K0 to within a
+    token. Block selection with a decaying budget is rejected."""
+    lengths, Hq, Hkv, d, K, W = [200, 33], 2, 1, 64, 32, 8
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=44)
+    a, ka = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    b, kb = oracle.select(q, k, cu, Hq, Hkv, K, W, decay_mu=1.0)
+    assert (a == b).all() and np.array_equal(ka, kb)
+    # budget law, read from a sequence long enough for every row to be full
+    L, K0, mu = 4000, 64, 0.5
+    k_start = round(2 * K0 / (1 + mu))
+    qq, kk, vv, cc = rand_inputs([L], 1, 1, 16, seed=45)
+    idx, _ = oracle.select(qq, kk, cc, 1, 1, k_start, 0, decay_mu=mu)
+    t = np.arange(L)
+    chosen = ((idx >= 0)).sum(axis=1)
+    Kt = chosen[t >= k_start]
+    assert abs(Kt.mean() - K0) < 1.0 + 1e-9 and chosen[-1] == oracle.decay_k_end(k_start, mu)
+    with pytest.raises(ValueError):
+        oracle.select(q, k, cu, Hq, Hkv, K, W, block=32, decay_mu=0.5)
+    with pytest.raises(ValueError):
+        oracle.select(q, k, cu, Hq, Hkv, K, W, decay_mu=1.5)
