@@ -168,6 +168,9 @@ def main():
     oam_ms = timed(lambda: hs2.hs2_select_ex(case.dims, case.varlen, case.q_full, case.k, idx, None,
                                              v=case.v, oam_beta=0.5, workspace=case.workspace,
                                              stream=stream), args.kernel_reps)
+    decay_ms = timed(lambda: hs2.hs2_select_ex(case.dims, case.varlen, case.q_full, case.k, idx,
+                                               None, decay_mu=0.5, workspace=case.workspace,
+                                               stream=stream), args.kernel_reps)
     full_out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
     full_ms = timed(lambda: hs2.hs2_select_full(case.dims, case.varlen, case.q_full, case.k, case.v,
                                                 idx, full_out, hs2.HS2_OUT_BF16,
@@ -194,9 +197,11 @@ def main():
     select_roof = {"bound": "mfma", "achieved": round(sel_tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
                    "unit": "TFLOP/s", "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4),
                    "algorithmic_flops": f_sel, "avg_call_ms": round(sel_ms, 4),
-                   "oam_avg_call_ms": round(oam_ms, 4),
+                   "oam_avg_call_ms": round(oam_ms, 4), "decay_avg_call_ms": round(decay_ms, 4),
                    "note": "whole hs2_select call (scores, top-k, exact-path launches); "
-                           "oam_avg_call_ms: hs2_select_ex with the output-aware metric, beta 0.5"}
+                           "oam_avg_call_ms: hs2_select_ex with the output-aware metric, beta 0.5; "
+                           "decay_avg_call_ms: hs2_select_ex with the position-decaying budget, "
+                           "top_k 1024 down to 512"}
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

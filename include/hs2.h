@@ -168,7 +168,16 @@ typedef struct {
      and S' replaces S in the selection (tokens or blocks) and in kth_score.
      Finite, >= 0; 0 = the plain score. */
   float oam_beta;
-  float reserved[3]; /* must be 0 */
+  /* Position-decaying budget (Stem page, Token Position-Decay paragraph): query
+     position t of a sequence of L tokens keeps
+       K_t = top_k - floor((top_k - k_end) * t / (L - 1)),  k_end = floor(decay_mu * top_k + 0.5)
+     candidates, top_k at the first position down to k_end at the last. Rows stay
+     top_k + window wide; a smaller budget leaves more -1 padding. 0 = no decay,
+     else in (0, 1]. Token selection only (HS2_ERR_UNSUPPORTED with
+     HS2_FLAG_BLOCK_SELECT). To keep the total of a uniform budget K0, pass
+     top_k = 2 K0 / (1 + decay_mu). */
+  float decay_mu;
+  float reserved[2]; /* must be 0 */
 } hs2_select_options;
 
 /*

@@ -107,17 +107,25 @@ def local_t(cu: np.ndarray, tg: np.ndarray) -> np.ndarray:
     return tg - cu[i]
 
 
-def check_structure(idx: np.ndarray, cu: np.ndarray, K: int, W: int, chunk: int = 8192):
-    """Structural invariants of every index row, in token chunks. idx [T, Hkv, K+W]."""
+def check_structure(idx: np.ndarray, cu: np.ndarray, K: int, W: int, chunk: int = 8192,
+                    n_glob=None):
+    """Structural invariants of every index row, in token chunks. idx [T, Hkv, K+W].
+    n_glob [T, Hkv] (optional): the expected number of global entries of each row
+    (default min(K, t-W+1)), e.g. the oracle's under a position-decaying budget."""
     T, Hkv, KW = idx.shape
     for a in range(0, T, chunk):
-        _check_structure_rows(idx[a:a + chunk], local_t(cu, np.arange(a, min(T, a + chunk))), K, W)
+        e = min(T, a + chunk)
+        _check_structure_rows(idx[a:e], local_t(cu, np.arange(a, e)), K, W,
+                              None if n_glob is None else n_glob[a:e])
 
 
-def _check_structure_rows(idx, tloc, K, W):
+def _check_structure_rows(idx, tloc, K, W, n_glob=None):
     KW = idx.shape[2]
     t = tloc[:, None, None]
-    n_t = np.minimum(t + 1, KW)
+    tt = np.broadcast_to(tloc[:, None], idx.shape[:2])
+    if n_glob is None:
+        n_glob = np.minimum(K, np.maximum(0, tt - W + 1))
+    n_t = (n_glob + np.minimum(W, tt + 1))[:, :, None]
     pos = np.arange(KW)[None, None, :]
     valid = np.broadcast_to(pos < n_t, idx.shape)
     assert (idx[~valid] == -1).all(), "padding must be -1"
@@ -126,16 +134,15 @@ def _check_structure_rows(idx, tloc, K, W):
     d = np.diff(idx, axis=2)
     assert (d[valid[:, :, 1:]] > 0).all(), "ascending and unique"
     # window: the last min(W, t+1) valid entries are t-W+1 .. t
-    tt = np.broadcast_to(tloc[:, None], idx.shape[:2])
     nt = np.broadcast_to(n_t[:, :, 0], idx.shape[:2])
     for w_ in range(1, W + 1):
         need = tt - w_ + 1 >= 0
         col = np.clip(nt - w_, 0, KW - 1)
         vals = np.take_along_axis(idx, col[:, :, None], axis=2)[:, :, 0]
         assert (~need | (vals == tt - w_ + 1)).all(), f"window position t-{w_ - 1} missing"
-    # global part: exactly min(K, t-W+1) entries below the window
-    n_glob = (np.where(valid, idx, 1 << 30) < (t - W + 1)).sum(axis=2)
-    assert (n_glob == np.minimum(K, np.maximum(0, tt - W + 1))).all(), "global count"
+    # global part: exactly n_glob entries below the window
+    got = (np.where(valid, idx, 1 << 30) < (t - W + 1)).sum(axis=2)
+    assert (got == n_glob).all(), "global count"
 
 
 def sample_tokens(lengths, K, W, head=256, tail=32, stride=509):

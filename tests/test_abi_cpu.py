@@ -241,3 +241,21 @@ def test_select_ex_option_validation(lib):
     e = hs2.VarlenArgs(FakeDev(0), [0])  # nothing to select: no pointer is needed
     assert L.hs2_select_ex(ctypes.byref(d), ctypes.byref(e.struct), ctypes.byref(hs2.SelectOptions(0.5)),
                            None, None, None, None, None, None, 0, None) == hs2.HS2_OK
+
+
+def test_select_ex_decay_validation(lib):
+    L = hs2.load_library()
+    v = varlen([5000])
+
+    def call(d, opts):
+        return L.hs2_select_ex(ctypes.byref(d), ctypes.byref(v.struct), ctypes.byref(opts), 1, 1,
+                               None, 1, None, 1, 1 << 40, None)
+
+    d = hs2.make_dims(32, 8, 1024, 128)
+    for mu in (-0.1, 1.01, float("nan"), float("inf")):
+        assert call(d, hs2.SelectOptions(0.0, mu)) == hs2.HS2_ERR_INVALID_ARG
+    o = hs2.SelectOptions(0.0, 0.5)
+    o.reserved[0] = 2.0
+    assert call(d, o) == hs2.HS2_ERR_INVALID_ARG
+    db = hs2.make_dims(32, 8, 1024, 128, flags=hs2.HS2_FLAG_BLOCK_SELECT)
+    assert call(db, hs2.SelectOptions(0.0, 0.5)) == hs2.HS2_ERR_UNSUPPORTED

@@ -54,7 +54,8 @@ class Dims(ctypes.Structure):
 
 
 class SelectOptions(ctypes.Structure):
-    _fields_ = [("oam_beta", ctypes.c_float), ("reserved", ctypes.c_float * 3)]
+    _fields_ = [("oam_beta", ctypes.c_float), ("decay_mu", ctypes.c_float),
+                ("reserved", ctypes.c_float * 2)]
 
 
 class Varlen(ctypes.Structure):
@@ -196,11 +197,14 @@ def hs2_prefill_block(dims: Dims, varlen: VarlenArgs, q_full, k, v, q_sparse: Se
 
 
 def hs2_select_ex(dims: Dims, varlen: VarlenArgs, q, k, idx_out, kth_score_out=None, v=None,
-                  oam_beta: float = 0.0, workspace=None, stream=None) -> None:
-    """hs2_select with the output-aware metric: key j's group score weighted by
-    max(1, |v_j|_2)^oam_beta (v [T,Hkv,128] needed when oam_beta > 0)."""
+                  oam_beta: float = 0.0, decay_mu: float = 0.0, workspace=None,
+                  stream=None) -> None:
+    """hs2_select with the selection variants: the output-aware metric (key j's group
+    score weighted by max(1, |v_j|_2)^oam_beta; v [T,Hkv,128] needed when oam_beta > 0)
+    and the position-decaying budget (top_k at a sequence's first position down to
+    floor(decay_mu * top_k + 0.5) at its last; 0 = none)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    opts = SelectOptions(float(oam_beta))
+    opts = SelectOptions(float(oam_beta), float(decay_mu))
     _check(load_library().hs2_select_ex(ctypes.byref(dims), ctypes.byref(varlen.struct),
                                         ctypes.byref(opts), _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(idx_out), _ptr(kth_score_out), _ptr(workspace),

@@ -194,8 +194,9 @@ float scale_log2(const hs2_dims* d) { return d->softmax_scale * 1.44269504088896
 
 int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
                const void* k, int32_t* idx_out, float* kth_out, void* ws, hipStream_t s,
-               const void* vv = nullptr, float oam_beta = 0.f) {
+               const void* vv = nullptr, float oam_beta = 0.f, int k_end = -1) {
   if (geo.T == 0) return HS2_OK;
+  if (k_end < 0) k_end = d->top_k;  // no decay
   char* w = static_cast<char*>(ws);
   float* lse2 = reinterpret_cast<float*>(w + geo.off_lse);
   uint64_t* cand = reinterpret_cast<uint64_t*>(w + geo.off_cand);
@@ -206,7 +207,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   uint32_t* kmax = reinterpret_cast<uint32_t*>(w + geo.off_kmax);
 
   const int G = geo.G;
-  const float gk = (float)G / (float)std::max(1, d->top_k);
+  const float gk = (float)G / (float)std::max(1, k_end);
   uint32_t gk_bits;
   std::memcpy(&gk_bits, &gk, 4);
 
@@ -219,6 +220,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.Hkv = d->num_kv_heads;
   sp.K = d->top_k;
   sp.W = d->window;
+  sp.k_end = k_end;
   sp.max_tiles = geo.max_tiles;
   sp.c = scale_log2(d);
   sp.bin_base = (int)(gk_bits >> 20) - (hs2::kBins - 1);
@@ -239,6 +241,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.Hkv = d->num_kv_heads;
   tp.K = d->top_k;
   tp.W = d->window;
+  tp.k_end = k_end;
   tp.max_tiles = geo.max_tiles;
   tp.tok = geo.tok;
   tp.block = geo.block;
@@ -413,18 +416,25 @@ int hs2_select_ex(const hs2_dims* dims, const hs2_varlen* varlen, const hs2_sele
   int st = validate(dims, varlen, &geo);
   if (st != HS2_OK) return st;
   float beta = 0.f;
+  int k_end = dims->top_k;
   if (opts) {
     beta = opts->oam_beta;
     if (!(std::isfinite(beta) && beta >= 0.f)) return HS2_ERR_INVALID_ARG;
+    const float mu = opts->decay_mu;
+    if (!(mu == 0.f || (mu > 0.f && mu <= 1.f))) return HS2_ERR_INVALID_ARG;
     for (float r : opts->reserved)
       if (r != 0.f) return HS2_ERR_INVALID_ARG;
+    if (mu > 0.f) {
+      if (geo.block) return HS2_ERR_UNSUPPORTED;  // blocks are ranked with one budget
+      k_end = (int)std::floor((double)mu * dims->top_k + 0.5);
+    }
   }
   if (geo.T == 0) return HS2_OK;
   if (!q || !k || !idx_out || (beta > 0.f && !v)) return HS2_ERR_INVALID_ARG;
   st = check_workspace(geo, workspace, workspace_bytes);
   if (st != HS2_OK) return st;
   return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace,
-                    static_cast<hipStream_t>(stream), v, beta);
+                    static_cast<hipStream_t>(stream), v, beta, k_end);
 }
 
 int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,

@@ -33,6 +33,14 @@ __host__ __device__ constexpr int tokens_per_task(int G) { return 4 * 16 * score
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Position-decaying budget (Stem page, Token Position-Decay paragraph): query
+// position t of a sequence of L tokens keeps K - floor((K - k_end) t / (L - 1))
+// candidates, K at the first position down to k_end at the last (k_end == K: none).
+__host__ __device__ inline int row_budget(int K, int k_end, int t, int L) {
+  if (L <= 1 || k_end == K) return K;
+  return K - (int)(((int64_t)(K - k_end) * t) / (L - 1));
+}
+
 // ---------------------------------------------------------------------------
 // Varlen task order (host and device): tasks are (sequence, tile of `tok`
 // tokens). Tiles further into a sequence cost more (more causal keys), so the
@@ -78,10 +86,11 @@ struct ScoreParams {
   const uint16_t* k;    // [T, Hkv, 128] bf16
   const int32_t* cu;    // [B+1]
   int B, Hq, Hkv, K, W;
+  int k_end;            // budget at a sequence's last position (K: no decay)
   int max_tiles;        // tiles of the longest sequence
   int64_t task_begin;   // first task of this chunk
   float c;              // softmax_scale * log2(e)
-  int bin_base;         // (bits(G/K) >> 20) - (kBins - 1)
+  int bin_base;         // (bits(G/max(1, k_end)) >> 20) - (kBins - 1)
   const uint32_t* kmax; // [B * Hkv] largest key norm of each (sequence, group), float bits
   int cand_cap;         // C
   uint32_t flags;
@@ -99,6 +108,7 @@ struct TopkParams {
   int64_t n_rows;       // rows of this chunk
   const int32_t* cu;
   int B, Hq, Hkv, K, W;
+  int k_end;            // budget at a sequence's last position (K: no decay)
   int max_tiles;
   int64_t task_begin;
   int tok;              // tokens per task

@@ -457,8 +457,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   if (tid < TOK) {
     const int t = t0 + tid;
     const int n_c = t - W + 1;
+    const int Kt = row_budget(K, p.k_end, t, L);
     int mode = kModeTrivial;
-    if (tid < ntok && K > 0 && n_c > K) {
+    if (tid < ntok && Kt > 0 && n_c > Kt) {
       if (p.block) mode = kModeEmit;  // block scores: one entry per candidate block, no sample
       else if (p.flags & 1u) mode = kModeExact;
       else if (n_c <= p.cand_cap) mode = kModeEmit;
@@ -478,11 +479,11 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   __syncthreads();
   load_nref();
 
-  // Histogram range: 8 bins per octave below G/K (the largest a K-th score can
-  // be); with key weights, below G * max weight / K.
+  // Histogram range: 8 bins per octave below G/K_t (the largest a K_t-th score
+  // can be; K_t >= k_end); with key weights, below G * max weight / k_end.
   int bin_base = p.bin_base;
   if (p.vw) {
-    const float top = (float)G * __uint_as_float(p.vwmax[seq * Hkv + g]) / (float)max(1, K);
+    const float top = (float)G * __uint_as_float(p.vwmax[seq * Hkv + g]) / (float)max(1, p.k_end);
     bin_base = (int)(__float_as_uint(top) >> 20) - (kBins - 1);
   }
   // output-aware metric: the log2 weight of the lane's key (column lc of tile ct)
@@ -550,9 +551,10 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     // threshold: interpolated where the sample's top count reaches r
     if (tid < TOK && sm.mode[tid] == kModeSample) {
       const int t = t0 + tid, n_c = t - W + 1;
+      const int Kt = row_budget(K, p.k_end, t, L);
       int n_s = 0;
       for (int kt = 0; kt < n_kt2; kt += kSampleStride) n_s += min(max(n_c - kt * kKeyTile, 0), kKeyTile);
-      const int r = (int)ceilf(kTauAlpha * (float)K * (float)n_s / (float)n_c) + kTauBeta;
+      const int r = (int)ceilf(kTauAlpha * (float)Kt * (float)n_s / (float)n_c) + kTauBeta;
       int mode = kModeExact;
       float tau = 0.f;
       if (r <= n_s) {
@@ -685,7 +687,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     } else if (mode == kModeEmit) {
       count = sm.cnt[tid];
       // block mode: ceil(n_c / 64) > K / 64 block entries, always within C
-      if (!p.block && (count > p.cand_cap || count < K)) count = -1;
+      if (!p.block && (count > p.cand_cap || count < row_budget(K, p.k_end, t0 + tid, L)))
+        count = -1;
     }
     p.cand_count[slot0 + tid] = count;
     if (count < 0) {

@@ -198,7 +198,7 @@ __device__ void mark_selected(KeyFn key, PosFn pos, int n, uint32_t kth, int kre
 }
 
 // Writes the index row: the selected positions (ascending, from sh.sel), then
-// the window [n_c, t]; n_sel + window == K + W here, so no padding.
+// the window [n_c, t], then -1 up to K + W (a decaying budget leaves room).
 __device__ void write_selected_row(int nwords, int n_c, int t, int KW, int32_t* row,
                                    const TopkShared& sh) {
   const int tid = threadIdx.x;
@@ -286,10 +286,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   if (r.t >= r.L) return;
   const int KW = p.K + p.W;
   const int n_c = r.t - p.W + 1;
+  const int Kt = row_budget(p.K, p.k_end, r.t, r.L);  // this row's budget
   int32_t* row = p.idx + ((size_t)(r.base + r.t) * p.Hkv + r.g) * KW;
   float* kth_out = p.kth ? p.kth + (size_t)(r.base + r.t) * p.Hkv + r.g : nullptr;
-  if (p.K == 0 || n_c <= p.K) {  // nothing to rank: [0, t] or the window only
-    const int start = (n_c <= p.K) ? 0 : n_c;
+  if (Kt == 0 || n_c <= Kt) {  // nothing to rank: [0, t] or the window only
+    const int start = (n_c <= Kt) ? 0 : n_c;
     const int n = r.t - start + 1;
     for (int o = l; o < KW; o += 64) row[o] = (o < n) ? start + o : -1;
     if (kth_out && l == 0) *kth_out = -1.f;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   mx = wave_max_u32(mx);
   // radix select of the K-th largest key below the common prefix, 8 bits per pass
   // (block mode: the (K / 64)-th largest block score)
-  const int k_sel = p.block ? p.K / p.block : p.K;
+  const int k_sel = p.block ? p.K / p.block : Kt;
   uint32_t prefix = mx, mask = 0xFFFFFFFFu;
   int kr = k_sel;
   if (mn != mx) {
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   int cnt = 0;
   for (int i = wb; i < we; i++) cnt += __popc(bm[i]);
   const int incl = wave_incl_scan(cnt, l);
-  const int base = __shfl(incl, 63, 64);  // number of selected positions (K)
+  const int base = __shfl(incl, 63, 64);  // number of selected positions (K_t)
   int off = incl - cnt;
   for (int i = wb; i < we; i++) {
     uint32_t mm = bm[i];
@@ -485,7 +486,8 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
     }
     __syncthreads();
     int krem;
-    const uint32_t kth = radix_kth([&](int i) { return dense[i]; }, n_c, p.K, sh, &krem);
+    const uint32_t kth = radix_kth([&](int i) { return dense[i]; }, n_c,
+                                   row_budget(p.K, p.k_end, r.t, r.L), sh, &krem);
     const int nwords = ceil_div(n_c, 32);
     mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth,
                   krem, nwords, sh);
