@@ -65,6 +65,18 @@ def _load():
     lib.hs2o_decode_sparse_attn.restype = i32
     lib.hs2o_bf16_round.argtypes = [f64]
     lib.hs2o_bf16_round.restype = ctypes.c_uint16
+    lib.hs2o_fp8_value.argtypes = [ctypes.c_uint8]
+    lib.hs2o_fp8_value.restype = f64
+    lib.hs2o_fp8_encode.argtypes = [ctypes.c_float]
+    lib.hs2o_fp8_encode.restype = ctypes.c_uint8
+    lib.hs2o_quantize_fp8.argtypes = [vp, vp, i64, ctypes.c_float]
+    lib.hs2o_quantize_fp8.restype = i32
+    lib.hs2o_sparse_attn_fp8.argtypes = [vp, vp, vp, f64, f64, vp, i32, i32, i32, i32, f64, i32, vp,
+                                         vp, i64, vp, vp, i32]
+    lib.hs2o_sparse_attn_fp8.restype = i32
+    lib.hs2o_decode_sparse_attn_fp8.argtypes = [vp, vp, vp, f64, f64, vp, i32, i32, i32, i32, f64,
+                                                i32, vp, vp, vp, i32]
+    lib.hs2o_decode_sparse_attn_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -279,3 +291,88 @@ def decode_sparse_attn(q_dec, k, v, cu_seqlens, Hq, Hkv, idx, scale=None, nthrea
 
 def bf16_round(x: float) -> int:
     return int(_load().hs2o_bf16_round(float(x)))
+
+
+# ---- FP8 KV cache (E4M3 codes, one fp32 scale per tensor) ----
+
+def fp8_value(code: int) -> float:
+    """Value of an E4M3 code (nan for the NaN codes)."""
+    return float(_load().hs2o_fp8_value(int(code) & 0xFF))
+
+
+def fp8_encode(x: float) -> int:
+    """Nearest E4M3 code of a float32 value (ties to even, saturating at +-448)."""
+    return int(_load().hs2o_fp8_encode(float(x)))
+
+
+def quantize_fp8(x, inv_scale: float):
+    """E4M3 codes of bf16 bits x: code = E4M3(float32(x) * float32(inv_scale))."""
+    x = _u16(x)
+    out = np.empty(x.shape, dtype=np.uint8)
+    if _load().hs2o_quantize_fp8(x.ctypes.data, out.ctypes.data, x.size, float(inv_scale)):
+        raise ValueError("hs2o_quantize_fp8: bad arguments")
+    return out
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint8, "FP8 tensors are passed as uint8 codes"
+    return a
+
+
+def sparse_attn_fp8(q, k8, v8, k_scale, v_scale, cu_seqlens, Hq, Hkv, idx, scale=None,
+                    tokens=None, nthreads=None, want_f64=True, want_bf16=True):
+    """sparse_attn over an FP8 cache: k = k_scale * E4M3(k8), v = v_scale * E4M3(v8)."""
+    lib = _load()
+    q, k8, v8, cu = _u16(q), _u8(k8), _u8(v8), _cu(cu_seqlens)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    d = q.shape[-1]
+    B = len(cu) - 1
+    T = int(cu[-1])
+    KW = idx.shape[-1]
+    assert idx.size == T * Hkv * KW
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    if tokens is not None:
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        n = len(tokens)
+    else:
+        n = T
+    o64 = np.empty((n, Hq, d), dtype=np.float64) if want_f64 else None
+    o16 = np.empty((n, Hq, d), dtype=np.uint16) if want_bf16 else None
+    if n == 0:
+        return o64, o16
+    r = lib.hs2o_sparse_attn_fp8(q.ctypes.data, k8.ctypes.data, v8.ctypes.data, float(k_scale),
+                                 float(v_scale), cu.ctypes.data, B, Hq, Hkv, d, scale, KW,
+                                 idx.ctypes.data, tokens.ctypes.data if tokens is not None else None,
+                                 n, o64.ctypes.data if o64 is not None else None,
+                                 o16.ctypes.data if o16 is not None else None,
+                                 nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_sparse_attn_fp8: bad arguments")
+    return o64, o16
+
+
+def decode_sparse_attn_fp8(q_dec, k8, v8, k_scale, v_scale, cu_seqlens, Hq, Hkv, idx, scale=None,
+                           nthreads=None, want_f64=True, want_bf16=True):
+    """decode_sparse_attn over an FP8 cache."""
+    lib = _load()
+    q_dec, k8, v8, cu = _u16(q_dec), _u8(k8), _u8(v8), _cu(cu_seqlens)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    d = q_dec.shape[-1]
+    B = len(cu) - 1
+    KW = idx.shape[-1]
+    assert idx.size == B * Hkv * KW and q_dec.size == B * Hq * d
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    o64 = np.empty((B, Hq, d), dtype=np.float64) if want_f64 else None
+    o16 = np.empty((B, Hq, d), dtype=np.uint16) if want_bf16 else None
+    if B == 0:
+        return o64, o16
+    r = lib.hs2o_decode_sparse_attn_fp8(q_dec.ctypes.data, k8.ctypes.data, v8.ctypes.data,
+                                        float(k_scale), float(v_scale), cu.ctypes.data, B, Hq, Hkv,
+                                        d, scale, KW, idx.ctypes.data,
+                                        o64.ctypes.data if o64 is not None else None,
+                                        o16.ctypes.data if o16 is not None else None,
+                                        nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_decode_sparse_attn_fp8: bad arguments")
+    return o64, o16

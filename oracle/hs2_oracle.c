@@ -76,6 +76,42 @@ static uint16_t d2bf(double x) {
   return (uint16_t)(sign | ((uint32_t)be << 7) | (m - 128));
 }
 
+/* ---- FP8 KV cache ----
+ * The pages store the KV cache in FP8 (HySparse2 news summary, cost paragraph:
+ * the cache size at 1M tokens with an FP8 cache) without naming the encoding;
+ * reading: OCP 8-bit floating point E4M3 ("e4m3fn"): sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 holds subnormals m * 2^-9; S.1111.111
+ * is NaN; there are no infinities, the largest finite value is 448. One fp32
+ * scale per tensor: value = scale * e4m3(code). */
+static double e4m3_to_d(uint8_t b) {
+  const int e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) v = NAN;
+  else if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return (b & 0x80) ? -v : v;
+}
+
+/* float -> E4M3, rounded to nearest (ties to an even code), saturating at
+ * +-448; NaN -> 0x7F. */
+static uint8_t f_to_e4m3(float x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs((double)x);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  int e2;
+  frexp(a, &e2); /* a in [2^(e2-1), 2^e2) */
+  int ue = e2 - 1;
+  if (ue < -6) ue = -6; /* subnormals share the spacing of the lowest binade */
+  const double s = ldexp(a, 3 - ue); /* a in units of the spacing 2^(ue-3) */
+  const double fl = floor(s), rem = s - fl;
+  uint32_t n = (uint32_t)fl;
+  if (rem > 0.5 || (rem == 0.5 && (n & 1u))) n++;
+  if (n < 8) return (uint8_t)(sign | n); /* subnormal (or zero): ue == -6 */
+  if (n == 16) { n = 8; ue++; }
+  return (uint8_t)(sign | ((uint32_t)(ue + 7) << 3) | (n - 8));
+}
+
 typedef struct {
   int B, Hq, Hkv, d, K, W;
   double scale;
@@ -211,7 +247,23 @@ typedef struct {
   /* decode: one query per sequence (q, idx and outputs indexed by sequence),
      at the sequence's last position */
   int decode;
+  /* FP8 KV cache (sparse attention): codes and per-tensor scales, used instead
+     of k / v when k8 is set */
+  const uint8_t *k8, *v8;
+  double k_scale, v_scale;
 } job_t;
+
+/* One K (is_v = 0) or V row of d values starting at element `off`, in double. */
+static void kv_row(const job_t* J, int is_v, size_t off, int d, double* out) {
+  if (J->k8) {
+    const uint8_t* p = (is_v ? J->v8 : J->k8) + off;
+    const double sc = is_v ? J->v_scale : J->k_scale;
+    for (int c = 0; c < d; c++) out[c] = sc * e4m3_to_d(p[c]);
+  } else {
+    const uint16_t* p = (is_v ? J->v : J->k) + off;
+    for (int c = 0; c < d; c++) out[c] = bf2d(p[c]);
+  }
+}
 
 static int64_t take(job_t* J, int64_t chunk, int64_t* end) {
   pthread_mutex_lock(&J->mu);
@@ -281,7 +333,7 @@ static void* sparse_worker(void* arg) {
   const int G = D->Hq / D->Hkv, KW = D->K + D->W, d = D->d;
   double* y = (double*)malloc(sizeof(double) * (size_t)KW);
   double* acc = (double*)malloc(sizeof(double) * (size_t)d);
-  double qd[1024];
+  double qd[1024], rd[1024];
   for (;;) {
     int64_t e, s = take(J, 16, &e);
     if (s >= J->n_rows) break;
@@ -305,9 +357,9 @@ static void* sparse_worker(void* arg) {
         for (int a = 0; a < KW; a++) {
           int32_t j = ir[a];
           if (j < 0 || j > t) { y[a] = -INFINITY; continue; } /* not in I_t */
-          const uint16_t* kr = J->k + ((size_t)(base + j) * D->Hkv + g) * d;
+          kv_row(J, 0, ((size_t)(base + j) * D->Hkv + g) * d, d, rd);
           double dot = 0.0;
-          for (int c = 0; c < d; c++) dot += qd[c] * bf2d(kr[c]);
+          for (int c = 0; c < d; c++) dot += qd[c] * rd[c];
           y[a] = D->scale * dot;
           if (y[a] > mu) mu = y[a];
         }
@@ -318,8 +370,8 @@ static void* sparse_worker(void* arg) {
             if (y[a] == -INFINITY) continue;
             double w = exp(y[a] - mu);
             den += w;
-            const uint16_t* vr = J->v + ((size_t)(base + ir[a]) * D->Hkv + g) * d;
-            for (int c = 0; c < d; c++) acc[c] += w * bf2d(vr[c]);
+            kv_row(J, 1, ((size_t)(base + ir[a]) * D->Hkv + g) * d, d, rd);
+            for (int c = 0; c < d; c++) acc[c] += w * rd[c];
           }
         }
         size_t o = ((size_t)r * D->Hq + h) * d;
@@ -582,3 +634,53 @@ int hs2o_full_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, cons
 
 /* double -> bf16 RNE, exported for tests of the rounding itself. */
 uint16_t hs2o_bf16_round(double x) { return d2bf(x); }
+
+/* E4M3 code <-> value, exported for tests of the encoding itself. */
+double hs2o_fp8_value(uint8_t code) { return e4m3_to_d(code); }
+uint8_t hs2o_fp8_encode(float x) { return f_to_e4m3(x); }
+
+/* Writing the FP8 cache: dst[i] = E4M3(float(src[i]) * inv_scale), the product
+ * rounded to float first, then to the nearest code (saturating at +-448). */
+int hs2o_quantize_fp8(const uint16_t* src, uint8_t* dst, int64_t n, float inv_scale) {
+  if (n < 0 || (n > 0 && (!src || !dst))) return -1;
+  for (int64_t i = 0; i < n; i++) {
+    const float v = (float)bf2d(src[i]) * inv_scale;
+    dst[i] = f_to_e4m3(v);
+  }
+  return 0;
+}
+
+/* Sparse attention (O7) over an FP8 KV cache: as hs2o_sparse_attn with
+ * k = k_scale * E4M3(k8), v = v_scale * E4M3(v8). */
+int hs2o_sparse_attn_fp8(const uint16_t* q, const uint8_t* k8, const uint8_t* v8, double k_scale,
+                         double v_scale, const int32_t* cu, int B, int Hq, int Hkv, int d,
+                         double scale, int KW, const int32_t* idx, const int64_t* tokens,
+                         int64_t n_tokens, double* o64, uint16_t* o16, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0, KW};
+  if (!q || !k8 || !v8 || !cu || !idx || check_dims(&D) || KW < 1) return -1;
+  int64_t T = cu[B];
+  if (!tokens) n_tokens = T;
+  for (int64_t r = 0; tokens && r < n_tokens; r++)
+    if (tokens[r] < 0 || tokens[r] >= T) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q; J.k8 = k8; J.v8 = v8; J.k_scale = k_scale; J.v_scale = v_scale;
+  J.rows = tokens; J.n_rows = n_tokens; J.idx_in = idx; J.o64 = o64; J.o16 = o16;
+  return run(&J, sparse_worker, nthreads);
+}
+
+/* Decode-step sparse attention over an FP8 KV cache (as hs2o_decode_sparse_attn). */
+int hs2o_decode_sparse_attn_fp8(const uint16_t* q_dec, const uint8_t* k8, const uint8_t* v8,
+                                double k_scale, double v_scale, const int32_t* cu, int B, int Hq,
+                                int Hkv, int d, double scale, int KW, const int32_t* idx,
+                                double* o64, uint16_t* o16, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, KW, 0, scale, cu, 0, 0.0, KW};
+  if (!q_dec || !k8 || !v8 || !cu || !idx || check_dims(&D) || KW < 1) return -1;
+  for (int b = 0; b < B; b++)
+    if (cu[b + 1] - cu[b] < 1) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q_dec; J.k8 = k8; J.v8 = v8; J.k_scale = k_scale; J.v_scale = v_scale;
+  J.n_rows = B; J.decode = 1; J.idx_in = idx; J.o64 = o64; J.o16 = o16;
+  return run(&J, sparse_worker, nthreads);
+}

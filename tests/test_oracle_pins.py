@@ -554,3 +554,119 @@ def test_position_decay_mu_one_is_plain_and_budget_mean():
         oracle.select(q, k, cu, Hq, Hkv, K, W, block=32, decay_mu=0.5)
     with pytest.raises(ValueError):
         oracle.select(q, k, cu, Hq, Hkv, K, W, decay_mu=1.5)
+
+
+# ---- FP8 KV cache: E4M3 codes against torch's float8_e4m3fn (a library routine) ----
+
+def _torch_e4m3_codes(x32):
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_code_values_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([oracle.fp8_value(c) for c in codes])
+    assert ((ref == mine) | (np.isnan(ref) & np.isnan(mine))).all()
+    assert np.isnan(mine[[0x7F, 0xFF]]).all() and np.isfinite(np.delete(mine, [0x7F, 0xFF])).all()
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def test_fp8_encoding_rounds_to_nearest_even_and_saturates():
+    """Every code value, every midpoint between neighbouring codes (ties go to the
+    even code), one float32 step either side of each midpoint and random values in
+    range all encode as torch does; beyond 448 the encoding saturates."""
+    vals = np.array(sorted({oracle.fp8_value(c) for c in range(0x7F)}), dtype=np.float64)  # >= 0
+    mids = (vals[:-1] + vals[1:]) / 2
+    xs = [vals.astype(np.float32), mids.astype(np.float32),
+          np.nextafter(mids.astype(np.float32), np.float32(0)),
+          np.nextafter(mids.astype(np.float32), np.float32(1000))]
+    rng = np.random.default_rng(7)
+    xs.append((rng.uniform(-1, 1, 20000) * 448).astype(np.float32))
+    xs.append((rng.uniform(-1, 1, 5000) * 2.0 ** -6).astype(np.float32))  # subnormal range
+    x = np.concatenate(xs)
+    x = np.concatenate([x, -x])
+    assert (np.abs(x) <= 448).all()
+    mine = np.array([oracle.fp8_encode(v) for v in x], dtype=np.uint8)
+    ref = _torch_e4m3_codes(x)
+    assert (mine == ref).all(), x[mine != ref][:5]
+    # ties: the midpoint of codes n and n+1 goes to the even one
+    for n in range(1, 0x7E):
+        m = np.float32((oracle.fp8_value(n) + oracle.fp8_value(n + 1)) / 2)
+        assert oracle.fp8_encode(m) == (n if n % 2 == 0 else n + 1)
+    for v, code in ((448.5, 0x7E), (1000.0, 0x7E), (3e38, 0x7E), (-500.0, 0xFE), (float("inf"), 0x7E)):
+        assert oracle.fp8_encode(v) == code
+    assert oracle.fp8_encode(float("nan")) & 0x7F == 0x7F
+
+
+def test_fp8_quantizer_rounds_the_float32_product():
+    x = synthgen.normal_bf16(61, 1, (4096,))
+    x = synthgen.float_to_bf16(bf(x) * 200.0)  # some beyond 448 at inverse scales >= 1
+    for inv in (1.0, 0.37, 3.0):
+        codes = oracle.quantize_fp8(x, inv)
+        prod = synthgen.bf16_to_float(x).astype(np.float32) * np.float32(inv)
+        ok = np.abs(prod) <= 448
+        assert ok.sum() > 1000 and (inv < 1 or (~ok).sum() > 50)
+        assert (codes[ok] == _torch_e4m3_codes(prod[ok])).all()
+        assert (codes[~ok] == np.where(prod[~ok] > 0, 0x7E, 0xFE)).all()
+
+
+def _fp8_cache(seed, shape, scale):
+    """E4M3 codes of N(0, 1) values at this scale, and the same values in bf16 (exact
+    when the scale is a power of two)."""
+    x = synthgen.normal_bf16(seed, 9, shape)
+    codes = oracle.quantize_fp8(x, 1.0 / scale)
+    vals = np.vectorize(oracle.fp8_value)(codes) * scale
+    return codes, synthgen.float_to_bf16(vals), vals
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_fp8_sparse_attention_equals_bf16_on_exact_values(G):
+    """With power-of-two scales every cached value is exact in bf16, and the FP8
+    sparse attention (prefill and decode) equals the pinned bf16 one on those values
+    bit for bit."""
+    lengths, Hkv, d, K, W = [300, 1, 90], 2, 128, 32, 8
+    Hq = G * Hkv
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=62)
+    T = int(cu[-1])
+    k8, kb, _ = _fp8_cache(63, (T, Hkv, d), 0.5)
+    v8, vb, _ = _fp8_cache(64, (T, Hkv, d), 4.0)
+    idx, _ = oracle.select(q, kb, cu, Hq, Hkv, K, W)
+    idx = idx.reshape(T, Hkv, K + W)
+    a64, a16 = oracle.sparse_attn_fp8(q, k8, v8, 0.5, 4.0, cu, Hq, Hkv, idx)
+    b64, b16 = oracle.sparse_attn(q, kb, vb, cu, Hq, Hkv, idx)
+    assert np.array_equal(a64, b64) and np.array_equal(a16, b16)
+    qd = synthgen.normal_bf16(65, 1, (len(lengths), Hq, d))
+    didx, _ = oracle.decode_select(qd, kb, cu, Hq, Hkv, K, W)
+    didx = didx.reshape(len(lengths), Hkv, K + W)
+    c64, _ = oracle.decode_sparse_attn_fp8(qd, k8, v8, 0.5, 4.0, cu, Hq, Hkv, didx)
+    e64, _ = oracle.decode_sparse_attn(qd, kb, vb, cu, Hq, Hkv, didx)
+    assert np.array_equal(c64, e64)
+
+
+def test_fp8_sparse_attention_against_torch_masked_softmax():
+    """Arbitrary scales: the FP8 sparse output equals a float64 torch softmax over
+    the dequantised keys with every unselected logit at -inf."""
+    lengths, Hq, Hkv, d, K, W = [200, 50], 4, 2, 128, 16, 8
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=66)
+    T = int(cu[-1])
+    ks, vs = 0.37, 1.9
+    k8, _, kval = _fp8_cache(67, (T, Hkv, d), ks)
+    v8, _, vval = _fp8_cache(68, (T, Hkv, d), vs)
+    idx, _ = oracle.select(q, k, cu, Hq, Hkv, K, W)
+    idx = idx.reshape(T, Hkv, K + W)
+    toks = np.array([0, 5, 199, 200, 249])
+    o64, _ = oracle.sparse_attn_fp8(q, k8, v8, ks, vs, cu, Hq, Hkv, idx, tokens=toks)
+    G = Hq // Hkv
+    for n, tg in enumerate(toks):
+        i = int(np.searchsorted(cu, tg, side="right") - 1)
+        base, t = int(cu[i]), int(tg - cu[i])
+        for h in range(Hq):
+            g = h // G
+            sel = idx[tg, g][(idx[tg, g] >= 0) & (idx[tg, g] <= t)]
+            mask = torch.full((t + 1,), -float("inf"), dtype=torch.float64)
+            mask[torch.from_numpy(sel.astype(np.int64))] = 0.0
+            kk = torch.from_numpy(kval[base:base + t + 1, g])
+            logits = (kk @ torch.from_numpy(bf(q[tg, h]))) / np.sqrt(d) + mask
+            ref = torch.softmax(logits, 0) @ torch.from_numpy(vval[base:base + t + 1, g])
+            assert np.allclose(o64[n, h], ref.numpy(), rtol=1e-12, atol=1e-13)
