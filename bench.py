@@ -30,8 +30,9 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "prefill tokens/sec (select+sparse attn) at L=32k; % MFMA peak, % HBM BW"
 
 
-def algorithmic_work(lengths, Hq, Hkv, d, K, W):
-    """Selection MFMA flops (two QK^T passes) and sparse-layer bytes per layer."""
+def algorithmic_work(lengths, Hq, Hkv, d, K, W, elem_bytes=2):
+    """Selection MFMA flops (two QK^T passes) and sparse-layer bytes per layer
+    (K/V elements of elem_bytes: 2 for bf16, 1 for the FP8 cache)."""
     KW = K + W
     pairs = sum(L * (L + 1) // 2 for L in lengths)
     f_sel = 4 * d * Hq * pairs
@@ -40,7 +41,7 @@ def algorithmic_work(lengths, Hq, Hkv, d, K, W):
         m = min(L, KW)
         n_sum += m * (m + 1) // 2 + (L - m) * KW  # sum_t min(t+1, KW)
     T = sum(lengths)
-    gathered = Hkv * n_sum * 2 * d * 2           # K and V rows, once per (t, g)
+    gathered = Hkv * n_sum * 2 * d * elem_bytes  # K and V rows, once per (t, g)
     idx_bytes = T * Hkv * KW * 4
     qo_bytes = 2 * T * Hq * d * 2
     return f_sel, gathered + idx_bytes + qo_bytes, n_sum
@@ -171,6 +172,16 @@ def main():
     decay_ms = timed(lambda: hs2.hs2_select_ex(case.dims, case.varlen, case.q_full, case.k, idx,
                                                None, decay_mu=0.5, workspace=case.workspace,
                                                stream=stream), args.kernel_reps)
+    # FP8 KV cache: the cache written by the quantizer, one sparse layer reading it
+    ks, vs = 1.0 / 16, 1.0 / 16
+    k8 = torch.empty((T, Hkv, d), dtype=torch.uint8, device="cuda")
+    v8 = torch.empty_like(k8)
+    quant_ms = timed(lambda: (hs2.hs2_quantize_fp8(case.k, k8, 1.0 / ks, stream=stream),
+                              hs2.hs2_quantize_fp8(case.v, v8, 1.0 / vs, stream=stream)),
+                     args.kernel_reps)
+    sp8_ms = timed(lambda: hs2.hs2_sparse_attn_fp8(case.dims, case.varlen, case.q_sparse[0], k8, v8,
+                                                   ks, vs, idx, outs[0], hs2.HS2_OUT_BF16,
+                                                   stream=stream), args.kernel_reps)
     full_out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
     full_ms = timed(lambda: hs2.hs2_select_full(case.dims, case.varlen, case.q_full, case.k, case.v,
                                                 idx, full_out, hs2.HS2_OUT_BF16,
@@ -194,6 +205,16 @@ def main():
                  "algorithmic_flops": f_out, "extra_ms": round(out_ms, 4),
                  "select_full_ms": round(full_ms, 4),
                  "note": "the full layer's own output (hs2_select_full minus hs2_select), bf16 out"}
+    _, b_sp8, _ = algorithmic_work(w.lengths, Hq, Hkv, d, K, W, elem_bytes=1)
+    q_bytes = 2 * T * Hkv * d * (2 + 1)  # K and V: bf16 read, codes written
+    fp8_roof = {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                "sparse_layer_ms": round(sp8_ms, 4),
+                "sparse_achieved": round(b_sp8 / (sp8_ms * 1e-3) / 1e9, 1),
+                "sparse_algorithmic_bytes": b_sp8,
+                "quantize_ms": round(quant_ms, 4),
+                "quantize_achieved": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                "note": "FP8 (E4M3) KV cache: hs2_quantize_fp8 of K and V, then one sparse layer "
+                        "over the codes (hs2_sparse_attn_fp8); bf16 layer: roofline.avg_launch_ms"}
     select_roof = {"bound": "mfma", "achieved": round(sel_tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
                    "unit": "TFLOP/s", "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4),
                    "algorithmic_flops": f_sel, "avg_call_ms": round(sel_ms, 4),
@@ -234,6 +255,7 @@ def main():
         "cpu_baseline": cpu,
         "select": select_roof,
         "full_layer_output": full_roof,
+        "fp8_kv": fp8_roof,
         "p50_ms": round(p50, 4), "p99_ms": round(p99, 4), "jitter_flag": bool(p99 > 1.3 * p50),
         "roofline_tokens_per_s": round(T / (f_sel / (MFMA_BF16_PEAK_TFS * 1e12)
                                             + len(outs) * b_sp / (HBM_PEAK_GBS * 1e9)), 1),

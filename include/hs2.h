@@ -232,6 +232,32 @@ int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const 
                            const void* k, const void* v, const int32_t* idx, void* out,
                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 KV cache (HySparse2 news summary, cost paragraph: the KV cache kept in
+ * FP8). Codes are OCP FP8 E4M3 ("e4m3fn": bias 7, subnormals m * 2^-9, largest
+ * finite 448, S.1111.111 NaN, no infinities) with one fp32 scale per tensor:
+ *   k[j,g,e] = k_scale * E4M3(k8[j,g,e]),  v[j,g,e] = v_scale * E4M3(v8[j,g,e]).
+ * k8, v8 [T,Hkv,128] uint8 device arrays, 8-byte aligned; scales finite, > 0.
+ *
+ * hs2_quantize_fp8 writes a cache: dst[i] = E4M3(float(src[i]) * inv_scale) for
+ * n bf16 values src (16-byte aligned) into dst (8-byte aligned): the product
+ * rounded to float, then to the nearest code (ties to even), saturating at
+ * +-448; NaN gives a NaN code. Pass inv_scale = 1 / scale.
+ */
+int hs2_quantize_fp8(const void* src, uint8_t* dst, int64_t n, float inv_scale, void* stream);
+
+/* hs2_sparse_attn over an FP8 cache (same q, idx, out, workspace and errors). */
+int hs2_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
+                        const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
+                        const int32_t* idx, void* out, int out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* hs2_decode_sparse_attn over an FP8 cache (same workspace as HS2_OP_DECODE_SPARSE). */
+int hs2_decode_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                               const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
+                               const int32_t* idx, void* out, int out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Static text for a status; for HS2_ERR_HIP the last HIP error of this thread. */
 const char* hs2_status_string(int status);
 

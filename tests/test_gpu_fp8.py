@@ -1,0 +1,182 @@
+"""GPU parity of the FP8 KV cache path against the oracle, through the C ABI:
+the quantizer (bit-exact E4M3 codes, including ties between codes, subnormals,
+saturation and the tail of a length not divisible by 8) and sparse attention over
+E4M3 K/V with per-tensor scales (A4: fp32 output within 1e-5; A3: bf16 output
+within 2e-2; both on the GPU's own index sets) in prefill and in the decode step
+(rows split over several wavefronts and merged)."""
+import numpy as np
+import pytest
+
+import synthgen
+from hs2_testlib import A3_TOL, A4_TOL, GpuCase, from_dev_bf16, log, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_level_sparse_hs2_amd as hs2
+    hs2.load_library()
+
+
+def gpu_quantize(x_bits, inv):
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    src = to_dev_bf16(x_bits)
+    dst = torch.empty(x_bits.shape, dtype=torch.uint8, device="cuda")
+    hs2.hs2_quantize_fp8(src, dst, inv)
+    torch.cuda.synchronize()
+    return dst
+
+
+def special_values():
+    """bf16 values that probe the encoding: every code's value and every midpoint
+    between neighbouring codes (ties; exact in bf16), zeros, subnormals, the
+    saturation edge and beyond."""
+    import oracle
+    vals = np.array(sorted({oracle.fp8_value(c) for c in range(0x7F)}))
+    mids = (vals[:-1] + vals[1:]) / 2
+    extra = np.array([0.0, 2.0 ** -10, 3 * 2.0 ** -11, 448.0, 456.0, 464.0, 480.0, 1e5, 3e38])
+    x = np.concatenate([vals, mids, extra])
+    x = np.concatenate([x, -x])
+    bits = synthgen.float_to_bf16(x)
+    exact = np.abs(x) < 1e5  # every code value and midpoint is a bf16 value
+    assert (synthgen.bf16_to_float(bits).astype(np.float64)[exact] == x[exact]).all()
+    return bits
+
+
+@pytest.mark.parametrize("n", [3, 8, 8 * 1000 + 5, 1 << 20])
+@pytest.mark.parametrize("inv", [1.0, 0.37, 3.0])
+def test_quantize_codes_bit_exact(n, inv):
+    import oracle
+    x = synthgen.float_to_bf16(synthgen.bf16_to_float(synthgen.normal_bf16(70 + n % 97, 1, (n,)))
+                               .astype(np.float64) * 200.0)
+    got = gpu_quantize(x, inv).cpu().numpy()
+    ref = oracle.quantize_fp8(x, inv)
+    bad = np.count_nonzero(got != ref)
+    log(f"quantize n={n} inv={inv}: mismatches {bad}")
+    assert bad == 0
+
+
+def test_quantize_ties_subnormals_saturation_and_nan():
+    import oracle
+    x = special_values()
+    for inv in (1.0, 0.5):
+        got = gpu_quantize(x, inv).cpu().numpy()
+        ref = oracle.quantize_fp8(x, inv)
+        bad = np.nonzero(got != ref)[0]
+        log(f"special values inv={inv}: {len(x)} values, mismatches {len(bad)} "
+            f"{[(float(synthgen.bf16_to_float(x[i:i+1])[0]), int(got[i]), int(ref[i])) for i in bad[:6]]}")
+        assert len(bad) == 0
+    nan = np.array([0x7FC0, 0xFFC0, 0x3F80], dtype=np.uint16)  # NaN, -NaN, 1.0
+    got = gpu_quantize(nan, 1.0).cpu().numpy()
+    assert (got[:2] & 0x7F == 0x7F).all() and got[2] == oracle.fp8_encode(1.0)
+
+
+def fp8_inputs(inp, ks, vs):
+    import oracle
+    return oracle.quantize_fp8(inp["k"], 1.0 / ks), oracle.quantize_fp8(inp["v"], 1.0 / vs)
+
+
+def check_sparse_fp8(case, k8, v8, ks, vs, idx_t, label):
+    import oracle
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    w, inp = case.w, case.inputs
+    cu = inp["cu_seqlens"]
+    idx = idx_t.cpu().numpy()
+    k8_d, v8_d = torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda()
+    for l, (qs_np, qs) in enumerate(zip(inp["q_sparse"], case.q_sparse)):
+        out32 = torch.empty((case.T, w.Hq, w.d), dtype=torch.float32, device="cuda")
+        out16 = torch.empty((case.T, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+        hs2.hs2_sparse_attn_fp8(case.dims, case.varlen, qs, k8_d, v8_d, ks, vs, idx_t, out32,
+                                hs2.HS2_OUT_F32)
+        hs2.hs2_sparse_attn_fp8(case.dims, case.varlen, qs, k8_d, v8_d, ks, vs, idx_t, out16,
+                                hs2.HS2_OUT_BF16)
+        torch.cuda.synchronize()
+        o64, o16 = oracle.sparse_attn_fp8(qs_np, k8, v8, ks, vs, cu, w.Hq, w.Hkv, idx,
+                                          scale=w.scale)
+        err4 = np.abs(out32.cpu().numpy() - o64).max()
+        g = synthgen.bf16_to_float(from_dev_bf16(out16)).astype(np.float64)
+        err3 = np.abs(g - synthgen.bf16_to_float(o16).astype(np.float64)).max()
+        log(f"  {label} layer {l}: A4 max-abs {err4:.3g} A3 max-abs {err3:.3g} "
+            f"(output scale {np.abs(o64).max():.3g})")
+        assert err4 <= A4_TOL and err3 <= A3_TOL
+
+
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_sparse_fp8_prefill(G):
+    w = synthgen.custom([1, 33, 700, 2100, 4500], Hq=2 * G, Hkv=2, K=256, W=32, n_sparse=1,
+                        seed=140 + G)
+    log(f"fp8 prefill: lengths={w.lengths} Hq={w.Hq} Hkv={w.Hkv} K={w.K} W={w.W}")
+    inp = synthgen.make_inputs(w)
+    case = GpuCase(w, inp)
+    idx_t, _ = case.select()
+    ks, vs = 0.037, 0.05  # codes ~ N(0, 27) and N(0, 20): well inside +-448
+    k8, v8 = fp8_inputs(inp, ks, vs)
+    check_sparse_fp8(case, k8, v8, ks, vs, idx_t, "scales 0.037/0.05")
+
+
+def test_fp8_chain_gpu_quantize_then_sparse():
+    """The GPU's own quantizer writes the cache the gather reads (codes checked
+    bit-exact first), at the full-size budget."""
+    import oracle
+    w = synthgen.custom([3000, 9000], Hq=16, Hkv=2, K=1024, W=128, n_sparse=2, seed=150)
+    log(f"fp8 chain: lengths={w.lengths} Hq={w.Hq} Hkv={w.Hkv} K={w.K} W={w.W}")
+    inp = synthgen.make_inputs(w)
+    case = GpuCase(w, inp)
+    idx_t, _ = case.select()
+    ks, vs = 1.0 / 16, 1.0 / 24
+    k8_d = gpu_quantize(inp["k"], 1.0 / ks)
+    v8_d = gpu_quantize(inp["v"], 1.0 / vs)
+    k8, v8 = k8_d.cpu().numpy(), v8_d.cpu().numpy()
+    assert (k8 == oracle.quantize_fp8(inp["k"], 1.0 / ks)).all()
+    assert (v8 == oracle.quantize_fp8(inp["v"], 1.0 / vs)).all()
+    check_sparse_fp8(case, k8, v8, ks, vs, idx_t, "gpu-quantized")
+
+
+@pytest.mark.parametrize("lengths,G", [([1, 2, 129, 1153, 5000, 17], 4), ([20000, 3000], 8),
+                                       ([40000], 1)])
+def test_sparse_fp8_decode(lengths, G):
+    import oracle
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    w = synthgen.custom(lengths, Hq=2 * G, Hkv=2, K=1024, W=128, n_sparse=1, seed=160 + G)
+    log(f"fp8 decode: lengths={w.lengths} Hq={w.Hq} Hkv={w.Hkv} K={w.K} W={w.W}")
+    inp = synthgen.make_decode_inputs(w)
+    cu = inp["cu_seqlens"]
+    B, Hq, Hkv, KW = len(lengths), w.Hq, w.Hkv, w.K + w.W
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    cache = hs2.VarlenArgs(cu_dev, [int(x) for x in cu])
+    dims = hs2.make_dims(Hq, Hkv, w.K, w.W, w.scale)
+    k, q = to_dev_bf16(inp["k"]), to_dev_bf16(inp["q_dec"])
+    nbytes = hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SELECT, 0)
+    ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
+    idx_t = torch.empty((B, Hkv, KW), dtype=torch.int32, device="cuda")
+    hs2.hs2_decode_select(dims, cache, q, k, idx_t, None, ws)
+    ks, vs = 0.037, 0.05
+    k8, v8 = fp8_inputs(inp, ks, vs)
+    k8_d, v8_d = torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda()
+    nsp = hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SPARSE, 0)
+    ws_sp = torch.empty(max(1, nsp), dtype=torch.uint8, device="cuda")
+    idx = None
+    for qs_np in inp["q_sparse_dec"]:
+        qs = to_dev_bf16(qs_np)
+        out32 = torch.empty((B, Hq, w.d), dtype=torch.float32, device="cuda")
+        out16 = torch.empty((B, Hq, w.d), dtype=torch.bfloat16, device="cuda")
+        hs2.hs2_decode_sparse_attn_fp8(dims, cache, qs, k8_d, v8_d, ks, vs, idx_t, out32,
+                                       hs2.HS2_OUT_F32, ws_sp)
+        hs2.hs2_decode_sparse_attn_fp8(dims, cache, qs, k8_d, v8_d, ks, vs, idx_t, out16,
+                                       hs2.HS2_OUT_BF16, ws_sp)
+        torch.cuda.synchronize()
+        idx = idx_t.cpu().numpy()
+        o64, o16 = oracle.decode_sparse_attn_fp8(qs_np, k8, v8, ks, vs, cu, Hq, Hkv, idx,
+                                                 scale=w.scale)
+        err4 = np.abs(out32.cpu().numpy() - o64).max()
+        g = synthgen.bf16_to_float(from_dev_bf16(out16)).astype(np.float64)
+        err3 = np.abs(g - synthgen.bf16_to_float(o16).astype(np.float64)).max()
+        log(f"  workspace {nsp} B: A4 max-abs {err4:.3g} A3 max-abs {err3:.3g}")
+        assert err4 <= A4_TOL and err3 <= A3_TOL

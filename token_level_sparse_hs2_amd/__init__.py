@@ -96,6 +96,13 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_decode_select.restype = i32
     lib.hs2_decode_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.hs2_decode_sparse_attn.restype = i32
+    f32 = ctypes.c_float
+    lib.hs2_quantize_fp8.argtypes = [vp, vp, i64, f32, vp]
+    lib.hs2_quantize_fp8.restype = i32
+    lib.hs2_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp, sz, vp]
+    lib.hs2_sparse_attn_fp8.restype = i32
+    lib.hs2_decode_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp, sz, vp]
+    lib.hs2_decode_sparse_attn_fp8.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_plan_task.argtypes = [ctypes.POINTER(ctypes.c_int32), i32, i32, i64,
@@ -240,6 +247,34 @@ def hs2_decode_sparse_attn(dims: Dims, cache: VarlenArgs, q, k, v, idx, out,
                                                  _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
                                                  out_dtype, _ptr(workspace), ws_bytes,
                                                  _stream(stream)))
+
+
+def hs2_quantize_fp8(src, dst, inv_scale: float, stream=None) -> None:
+    """FP8 cache codes: dst (uint8, same element count) = E4M3(float(src) * inv_scale)."""
+    n = src.numel()
+    assert dst.numel() == n
+    _check(load_library().hs2_quantize_fp8(_ptr(src), _ptr(dst), n, float(inv_scale),
+                                           _stream(stream)))
+
+
+def hs2_sparse_attn_fp8(dims: Dims, varlen: VarlenArgs, q, k8, v8, k_scale: float, v_scale: float,
+                        idx, out, out_dtype: int = HS2_OUT_BF16, stream=None) -> None:
+    """hs2_sparse_attn over an FP8 cache: k = k_scale * E4M3(k8), v = v_scale * E4M3(v8)."""
+    _check(load_library().hs2_sparse_attn_fp8(ctypes.byref(dims), ctypes.byref(varlen.struct),
+                                              _ptr(q), _ptr(k8), _ptr(v8), float(k_scale),
+                                              float(v_scale), _ptr(idx), _ptr(out), out_dtype,
+                                              None, 0, _stream(stream)))
+
+
+def hs2_decode_sparse_attn_fp8(dims: Dims, cache: VarlenArgs, q, k8, v8, k_scale: float,
+                               v_scale: float, idx, out, out_dtype: int = HS2_OUT_BF16,
+                               workspace=None, stream=None) -> None:
+    """hs2_decode_sparse_attn over an FP8 cache."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().hs2_decode_sparse_attn_fp8(
+        ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(k8), _ptr(v8),
+        float(k_scale), float(v_scale), _ptr(idx), _ptr(out), out_dtype, _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def hs2_plan_task(cu_host: Sequence[int], rows_per_task: int, task: int):

@@ -292,14 +292,34 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   return HS2_OK;
 }
 
+// K/V of a sparse launch: bf16 rows, or (fp8_scales = {k_scale, v_scale}) E4M3 codes
+void set_kv(hs2::SparseParams* p, const void* k, const void* v, const float* fp8_scales) {
+  if (fp8_scales) {
+    p->k8 = static_cast<const uint8_t*>(k);
+    p->v8 = static_cast<const uint8_t*>(v);
+    p->v_scale = fp8_scales[1];
+  } else {
+    p->k = static_cast<const uint16_t*>(k);
+    p->v = static_cast<const uint16_t*>(v);
+  }
+}
+
+// FP8 scales: finite and > 0; code rows are read 8 bytes at a time
+int check_fp8(const void* k8, const void* v8, float k_scale, float v_scale) {
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return HS2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k8) | reinterpret_cast<uintptr_t>(v8)) & 7u)
+    return HS2_ERR_INVALID_ARG;
+  return HS2_OK;
+}
+
 int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
                const void* k, const void* vv, const int32_t* idx, void* out, int out_dtype,
-               hipStream_t s) {
+               hipStream_t s, const float* fp8_scales = nullptr) {
   if (geo.T == 0) return HS2_OK;
   hs2::SparseParams p{};
   p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(vv);
+  set_kv(&p, k, vv, fp8_scales);
   p.idx = idx;
   p.cu = v->cu_seqlens;
   p.B = v->batch;
@@ -307,10 +327,10 @@ int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   p.Hkv = d->num_kv_heads;
   p.KW = d->top_k + d->window;
   p.T = geo.T;
-  p.c = scale_log2(d);
+  p.c = scale_log2(d) * (fp8_scales ? fp8_scales[0] : 1.f);
   p.out = out;
   p.n_part = 1;
-  hipError_t e = hs2::launch_sparse(geo.G, out_dtype == HS2_OUT_F32, p, s);
+  hipError_t e = hs2::launch_sparse(geo.G, out_dtype == HS2_OUT_F32, fp8_scales != nullptr, p, s);
   if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
   return HS2_OK;
 }
@@ -509,21 +529,26 @@ int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
   return HS2_OK;
 }
 
-int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
-                           const void* k, const void* v, const int32_t* idx, void* out,
-                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int run_decode_sparse(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
+                      const void* v, const int32_t* idx, void* out, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream, const float* fp8_scales) {
   DecodeGeometry dg;
   int st = validate_decode(dims, cache, &dg);
   if (st != HS2_OK) return st;
   if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (fp8_scales && check_fp8(k, v, fp8_scales[0], fp8_scales[1]) != HS2_OK)
+    return HS2_ERR_INVALID_ARG;
   if (dg.geo.B == 0) return HS2_OK;
   if (!q || !k || !v || !idx || !out) return HS2_ERR_INVALID_ARG;
   if (dg.sparse_bytes > 0 && (!workspace || workspace_bytes < dg.sparse_bytes))
     return HS2_ERR_WORKSPACE;
   hs2::SparseParams p{};
   p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
+  set_kv(&p, k, v, fp8_scales);
   p.idx = idx;
   p.cu = cache->cu_seqlens;
   p.B = cache->batch;
@@ -531,7 +556,7 @@ int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const 
   p.Hkv = dims->num_kv_heads;
   p.KW = dims->top_k + dims->window;
   p.T = cache->batch;
-  p.c = scale_log2(dims);
+  p.c = scale_log2(dims) * (fp8_scales ? fp8_scales[0] : 1.f);
   p.out = out;
   p.decode = 1;
   p.n_part = dg.n_part;
@@ -540,8 +565,59 @@ int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const 
     p.part_o = reinterpret_cast<float*>(w + dg.off_po);
     p.part_ml = reinterpret_cast<float2*>(w + dg.off_pml);
   }
-  hipError_t e = hs2::launch_sparse(dg.geo.G, out_dtype == HS2_OUT_F32, p, static_cast<hipStream_t>(stream));
+  hipError_t e = hs2::launch_sparse(dg.geo.G, out_dtype == HS2_OUT_F32, fp8_scales != nullptr, p,
+                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode sparse attention kernel");
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                           const void* k, const void* v, const int32_t* idx, void* out,
+                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_decode_sparse(dims, cache, q, k, v, idx, out, out_dtype, workspace, workspace_bytes,
+                           stream, nullptr);
+}
+
+int hs2_decode_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                               const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
+                               const int32_t* idx, void* out, int out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const float sc[2] = {k_scale, v_scale};
+  return run_decode_sparse(dims, cache, q, k8, v8, idx, out, out_dtype, workspace,
+                           workspace_bytes, stream, sc);
+}
+
+int hs2_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
+                        const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
+                        const int32_t* idx, void* out, int out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (check_fp8(k8, v8, k_scale, v_scale) != HS2_OK) return HS2_ERR_INVALID_ARG;
+  if (geo.T == 0) return HS2_OK;
+  if (!q || !k8 || !v8 || !idx || !out) return HS2_ERR_INVALID_ARG;
+  const float sc[2] = {k_scale, v_scale};
+  return run_sparse(dims, varlen, geo, q, k8, v8, idx, out, out_dtype,
+                    static_cast<hipStream_t>(stream), sc);
+}
+
+int hs2_quantize_fp8(const void* src, uint8_t* dst, int64_t n, float inv_scale, void* stream) {
+  if (n < 0 || !(std::isfinite(inv_scale) && inv_scale > 0.f)) return HS2_ERR_INVALID_ARG;
+  if (n == 0) return HS2_OK;
+  if (!src || !dst) return HS2_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(dst) & 7u))
+    return HS2_ERR_INVALID_ARG;
+  hipError_t e = hs2::launch_quantize_fp8(static_cast<const uint16_t*>(src), dst, n, inv_scale,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize kernel");
   return HS2_OK;
 }
 

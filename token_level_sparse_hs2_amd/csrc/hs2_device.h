@@ -34,6 +34,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint2 ldg64(const void* p) {
+  return *reinterpret_cast<const uint2*>(p);
+}
 __device__ __forceinline__ uint4 ldg128(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

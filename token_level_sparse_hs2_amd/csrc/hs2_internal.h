@@ -143,6 +143,11 @@ struct SparseParams {
   float c;              // softmax_scale * log2(e)
   void* out;            // [T, Hq, 128] bf16 or f32
   int decode;           // query row r is sequence r at its last position
+  // FP8 KV cache (E4M3 codes, per-tensor scales): k8 / v8 [T, Hkv, 128] replace
+  // k / v; the key scale is folded into c, the value scale multiplies the output
+  const uint8_t* k8;
+  const uint8_t* v8;
+  float v_scale;
   // split rows (decode): n_part waves share a row's index entries, each writing
   // an unnormalised partial that sparse_combine merges
   int n_part;           // 1 = one wave per row, output written directly
@@ -195,7 +200,10 @@ hipError_t launch_value_weights(const uint16_t* v, const int32_t* cu, int B, int
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
-hipError_t launch_sparse(int G, bool precise, const SparseParams& p, hipStream_t s);
+hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, hipStream_t s);
+// dst[i] = E4M3(float(src[i]) * inv_scale), round to nearest even, saturating at +-448
+hipError_t launch_quantize_fp8(const uint16_t* src, uint8_t* dst, int64_t n, float inv_scale,
+                               hipStream_t s);
 hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s);
 hipError_t launch_full_out(int G, bool precise, const FullOutParams& p, int64_t n_tasks,
                            hipStream_t s);

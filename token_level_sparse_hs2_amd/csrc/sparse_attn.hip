@@ -16,6 +16,17 @@
 // group share the gather) and, transposed, of O^T = V^T P^T. Online softmax in the log2 domain, fp32 accumulation. P enters
 // the matrix product as a sum of bf16 parts (two parts: ~16 mantissa bits; three
 // in the precise mode: ~24 bits), so rounding P to bf16 adds no visible error.
+//
+// FP8 KV cache (HySparse2 news summary, cost paragraph: the cache kept in FP8):
+// E4M3 codes with one fp32 scale per tensor. A lane gathers its 8 codes of a
+// 128-byte row (the elements of its 16-byte chunk of the bf16 layout) and widens
+// them with v_cvt_scalef32_pk_bf16_fp8 at scale 1, which is exact (every E4M3 value
+// is a bf16 value), so the LDS layout and the matrix code are those of the bf16
+// cache; the key scale is folded into the softmax constant and the value scale
+// into the output.
+#include <algorithm>
+#include <type_traits>
+
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -24,7 +35,13 @@ namespace hs2 {
 constexpr int kChunk = 32;  // index entries per step
 constexpr int kMaxParts = 32;  // partials merged per row (split rows of a decode step)
 
-template <int G, bool PRECISE>
+// Two E4M3 codes (bytes 2 HI, 2 HI + 1 of x) -> two bf16 in a word.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, HI));
+}
+
+template <int G, bool PRECISE, bool FP8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   __shared__ uint4 klds[4][kChunk][16];  // per wave: 32 K rows x 256 B, swizzled 16-byte chunks
   __shared__ uint4 vlds[4][kChunk][16];  // per wave: 32 V rows
@@ -66,9 +83,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   for (int i = 0; i < 8; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // this sequence's K/V rows of group g; row j starts at byte j * row_stride
-  const char* kseq = reinterpret_cast<const char*>(p.k + ((size_t)base * Hkv + g) * kHeadDim);
-  const char* vseq = reinterpret_cast<const char*>(p.v + ((size_t)base * Hkv + g) * kHeadDim);
-  const uint32_t row_stride = (uint32_t)Hkv * kHeadDim * 2;
+  constexpr int kElemBytes = FP8 ? 1 : 2;
+  const char* kseq = FP8 ? reinterpret_cast<const char*>(p.k8) : reinterpret_cast<const char*>(p.k);
+  const char* vseq = FP8 ? reinterpret_cast<const char*>(p.v8) : reinterpret_cast<const char*>(p.v);
+  kseq += ((size_t)base * Hkv + g) * kHeadDim * kElemBytes;
+  vseq += ((size_t)base * Hkv + g) * kHeadDim * kElemBytes;
+  const uint32_t row_stride = (uint32_t)Hkv * kHeadDim * kElemBytes;
   uint4(*vl)[16] = vlds[w];
   const int n_chunks = (KW + kChunk - 1) / kChunk;
   // this wave's steps: all of them, or its part's share
@@ -92,10 +112,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
     }
   };
   // gather the chunk's K and V rows, fully coalesced: load r covers keys
-  // 4r .. 4r+3, 16 lanes per 256-byte row (lane: key 4r + lq, 16-byte chunk lc)
+  // 4r .. 4r+3, 16 lanes per row (lane: key 4r + lq, elements 8 lc .. 8 lc + 7:
+  // 16 bytes of a bf16 row, 8 bytes of an FP8 one)
+  using Piece = std::conditional_t<FP8, uint2, uint4>;
   struct Gather {
-    uint4 kr[8];
-    uint4 vr[8];
+    Piece kr[8];
+    Piece vr[8];
   };
   auto gather = [&](const int (&j)[2], Gather& gb) {
 #pragma unroll
@@ -103,10 +125,23 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
       const int key = 4 * r + lq;  // entry of the chunk; its index is held by lane (key & 15)
       const int jj = __shfl(j[key >> 4], key & 15, 64);
       const bool ok = jj >= 0 && jj <= t;
-      const uint32_t off = (uint32_t)(ok ? jj : 0) * row_stride + 16u * lc;
-      gb.kr[r] = ldg128(kseq + off);
-      gb.vr[r] = ldg128(vseq + off);
+      const uint32_t off = (uint32_t)(ok ? jj : 0) * row_stride + (8u * kElemBytes) * lc;
+      if constexpr (FP8) {
+        gb.kr[r] = ldg64(kseq + off);
+        gb.vr[r] = ldg64(vseq + off);
+      } else {
+        gb.kr[r] = ldg128(kseq + off);
+        gb.vr[r] = ldg128(vseq + off);
+      }
     }
+  };
+  // a gathered piece as 8 bf16 (FP8: widened exactly)
+  auto widen = [&](const Piece& x) HS2_INLINE -> uint4 {
+    if constexpr (FP8)
+      return make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
+                        e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
+    else
+      return x;
   };
   uint4(*kl)[16] = klds[w];
 
@@ -124,8 +159,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
 #pragma unroll
     for (int r = 0; r < 8; r++) {
       const int key = 4 * r + lq;
-      kl[key][lc ^ (key & 15)] = gb.kr[r];
-      vl[key][lc ^ (2 * (key & 7))] = gb.vr[r];
+      kl[key][lc ^ (key & 15)] = widen(gb.kr[r]);
+      vl[key][lc ^ (2 * (key & 7))] = widen(gb.vr[r]);
     }
     wave_lds_fence();
     // raw scores S^T (keys x heads); lane: head lc, keys 16*mt + 4*lq + i
@@ -246,19 +281,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   }
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
+  const float osc = FP8 ? p.v_scale : 1.f;  // the value scale, outside the sums
   if (p.n_part > 1) {  // unnormalised partial of this part (m = -inf, sum 0 if it had none)
     if (lc < G) {
       const size_t slot = (size_t)vr * Hkv + g;
       float* po = p.part_o + (slot * G + lc) * kHeadDim;
 #pragma unroll
       for (int dt = 0; dt < 8; dt++)
-        *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lq) = o[dt];
+        *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lq) = FP8 ? o[dt] * osc : o[dt];
       if (lq == 0) p.part_ml[slot * G + lc] = make_float2(m, lsum);
     }
     return;
   }
   if (lc < G) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float inv = lsum > 0.f ? osc / lsum : 0.f;
     const size_t ob = ((size_t)tg * Hq + g * G + lc) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
@@ -317,14 +353,18 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(SparseParams p) {
 }
 
 template <int G>
-static hipError_t launch_sparse_g(bool precise, const SparseParams& p, hipStream_t s) {
+static hipError_t launch_sparse_g(bool precise, bool fp8, const SparseParams& p, hipStream_t s) {
   const int64_t blocks = ((p.T * p.n_part + 3) / 4) * p.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (precise)
-    hipLaunchKernelGGL((sparse_attn_kernel<G, true>), dim3((unsigned)blocks), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((sparse_attn_kernel<G, false>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (fp8) {
+    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, true>), grid, block, 0, s, p);
+  } else {
+    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, false>), grid, block, 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_part <= 1) return e;
   const int64_t rows = p.T * p.Hkv;
@@ -336,15 +376,58 @@ static hipError_t launch_sparse_g(bool precise, const SparseParams& p, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_sparse(int G, bool precise, const SparseParams& p, hipStream_t s) {
+hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, hipStream_t s) {
   switch (G) {
-    case 1: return launch_sparse_g<1>(precise, p, s);
-    case 2: return launch_sparse_g<2>(precise, p, s);
-    case 4: return launch_sparse_g<4>(precise, p, s);
-    case 8: return launch_sparse_g<8>(precise, p, s);
-    case 16: return launch_sparse_g<16>(precise, p, s);
+    case 1: return launch_sparse_g<1>(precise, fp8, p, s);
+    case 2: return launch_sparse_g<2>(precise, fp8, p, s);
+    case 4: return launch_sparse_g<4>(precise, fp8, p, s);
+    case 8: return launch_sparse_g<8>(precise, fp8, p, s);
+    case 16: return launch_sparse_g<16>(precise, fp8, p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Writing the FP8 cache: 8 elements per thread (one 16-byte load, one 8-byte
+// store), grid-stride; the product with inv_scale is rounded to fp32, clamped to
+// +-448 (NaN stays NaN: the comparisons fail) and rounded to the nearest E4M3
+// code by v_cvt_pk_fp8_f32. A tail of n % 8 elements is done one by one.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* src, uint8_t* dst,
+                                                           int64_t n, float inv_scale) {
+  auto q = [&](float x) HS2_INLINE {
+    const float y = x * inv_scale;
+    return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+  };
+  const int64_t n8 = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 x = ldg128(src + 8 * i);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      int r = 0;
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_bits_to_f32(w[2 * h] & 0xFFFFu)),
+                                          q(__uint_as_float(w[2 * h] & 0xFFFF0000u)), r, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_bits_to_f32(w[2 * h + 1] & 0xFFFFu)),
+                                          q(__uint_as_float(w[2 * h + 1] & 0xFFFF0000u)), r, true);
+      out[h] = (uint32_t)r;
+    }
+    *reinterpret_cast<uint2*>(dst + 8 * i) = make_uint2(out[0], out[1]);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (int)(n - 8 * n8)) {
+    const int64_t i = 8 * n8 + threadIdx.x;
+    const int r = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_bits_to_f32(src[i])), 0.f, 0, false);
+    dst[i] = (uint8_t)(r & 0xFF);
+  }
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* src, uint8_t* dst, int64_t n, float inv_scale,
+                               hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n / 8 + 255) / 256;
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 4096));
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n, inv_scale);
+  return hipGetLastError();
 }
 
 }  // namespace hs2
