@@ -45,7 +45,9 @@ template <int G, bool PRECISE, bool FP8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   __shared__ uint4 klds[4][kChunk][16];  // per wave: 32 K rows x 256 B, swizzled 16-byte chunks
   __shared__ uint4 vlds[4][kChunk][16];  // per wave: 32 V rows
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  // the wave index is uniform: row, sequence and K/V row pointers live in SGPRs,
+  // so the gathers take a scalar base and a 32-bit lane offset
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const int lq = l >> 4, lc = l & 15;
   const int Hkv = p.Hkv, Hq = p.Hq, KW = p.KW;
   const int g = blockIdx.x % Hkv;
@@ -120,12 +122,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
     Piece vr[8];
   };
   auto gather = [&](const int (&j)[2], Gather& gb) {
+    // byte offset of the row of each of the lane's two entries (row 0 if invalid)
+    int roff[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+      roff[mt] = (int)((uint32_t)(j[mt] >= 0 && j[mt] <= t ? j[mt] : 0) * row_stride);
 #pragma unroll
     for (int r = 0; r < 8; r++) {
-      const int key = 4 * r + lq;  // entry of the chunk; its index is held by lane (key & 15)
-      const int jj = __shfl(j[key >> 4], key & 15, 64);
-      const bool ok = jj >= 0 && jj <= t;
-      const uint32_t off = (uint32_t)(ok ? jj : 0) * row_stride + (8u * kElemBytes) * lc;
+      const int key = 4 * r + lq;  // entry of the chunk; its offset is held by lane (key & 15)
+      const uint32_t off =
+          (uint32_t)__shfl(roff[key >> 4], key & 15, 64) + (8u * kElemBytes) * lc;
       if constexpr (FP8) {
         gb.kr[r] = ldg64(kseq + off);
         gb.vr[r] = ldg64(vseq + off);
