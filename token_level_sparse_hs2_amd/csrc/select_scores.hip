@@ -328,18 +328,24 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     for (int rt = 0; rt < RT; rt++)
       nref4[rt] = *reinterpret_cast<const f32x4*>(&sm.nref[w * ROWS_W + 16 * rt + 4 * lq]);
   };
-  auto compute = [&](int buf) HS2_INLINE {
+  // the MFMAs of column tile ct (16 keys) for every row tile
+  auto compute_ct = [&](int buf, int ct) HS2_INLINE {
+    const int kk = 16 * ct + lc;  // kk & 15 == lc
 #pragma unroll
-    for (int ct = 0; ct < 4; ct++) {
-      const int kk = 16 * ct + lc;  // kk & 15 == lc
+    for (int ks = 0; ks < 4; ks++) {
+      const bf16x8 b = as_bf16x8(to_u32x4(sm.u.ktile[buf][kk][(4 * ks + lq) ^ lc]));
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        const bf16x8 b = as_bf16x8(to_u32x4(sm.u.ktile[buf][kk][(4 * ks + lq) ^ lc]));
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-          acc[rt][ct] = mfma16x16x32(qa[rt][ks], b, ks == 0 ? nref4[rt] : acc[rt][ct]);
-      }
+      for (int rt = 0; rt < RT; rt++)
+        acc[rt][ct] = mfma16x16x32(qa[rt][ks], b, ks == 0 ? nref4[rt] : acc[rt][ct]);
     }
+  };
+  auto compute = [&](int buf) HS2_INLINE {
+    // the wave's matrix block issues at raised priority, so that the other wave on
+    // the SIMD fills the matrix core's busy cycles with its exponentials
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++) compute_ct(buf, ct);
+    __builtin_amdgcn_s_setprio(0);
   };
   // keys beyond a row's token are -inf (only tiles that reach past t0)
   auto mask_causal = [&](int kt) HS2_INLINE {
@@ -370,15 +376,17 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) lsum[rt][i] = 0.f;
+    auto sum_ct = [&](int ct) HS2_INLINE {
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) lsum[rt][i] += fast_exp2(acc[rt][ct][i] * c);
+    };
     sweep(n_kt1, 0, 1, kend1, Ring{}, false, [&](int kt, int buf) HS2_INLINE {
       compute(buf);
       mask_causal(kt);
 #pragma unroll
-      for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          lsum[rt][i] += (fast_exp2(acc[rt][0][i] * c) + fast_exp2(acc[rt][1][i] * c)) +
-                         (fast_exp2(acc[rt][2][i] * c) + fast_exp2(acc[rt][3][i] * c));
+      for (int ct = 0; ct < 4; ct++) sum_ct(ct);
     });
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
