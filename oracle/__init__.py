@@ -77,6 +77,9 @@ def _load():
     lib.hs2o_decode_sparse_attn_fp8.argtypes = [vp, vp, vp, f64, f64, vp, i32, i32, i32, i32, f64,
                                                 i32, vp, vp, vp, i32]
     lib.hs2o_decode_sparse_attn_fp8.restype = i32
+    lib.hs2o_decode_select_fp8.argtypes = [vp, vp, f64, vp, i32, i32, i32, i32, f64, i32, i32, vp,
+                                           vp, i32]
+    lib.hs2o_decode_select_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -376,3 +379,23 @@ def decode_sparse_attn_fp8(q_dec, k8, v8, k_scale, v_scale, cu_seqlens, Hq, Hkv,
     if r != 0:
         raise ValueError("hs2o_decode_sparse_attn_fp8: bad arguments")
     return o64, o16
+
+
+def decode_select_fp8(q_dec, k8, k_scale, cu_seqlens, Hq, Hkv, K, W, scale=None, nthreads=None):
+    """decode_select over an FP8 key cache: k = k_scale * E4M3(k8)."""
+    lib = _load()
+    q_dec, k8, cu = _u16(q_dec), _u8(k8), _cu(cu_seqlens)
+    d = q_dec.shape[-1]
+    B = len(cu) - 1
+    assert q_dec.size == B * Hq * d
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(d))
+    idx = np.empty((B * Hkv, K + W), dtype=np.int32)
+    kth = np.empty(B * Hkv, dtype=np.float64)
+    if B == 0:
+        return idx, kth
+    r = lib.hs2o_decode_select_fp8(q_dec.ctypes.data, k8.ctypes.data, float(k_scale), cu.ctypes.data,
+                                   B, Hq, Hkv, d, scale, K, W, idx.ctypes.data, kth.ctypes.data,
+                                   nthreads or default_threads())
+    if r != 0:
+        raise ValueError("hs2o_decode_select_fp8: bad arguments")
+    return idx, kth

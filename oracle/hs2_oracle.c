@@ -141,11 +141,12 @@ static int find_seq(const dims_t* D, int64_t t_global) {
 
 /* ---- O1 + O2: per-head row statistics and the group score of one row ---- */
 /* Row (t, g) of the sequence starting at token `base`; qt holds the query
- * token's Hq query rows [Hq, d]. S_out[j] for j in [0, t]; scratch z holds
+ * token's Hq query rows [Hq, d]. Keys are bf16 (k), or with k8 set FP8 codes of
+ * value k_scale * E4M3(code). S_out[j] for j in [0, t]; scratch z holds
  * G*(t+1) doubles. */
-static void row_group_scores(const dims_t* D, const uint16_t* qt, const uint16_t* k, int64_t base,
-                             int64_t t, int g, double* z, double* S_out, double* m_out,
-                             double* l_out) {
+static void row_group_scores(const dims_t* D, const uint16_t* qt, const uint16_t* k,
+                             const uint8_t* k8, double k_scale, int64_t base, int64_t t, int g,
+                             double* z, double* S_out, double* m_out, double* l_out) {
   const int G = D->Hq / D->Hkv, d = D->d;
   const int64_t n = t + 1;
   for (int hh = 0; hh < G; hh++) {
@@ -156,9 +157,12 @@ static void row_group_scores(const dims_t* D, const uint16_t* qt, const uint16_t
     double* zr = z + (size_t)hh * n;
     double m = -INFINITY;
     for (int64_t j = 0; j < n; j++) { /* causal keys j <= t */
-      const uint16_t* kr = k + ((size_t)(base + j) * D->Hkv + g) * d;
+      const size_t off = ((size_t)(base + j) * D->Hkv + g) * d;
       double acc = 0.0;
-      for (int e = 0; e < d; e++) acc += qd[e] * bf2d(kr[e]);
+      if (k8)
+        for (int e = 0; e < d; e++) acc += qd[e] * (k_scale * e4m3_to_d(k8[off + e]));
+      else
+        for (int e = 0; e < d; e++) acc += qd[e] * bf2d(k[off + e]);
       zr[j] = D->scale * acc;
       if (zr[j] > m) m = zr[j];
     }
@@ -304,7 +308,7 @@ static void* select_worker(void* arg) {
         t = tg - base;
         qt = J->q + (size_t)tg * D->Hq * D->d;
       }
-      row_group_scores(D, qt, J->k, base, t, g, z, S, NULL, NULL);
+      row_group_scores(D, qt, J->k, J->k8, J->k_scale, base, t, g, z, S, NULL, NULL);
       if (D->oam_beta > 0.0) {
         /* output-aware metric (Stem page, OAM paragraph): the logit term
          * beta * max(0, log |v_j|_2) multiplies key j's probability, and so its
@@ -499,7 +503,8 @@ int hs2o_group_scores(const uint16_t* q, const uint16_t* k, const int32_t* cu, i
   int64_t base = cu[i], t = t_global - base;
   double* z = (double*)malloc(sizeof(double) * (size_t)(Hq / Hkv) * (size_t)(t + 1));
   if (!z) return -1;
-  row_group_scores(&D, q + (size_t)t_global * Hq * d, k, base, t, g, z, S_out, m_out, l_out);
+  row_group_scores(&D, q + (size_t)t_global * Hq * d, k, NULL, 1.0, base, t, g, z, S_out, m_out,
+                   l_out);
   free(z);
   return 0;
 }
@@ -544,6 +549,22 @@ int hs2o_decode_select(const uint16_t* q_dec, const uint16_t* k, const int32_t* 
   memset(&J, 0, sizeof(J));
   J.D = &D; J.q = q_dec; J.k = k; J.n_rows = (int64_t)B * Hkv; J.decode = 1;
   J.idx_out = idx_out; J.kth_out = kth_out; J.max_len = max_len(&D);
+  return run(&J, select_worker, nthreads);
+}
+
+/* Decode-step selection over an FP8 key cache (k = k_scale * E4M3(k8)); as
+ * hs2o_decode_select otherwise. */
+int hs2o_decode_select_fp8(const uint16_t* q_dec, const uint8_t* k8, double k_scale,
+                           const int32_t* cu, int B, int Hq, int Hkv, int d, double scale, int K,
+                           int W, int32_t* idx_out, double* kth_out, int nthreads) {
+  dims_t D = {B, Hq, Hkv, d, K, W, scale, cu, 0, 0.0, K};
+  if (!q_dec || !k8 || !cu || !idx_out || check_dims(&D)) return -1;
+  for (int b = 0; b < B; b++)
+    if (cu[b + 1] - cu[b] < 1) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.D = &D; J.q = q_dec; J.k8 = k8; J.k_scale = k_scale; J.n_rows = (int64_t)B * Hkv;
+  J.decode = 1; J.idx_out = idx_out; J.kth_out = kth_out; J.max_len = max_len(&D);
   return run(&J, select_worker, nthreads);
 }
 

@@ -670,3 +670,36 @@ def test_fp8_sparse_attention_against_torch_masked_softmax():
             logits = (kk @ torch.from_numpy(bf(q[tg, h]))) / np.sqrt(d) + mask
             ref = torch.softmax(logits, 0) @ torch.from_numpy(vval[base:base + t + 1, g])
             assert np.allclose(o64[n, h], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_fp8_decode_selection():
+    """Decode selection over an FP8 key cache: with a power-of-two scale it equals
+    the pinned bf16 decode selection on the same (exactly representable) keys, bit
+    for bit; with any scale it equals a numpy ranking of the group score computed
+    from the dequantised keys (S desc, position asc)."""
+    lengths, Hq, Hkv, d, K, W = [1, 40, 300, 97], 8, 2, 128, 24, 8
+    G = Hq // Hkv
+    q, k, v, cu = rand_inputs(lengths, Hq, Hkv, d, seed=71)
+    T, B = int(cu[-1]), len(lengths)
+    qd = synthgen.normal_bf16(72, 1, (B, Hq, d))
+    k8, kb, _ = _fp8_cache(73, (T, Hkv, d), 0.25)
+    a, ka = oracle.decode_select_fp8(qd, k8, 0.25, cu, Hq, Hkv, K, W)
+    b, kb_ = oracle.decode_select(qd, kb, cu, Hq, Hkv, K, W)
+    assert (a == b).all() and np.array_equal(ka, kb_)
+    ks = 0.037
+    k8, _, kval = _fp8_cache(74, (T, Hkv, d), ks)
+    idx, kth = oracle.decode_select_fp8(qd, k8, ks, cu, Hq, Hkv, K, W)
+    for bi in range(B):
+        base, L = int(cu[bi]), int(cu[bi + 1] - cu[bi])
+        t, n_c = L - 1, max(0, L - W)
+        for g in range(Hkv):
+            z = (bf(qd[bi, g * G:(g + 1) * G]) @ kval[base:base + L, g].T) / np.sqrt(d)
+            p = np.exp(z - z.max(1, keepdims=True))
+            S = (p / p.sum(1, keepdims=True)).sum(0)
+            order = sorted(range(n_c), key=lambda j: (-S[j], j))
+            take = order if n_c <= K else order[:K]
+            want = sorted(set(take) | set(range(n_c, L)))
+            row = idx[bi * Hkv + g]
+            assert list(row[row >= 0]) == want
+            if n_c > K:
+                assert abs(kth[bi * Hkv + g] - S[order[K - 1]]) <= 1e-12
