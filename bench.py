@@ -264,14 +264,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def decode_work(lengths, Hq, Hkv, d, K, W, n_sparse):
+def decode_work(lengths, Hq, Hkv, d, K, W, n_sparse, elem_bytes=2):
     """Algorithmic HBM bytes of one decode step: the K cache read once and the logits
     written and read once (selection), then per sparse layer the gathered K/V rows,
-    the index rows and the queries/outputs of the new tokens."""
+    the index rows and the queries/outputs of the new tokens (K/V elements of
+    elem_bytes: 2 for bf16, 1 for the FP8 cache)."""
     KW, B, T = K + W, len(lengths), sum(lengths)
-    sel = T * Hkv * d * 2 + 2 * T * Hq * 4 + B * Hq * d * 2 + B * Hkv * KW * 4
+    sel = T * Hkv * d * elem_bytes + 2 * T * Hq * 4 + B * Hq * d * 2 + B * Hkv * KW * 4
     n = sum(min(L, KW) for L in lengths)
-    sp = Hkv * n * 2 * d * 2 + B * Hkv * KW * 4 + 2 * B * Hq * d * 2
+    sp = Hkv * n * 2 * d * elem_bytes + B * Hkv * KW * 4 + 2 * B * Hq * d * 2
     return sel, sp
 
 
@@ -335,6 +336,23 @@ def main_decode(args):
     sel_ms = timed(select, 20)
     sp_ms = timed(lambda: sparse(0), 20)
     b_sel, b_sp = decode_work(w.lengths, Hq, Hkv, d, K, W, len(qs))
+    # the same step over an FP8 (E4M3) KV cache: selection and sparse layers read codes
+    ks8, vs8 = 1.0 / 16, 1.0 / 16
+    k8 = torch.empty((T, Hkv, d), dtype=torch.uint8, device="cuda")
+    v8 = torch.empty_like(k8)
+    hs2.hs2_quantize_fp8(k, k8, 1.0 / ks8, stream=stream)
+    hs2.hs2_quantize_fp8(v, v8, 1.0 / vs8, stream=stream)
+    idx8 = torch.empty_like(idx)
+
+    def step_fp8():
+        hs2.hs2_decode_select_fp8(dims, cache, q, k8, ks8, idx8, None, ws, stream=stream)
+        for i in range(len(qs)):
+            hs2.hs2_decode_sparse_attn_fp8(dims, cache, qs[i], k8, v8, ks8, vs8, idx8, outs[i],
+                                           hs2.HS2_OUT_BF16, ws_sp, stream=stream)
+
+    step8_ms = timed(step_fp8, 20)
+    b_sel8, b_sp8 = decode_work(w.lengths, Hq, Hkv, d, K, W, len(qs), elem_bytes=1)
+    b_step8 = b_sel8 + len(qs) * b_sp8
     b_step = b_sel + len(qs) * b_sp
     gbs = b_step / (step_ms * 1e-3) / 1e9
 
@@ -369,6 +387,12 @@ def main_decode(args):
                      "kernel": "whole decode step", "algorithmic_bytes_per_step": b_step},
         "select_ms": round(sel_ms, 5), "sparse_layer_ms": round(sp_ms, 5),
         "select_bytes": b_sel, "sparse_layer_bytes": b_sp,
+        "fp8_kv": {"ms_per_step": round(step8_ms, 5),
+                   "tokens_per_s": round(B / (step8_ms * 1e-3), 1),
+                   "achieved": round(b_step8 / (step8_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                   "algorithmic_bytes_per_step": b_step8,
+                   "note": "the same step over an E4M3 KV cache (hs2_decode_select_fp8 + "
+                           "hs2_decode_sparse_attn_fp8)"},
         "cpu_baseline": cpu, "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)

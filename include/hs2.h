@@ -252,6 +252,12 @@ int hs2_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const vo
                         const int32_t* idx, void* out, int out_dtype, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* hs2_decode_select over an FP8 key cache: the full layer's decode queries
+ * against k = k_scale * E4M3(k8) (same idx, kth, workspace and errors). */
+int hs2_decode_select_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                          const uint8_t* k8, float k_scale, int32_t* idx_out, float* kth_score_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* hs2_decode_sparse_attn over an FP8 cache (same workspace as HS2_OP_DECODE_SPARSE). */
 int hs2_decode_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
                                const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,

@@ -259,3 +259,26 @@ def test_select_ex_decay_validation(lib):
     assert call(d, o) == hs2.HS2_ERR_INVALID_ARG
     db = hs2.make_dims(32, 8, 1024, 128, flags=hs2.HS2_FLAG_BLOCK_SELECT)
     assert call(db, hs2.SelectOptions(0.0, 0.5)) == hs2.HS2_ERR_UNSUPPORTED
+
+
+def test_fp8_entry_point_validation(lib):
+    L = hs2.load_library()
+    d = hs2.make_dims(32, 8, 1024, 128)
+    v = varlen([5000])
+    assert L.hs2_quantize_fp8(8, 8, -1, 1.0, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_quantize_fp8(8, 8, 16, 0.0, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_quantize_fp8(8, 8, 16, float("nan"), None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_quantize_fp8(24, 8, 16, 1.0, None) == hs2.HS2_ERR_INVALID_ARG  # src not 16-aligned
+    assert L.hs2_quantize_fp8(None, None, 0, 1.0, None) == hs2.HS2_OK
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0)):
+        assert L.hs2_sparse_attn_fp8(ctypes.byref(d), ctypes.byref(v.struct), 8, 8, 8, ks, vs, 8, 8,
+                                     0, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_sparse_attn_fp8(ctypes.byref(d), ctypes.byref(v.struct), 8, 12, 8, 1.0, 1.0, 8, 8,
+                                 0, None, 0, None) == hs2.HS2_ERR_INVALID_ARG  # k8 not 8-aligned
+    dc = varlen([100, 50])
+    assert L.hs2_decode_select_fp8(ctypes.byref(d), ctypes.byref(dc.struct), 8, 8, -2.0, 8, None, 8,
+                                   1 << 40, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_decode_select_fp8(ctypes.byref(d), ctypes.byref(dc.struct), 8, None, 1.0, 8, None,
+                                   8, 1 << 40, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_decode_sparse_attn_fp8(ctypes.byref(d), ctypes.byref(dc.struct), 8, 8, 8, 1.0, 0.0,
+                                        8, 8, 0, 8, 1 << 40, None) == hs2.HS2_ERR_INVALID_ARG

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import synthgen
-from hs2_testlib import A3_TOL, A4_TOL, GpuCase, from_dev_bf16, log, to_dev_bf16
+from hs2_testlib import (A1_TOL, A2_MIN, A3_TOL, A4_TOL, GpuCase, _check_structure_rows,
+                         from_dev_bf16, log, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,14 +153,51 @@ def test_sparse_fp8_decode(lengths, G):
     cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
     cache = hs2.VarlenArgs(cu_dev, [int(x) for x in cu])
     dims = hs2.make_dims(Hq, Hkv, w.K, w.W, w.scale)
-    k, q = to_dev_bf16(inp["k"]), to_dev_bf16(inp["q_dec"])
+    q = to_dev_bf16(inp["q_dec"])
     nbytes = hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SELECT, 0)
     ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
     idx_t = torch.empty((B, Hkv, KW), dtype=torch.int32, device="cuda")
-    hs2.hs2_decode_select(dims, cache, q, k, idx_t, None, ws)
+    kth_t = torch.empty((B, Hkv), dtype=torch.float32, device="cuda")
     ks, vs = 0.037, 0.05
     k8, v8 = fp8_inputs(inp, ks, vs)
     k8_d, v8_d = torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda()
+    # the full layer's selection over the FP8 key cache
+    hs2.hs2_decode_select_fp8(dims, cache, q, k8_d, ks, idx_t, kth_t, ws)
+    torch.cuda.synchronize()
+    gidx = idx_t.cpu().numpy()
+    tloc = (cu[1:] - cu[:-1] - 1).astype(np.int64)
+    _check_structure_rows(gidx, tloc, w.K, w.W)
+    o_idx, o_kth = oracle.decode_select_fp8(inp["q_dec"], k8, ks, cu, Hq, Hkv, w.K, w.W,
+                                            scale=w.scale)
+    o_idx = o_idx.reshape(B, Hkv, KW)
+    kval = np.vectorize(oracle.fp8_value)(k8) * ks
+    G = Hq // Hkv
+    inter = tot = same = 0
+    worst = np.inf
+    for b in range(B):
+        for g in range(Hkv):
+            a_, o_ = gidx[b, g][gidx[b, g] >= 0], o_idx[b, g][o_idx[b, g] >= 0]
+            inter += len(np.intersect1d(a_, o_))
+            tot += len(o_)
+            if len(a_) == len(o_) and (a_ == o_).all():
+                same += 1
+                continue
+            base = int(cu[b])
+            z = (synthgen.bf16_to_float(inp["q_dec"][b, g * G:(g + 1) * G]).astype(np.float64)
+                 @ kval[base:base + tloc[b] + 1, g].T) * w.scale
+            pz = np.exp(z - z.max(1, keepdims=True))
+            S = (pz / pz.sum(1, keepdims=True)).sum(0)
+            glob = a_[a_ < tloc[b] - w.W + 1]
+            if len(glob):
+                worst = min(worst, S[glob].min() - o_kth[b * Hkv + g])
+    overlap = inter / max(1, tot)
+    log(f"  fp8 select: rows {B * Hkv} identical {same} overlap {overlap:.6f} A1 margin {worst:.3g}")
+    assert overlap >= A2_MIN and worst >= -A1_TOL
+    kth = kth_t.cpu().numpy().reshape(-1)
+    assert ((kth == -1.0) == (o_kth == -1.0)).all()
+    sel = o_kth > 0
+    if sel.any():
+        assert (np.abs(kth[sel] - o_kth[sel]) / o_kth[sel]).max() <= 1e-3
     nsp = hs2.hs2_workspace_size(dims, cache, hs2.HS2_OP_DECODE_SPARSE, 0)
     ws_sp = torch.empty(max(1, nsp), dtype=torch.uint8, device="cuda")
     idx = None

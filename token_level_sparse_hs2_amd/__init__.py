@@ -103,6 +103,8 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_sparse_attn_fp8.restype = i32
     lib.hs2_decode_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp, sz, vp]
     lib.hs2_decode_sparse_attn_fp8.restype = i32
+    lib.hs2_decode_select_fp8.argtypes = [D, V, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.hs2_decode_select_fp8.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_plan_task.argtypes = [ctypes.POINTER(ctypes.c_int32), i32, i32, i64,
@@ -264,6 +266,15 @@ def hs2_sparse_attn_fp8(dims: Dims, varlen: VarlenArgs, q, k8, v8, k_scale: floa
                                               _ptr(q), _ptr(k8), _ptr(v8), float(k_scale),
                                               float(v_scale), _ptr(idx), _ptr(out), out_dtype,
                                               None, 0, _stream(stream)))
+
+
+def hs2_decode_select_fp8(dims: Dims, cache: VarlenArgs, q, k8, k_scale: float, idx_out,
+                          kth_score_out=None, workspace=None, stream=None) -> None:
+    """hs2_decode_select over an FP8 key cache: k = k_scale * E4M3(k8)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().hs2_decode_select_fp8(
+        ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(k8), float(k_scale),
+        _ptr(idx_out), _ptr(kth_score_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def hs2_decode_sparse_attn_fp8(dims: Dims, cache: VarlenArgs, q, k8, v8, k_scale: float,

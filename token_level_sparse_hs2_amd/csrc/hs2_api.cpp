@@ -492,19 +492,26 @@ int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
   return HS2_OK;
 }
 
-int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
-                      int32_t* idx_out, float* kth_score_out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode selection; k8 set: the keys are an FP8 cache of scale k_scale
+int run_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
+                      const uint8_t* k8, float k_scale, int32_t* idx_out, float* kth_score_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   DecodeGeometry dg;
   int st = validate_decode(dims, cache, &dg);
   if (st != HS2_OK) return st;
+  if (k8 && check_fp8(k8, k8, k_scale, 1.f) != HS2_OK) return HS2_ERR_INVALID_ARG;
   if (dg.geo.B == 0) return HS2_OK;
-  if (!q || !k || !idx_out) return HS2_ERR_INVALID_ARG;
+  if (!q || !(k || k8) || !idx_out) return HS2_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < dg.bytes) return HS2_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);
   hs2::DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
+  p.k8 = k8;
   p.cu = cache->cu_seqlens;
   p.B = cache->batch;
   p.Hq = dims->num_q_heads;
@@ -515,7 +522,7 @@ int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
   p.T = dg.geo.T;
   p.n_split = dg.n_split;
   p.bitmap_words = dg.bitmap_words;
-  p.c = scale_log2(dims);
+  p.c = scale_log2(dims) * (k8 ? k_scale : 1.f);
   p.z2 = reinterpret_cast<float*>(w + dg.off_z2);
   p.part = reinterpret_cast<float2*>(w + dg.off_part);
   p.dense = reinterpret_cast<uint32_t*>(w + dg.off_dense);
@@ -527,6 +534,24 @@ int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
   e = hs2::launch_decode_select(dg.geo.G, p, dg.lds, s);
   if (e != hipSuccess) return hip_fail(e, "decode select kernel");
   return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs2_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void* q, const void* k,
+                      int32_t* idx_out, float* kth_score_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return run_decode_select(dims, cache, q, k, nullptr, 1.f, idx_out, kth_score_out, workspace,
+                           workspace_bytes, stream);
+}
+
+int hs2_decode_select_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                          const uint8_t* k8, float k_scale, int32_t* idx_out, float* kth_score_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return run_decode_select(dims, cache, q, nullptr, k8, k_scale, idx_out, kth_score_out,
+                           workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -34,6 +34,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Two E4M3 codes (bytes 2 HI, 2 HI + 1 of x) -> two bf16 in a word, at scale 1:
+// exact, every E4M3 value being a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, HI));
+}
+
 __device__ __forceinline__ uint2 ldg64(const void* p) {
   return *reinterpret_cast<const uint2*>(p);
 }

@@ -162,6 +162,7 @@ constexpr int kDecodeCandCap = 4096;  // candidates ranked in LDS per decode row
 struct DecodeParams {
   const uint16_t* q;    // [B, Hq, 128]
   const uint16_t* k;    // [T, Hkv, 128] cache
+  const uint8_t* k8;    // or an FP8 key cache (E4M3 codes; the scale is folded into c)
   const int32_t* cu;    // [B+1] cache offsets
   int B, Hq, Hkv, K, W;
   int max_seqlen;

@@ -723,7 +723,7 @@ __device__ __forceinline__ void merge_max_sum(float& m, float& s, float m2, floa
   m = mn;
 }
 
-template <int G>
+template <int G, bool FP8>
 __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
   __shared__ float2 red[4][16];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -752,22 +752,34 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
   float m[4], sm[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) { m[i] = -INFINITY; sm[i] = 0.f; }
-  const uint16_t* kg = p.k + ((size_t)base * Hkv + g) * kHeadDim;
-  const size_t kstride = (size_t)Hkv * kHeadDim;
-  // B operand: key jt + lc (clamped to the split; masked below), d = 32 ks + 8 lq.
+  const size_t kstride = (size_t)Hkv * kHeadDim;  // elements per cached token
+  const size_t kbase = ((size_t)base * Hkv + g) * kHeadDim;
+  // B operand: key jt + lc (clamped to the split; masked below), d = 32 ks + 8 lq:
+  // 16 bytes of a bf16 row, or 8 bytes of an FP8 one widened exactly to bf16.
   // The next step's rows are in flight while this step computes (the loads are
   // unconditional, clamped, so the compiler's wait leaves them in flight).
-  auto load_keys = [&](int jt, u32x4 (&kv)[4]) {
-    const int j = min(jt + lc, j1 - 1);
+  using Raw = std::conditional_t<FP8, uint2, uint4>;
+  auto load_keys = [&](int jt, Raw (&kv)[4]) {
+    const size_t row = kbase + (size_t)min(jt + lc, j1 - 1) * kstride;
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) kv[ks] = to_u32x4(ldg128(kg + (size_t)j * kstride + 32 * ks + 8 * lq));
+    for (int ks = 0; ks < 4; ks++) {
+      if constexpr (FP8) kv[ks] = ldg64(p.k8 + row + 32 * ks + 8 * lq);
+      else kv[ks] = ldg128(p.k + row + 32 * ks + 8 * lq);
+    }
   };
-  u32x4 kn[4];
+  auto widen = [&](const Raw& x) HS2_INLINE -> u32x4 {
+    if constexpr (FP8)
+      return u32x4{e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
+                   e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y)};
+    else
+      return to_u32x4(x);
+  };
+  Raw kn[4];
   load_keys(j0 + 16 * w, kn);
   for (int jt = j0 + 16 * w; jt < j1; jt += 64) {
     u32x4 kv[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) kv[ks] = kn[ks];
+    for (int ks = 0; ks < 4; ks++) kv[ks] = widen(kn[ks]);
     load_keys(jt + 64, kn);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -807,18 +819,23 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
   }
 }
 
-hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s) {
+template <bool FP8>
+static hipError_t launch_decode_logits_t(int G, const DecodeParams& p, hipStream_t s) {
   if (p.B <= 0) return hipSuccess;
   const dim3 grid(p.n_split, p.Hkv, p.B), block(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL(decode_logits_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(decode_logits_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(decode_logits_kernel<4>, grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(decode_logits_kernel<8>, grid, block, 0, s, p); break;
-    case 16: hipLaunchKernelGGL(decode_logits_kernel<16>, grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_logits_kernel<1, FP8>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_logits_kernel<2, FP8>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_logits_kernel<4, FP8>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_logits_kernel<8, FP8>), grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((decode_logits_kernel<16, FP8>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s) {
+  return p.k8 ? launch_decode_logits_t<true>(G, p, s) : launch_decode_logits_t<false>(G, p, s);
 }
 
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s) {

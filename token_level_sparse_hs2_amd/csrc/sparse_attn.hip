@@ -35,12 +35,6 @@ namespace hs2 {
 constexpr int kChunk = 32;  // index entries per step
 constexpr int kMaxParts = 32;  // partials merged per row (split rows of a decode step)
 
-// Two E4M3 codes (bytes 2 HI, 2 HI + 1 of x) -> two bf16 in a word.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, HI));
-}
-
 template <int G, bool PRECISE, bool FP8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   __shared__ uint4 klds[4][kChunk][16];  // per wave: 32 K rows x 256 B, swizzled 16-byte chunks
