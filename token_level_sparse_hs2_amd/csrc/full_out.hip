@@ -30,15 +30,10 @@ namespace hs2 {
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kOutRT = 2;                  // 16-row tiles per wave
 constexpr int kOutRowsW = 16 * kOutRT;     // MFMA rows per wave
 constexpr int kOutSlots = 2;               // ring depth (K and V each)
 
-__device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 struct OutSmem {
   uint4 k[kOutSlots][kKeyTile][16];  // K rows: chunk c of key r at c ^ (r & 15)

@@ -44,6 +44,13 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
 __device__ __forceinline__ uint2 ldg64(const void* p) {
   return *reinterpret_cast<const uint2*>(p);
 }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// v_mfma_f32_16x16x16_bf16: A lane l = row l & 15, k = 4 (l >> 4) .. +3; B lane l =
+// column l & 15, same k; C as for 16x16x32
+__device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint4 ldg128(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

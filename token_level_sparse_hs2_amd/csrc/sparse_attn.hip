@@ -32,13 +32,18 @@
 
 namespace hs2 {
 
-constexpr int kChunk = 32;  // index entries per step
 constexpr int kMaxParts = 32;  // partials merged per row (split rows of a decode step)
 
-template <int G, bool PRECISE, bool FP8>
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
-  __shared__ uint4 klds[4][kChunk][16];  // per wave: 32 K rows x 256 B, swizzled 16-byte chunks
-  __shared__ uint4 vlds[4][kChunk][16];  // per wave: 32 V rows
+// CH index entries per step: 32 for a bf16 cache; 16 for an FP8 one, which halves
+// the LDS slice and the staging registers so that four waves per SIMD fit (measured
+// 5% faster there; a bf16 cache at 16 entries and three waves was 1.6% slower).
+// MT = CH / 16 key tiles per step.
+template <int G, bool PRECISE, bool FP8, int CH>
+__global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn_kernel(
+    SparseParams p) {
+  constexpr int MT = CH / 16, NR = CH / 4;
+  __shared__ uint4 klds[4][CH][16];  // per wave: CH K rows x 256 B, swizzled 16-byte chunks
+  __shared__ uint4 vlds[4][CH][16];  // per wave: CH V rows
   // the wave index is uniform: row, sequence and K/V row pointers live in SGPRs,
   // so the gathers take a scalar base and a 32-bit lane offset
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
@@ -86,24 +91,23 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   vseq += ((size_t)base * Hkv + g) * kHeadDim * kElemBytes;
   const uint32_t row_stride = (uint32_t)Hkv * kHeadDim * kElemBytes;
   uint4(*vl)[16] = vlds[w];
-  const int n_chunks = (KW + kChunk - 1) / kChunk;
+  const int n_chunks = (KW + CH - 1) / CH;
   // this wave's steps: all of them, or its part's share
   const int per_part = (n_chunks + p.n_part - 1) / p.n_part;
   const int c_begin = part * per_part, c_end = min(n_chunks, c_begin + per_part);
 
-  // index entries of chunk c for the lane's two A rows (keys 16*mt + lc)
-  // Index entries of chunk c for the lane's two A rows (keys 16*mt + lc). The raw
+  // Index entries of chunk c for the lane's MT A rows (keys 16*mt + lc). The raw
   // load is unconditional (clamped to a valid entry) and its value is only used
   // two chunks later by valid_idx(); loads skipped on some path, or consumed at
   // once, would make the compiler drain the gather in flight behind them.
-  auto load_raw = [&](int c, int (&r)[2]) {
+  auto load_raw = [&](int c, int (&r)[MT]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) r[mt] = irow[min(c * kChunk + 16 * mt + lc, KW - 1)];
+    for (int mt = 0; mt < MT; mt++) r[mt] = irow[min(c * CH + 16 * mt + lc, KW - 1)];
   };
-  auto valid_idx = [&](int c, const int (&r)[2], int (&j)[2]) {
+  auto valid_idx = [&](int c, const int (&r)[MT], int (&j)[MT]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      const int e = c * kChunk + 16 * mt + lc;
+    for (int mt = 0; mt < MT; mt++) {
+      const int e = c * CH + 16 * mt + lc;
       j[mt] = (c < c_end && e < KW) ? r[mt] : -1;
     }
   };
@@ -112,17 +116,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   // 16 bytes of a bf16 row, 8 bytes of an FP8 one)
   using Piece = std::conditional_t<FP8, uint2, uint4>;
   struct Gather {
-    Piece kr[8];
-    Piece vr[8];
+    Piece kr[NR];
+    Piece vr[NR];
   };
-  auto gather = [&](const int (&j)[2], Gather& gb) {
-    // byte offset of the row of each of the lane's two entries (row 0 if invalid)
-    int roff[2];
+  auto gather = [&](const int (&j)[MT], Gather& gb) {
+    // byte offset of the row of each of the lane's entries (row 0 if invalid)
+    int roff[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < MT; mt++)
       roff[mt] = (int)((uint32_t)(j[mt] >= 0 && j[mt] <= t ? j[mt] : 0) * row_stride);
 #pragma unroll
-    for (int r = 0; r < 8; r++) {
+    for (int r = 0; r < NR; r++) {
       const int key = 4 * r + lq;  // entry of the chunk; its offset is held by lane (key & 15)
       const uint32_t off =
           (uint32_t)__shfl(roff[key >> 4], key & 15, 64) + (8u * kElemBytes) * lc;
@@ -148,25 +152,30 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
   constexpr int NSPLIT = PRECISE ? 3 : 2;
   constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
 
-  auto consume = [&](const int (&j)[2], const Gather& gb) {
-    const bool ok0 = j[0] >= 0 && j[0] <= t, ok1 = j[1] >= 0 && j[1] <= t;
-    const uint64_t bal0 = __ballot(ok0), bal1 = __ballot(ok1);
-    if ((bal0 | bal1) == 0) return;
-    const bool full = (bal0 & bal1) == ~0ull;
+  auto consume = [&](const int (&j)[MT], const Gather& gb) {
+    uint64_t bal[MT], any = 0, all = ~0ull;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      bal[mt] = __ballot(j[mt] >= 0 && j[mt] <= t);
+      any |= bal[mt];
+      all &= bal[mt];
+    }
+    if (any == 0) return;
+    const bool full = all == ~0ull;
     wave_lds_fence();  // previous chunk's reads of kl / vl are done
     // rows into LDS. K: 16-byte chunk ch of key r at physical chunk ch ^ (r & 15);
     // V: at ch ^ (2 * (r & 7)) (suits the transposing reads below)
 #pragma unroll
-    for (int r = 0; r < 8; r++) {
+    for (int r = 0; r < NR; r++) {
       const int key = 4 * r + lq;
       kl[key][lc ^ (key & 15)] = widen(gb.kr[r]);
       vl[key][lc ^ (2 * (key & 7))] = widen(gb.vr[r]);
     }
     wave_lds_fence();
     // raw scores S^T (keys x heads); lane: head lc, keys 16*mt + 4*lq + i
-    f32x4 s[2];
+    f32x4 s[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
+    for (int mt = 0; mt < MT; mt++) {
       s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int key = 16 * mt + lc;
 #pragma unroll
@@ -177,15 +186,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
     }
     if (!full) {  // entry 16*mt + 4*lq + i is valid iff bit (4*lq + i) of the ballot
 #pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        const uint64_t bal = mt ? bal1 : bal0;
+      for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
         for (int i = 0; i < 4; i++)
-          if (!((bal >> (4 * lq + i)) & 1ull)) s[mt][i] = -INFINITY;
+          if (!((bal[mt] >> (4 * lq + i)) & 1ull)) s[mt][i] = -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+    if constexpr (MT == 2)
+      mx = fmaxf(mx, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = max_xor32(max_xor16(mx));
     mx *= c;  // finite: the chunk has a valid entry
     // the reference m only moves when a score passes it by the slack (never
@@ -198,10 +207,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
       for (int i = 0; i < 8; i++) o[i] *= alpha;
       m = m_new;
     }
-    float pv[8];
+    float pv[4 * MT];
     float psum = 0.f;
 #pragma unroll
-    for (int sidx = 0; sidx < 8; sidx++) {
+    for (int sidx = 0; sidx < 4 * MT; sidx++) {
       pv[sidx] = fast_exp2(fmaf(s[sidx >> 2][sidx & 3], c, -m));
       psum += pv[sidx];
     }
@@ -211,18 +220,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
     // P is split into bf16 parts p = p0 + p1 (+ p2 in the precise mode), each the
     // bf16 rounding of what the previous parts leave, so P.V keeps ~16 (~24)
     // mantissa bits of P; V is bf16 already, so every product is exact.
-    bf16x8 pb[NSPLIT];
+    // (MT = 1: 16x16x16 MFMA, k slot s <-> key 4lq + s.)
+    uint32_t pk[NSPLIT][2 * MT];
 #pragma unroll
     for (int part = 0; part < NSPLIT; part++) {
-      u32x4 pk;
 #pragma unroll
-      for (int u = 0; u < 4; u++) pk[u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
-      pb[part] = as_bf16x8(pk);
+      for (int u = 0; u < 2 * MT; u++) pk[part][u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
       if (part + 1 < NSPLIT) {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          pv[2 * u] -= bf16_bits_to_f32(pk[u] & 0xFFFFu);
-          pv[2 * u + 1] -= __uint_as_float(pk[u] & 0xFFFF0000u);
+        for (int u = 0; u < 2 * MT; u++) {
+          pv[2 * u] -= bf16_bits_to_f32(pk[part][u] & 0xFFFFu);
+          pv[2 * u + 1] -= __uint_as_float(pk[part][u] & 0xFFFF0000u);
         }
       }
     }
@@ -236,9 +244,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
       typedef short i16x4 __attribute__((ext_vector_type(4)));
-      uint2 hv[2];
+      uint2 hv[MT];
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
+      for (int h = 0; h < MT; h++) {
         const int key = 16 * h + key_lo;
         const int d0 = 16 * dt + dsub;
         const int phys = (d0 >> 3) ^ (2 * (key & 7));
@@ -246,17 +254,27 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseParams p) {
         hv[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                               (i16x4 __attribute__((address_space(3)))*)(src)));
       }
-      const u32x4 av = {hv[0].x, hv[0].y, hv[1].x, hv[1].y};
-      const bf16x8 va = as_bf16x8(av);
+      if constexpr (MT == 2) {
+        const bf16x8 va = as_bf16x8(u32x4{hv[0].x, hv[0].y, hv[1].x, hv[1].y});
 #pragma unroll
-      for (int part = 0; part < NSPLIT; part++) o[dt] = mfma16x16x32(va, pb[part], o[dt]);
+        for (int part = 0; part < NSPLIT; part++)
+          o[dt] = mfma16x16x32(va, as_bf16x8(u32x4{pk[part][0], pk[part][1], pk[part][2],
+                                                   pk[part][3]}),
+                               o[dt]);
+      } else {
+        const s16x4 va = __builtin_bit_cast(s16x4, hv[0]);
+#pragma unroll
+        for (int part = 0; part < NSPLIT; part++)
+          o[dt] = mfma16x16x16(va, __builtin_bit_cast(s16x4, make_uint2(pk[part][0], pk[part][1])),
+                               o[dt]);
+      }
     }
   };
 
   // software pipeline: while chunk c computes, the gather of chunk c+1 and the
   // index entries of chunks c+2 and c+3 are in flight. Entries past the row are
   // -1: their gathers read row 0 and are skipped.
-  int r1[2], r2[2], ja[2], jb[2];
+  int r1[MT], r2[MT], ja[MT], jb[MT];
   Gather ga, gb;
   load_raw(c_begin, ja);
   load_raw(c_begin + 1, r1);
@@ -359,11 +377,11 @@ static hipError_t launch_sparse_g(bool precise, bool fp8, const SparseParams& p,
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
   if (fp8) {
-    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, true>), grid, block, 0, s, p);
+    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, true, 16>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, true, 16>), grid, block, 0, s, p);
   } else {
-    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, false>), grid, block, 0, s, p);
+    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, false, 32>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, false, 32>), grid, block, 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_part <= 1) return e;
