@@ -39,6 +39,7 @@ struct Geometry {
   size_t select_bytes = 0;
   size_t exact_lds = 0;
   int topk_rows_per_block = 4;
+  int sbuf_words = 0;
   bool exact_only = false;  // K above the register-ranked limit: every row takes the exact path
   int block = 0;            // block selection: tokens per block
 };
@@ -128,7 +129,10 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   geo->exact_lds =
       (hs2::kTopkBins + 16 + 2 * (size_t)geo->bitmap_words + 16 * hs2::kHeadDim) * sizeof(uint32_t);
   // top-K waves: a 256-bin histogram and one bitmap each; up to 4 waves per block
-  const size_t per_wave = (256 + (size_t)geo->bitmap_words) * sizeof(uint32_t);
+  // a 256-bin histogram, a bitmap and the staging of the selected positions
+  geo->sbuf_words = std::min(d->top_k, hs2::kMaxRankedK);
+  const size_t per_wave =
+      (256 + (size_t)geo->bitmap_words + (size_t)geo->sbuf_words) * sizeof(uint32_t);
   geo->topk_rows_per_block = (int)std::max<size_t>(1, std::min<size_t>(4, 40960 / per_wave));
   return HS2_OK;
 }
@@ -247,6 +251,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.block = geo.block;
   tp.cand_cap = geo.cand_cap;
   tp.bitmap_words = geo.bitmap_words;
+  tp.sbuf_words = geo.sbuf_words;
   tp.c = sp.c;
   tp.cand = cand;
   tp.cand_count = count;

@@ -115,6 +115,7 @@ struct TopkParams {
   int block;            // 0, or kBlockTokens: candidates are (block score, block index)
   int cand_cap;
   int bitmap_words;     // words per bitmap in LDS (covers max_seqlen)
+  int sbuf_words;       // per-wave LDS staging of the selected positions (min(K, kMaxRankedK))
   float c;
   const uint64_t* cand;
   const int32_t* cand_count;

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   extern __shared__ uint32_t smem[];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int waves = blockDim.x >> 6;
-  uint32_t* hist = smem + (size_t)w * (256 + p.bitmap_words);
+  uint32_t* hist = smem + (size_t)w * (256 + p.bitmap_words + p.sbuf_words);
   uint32_t* bm = hist + 256;
   const int64_t slot = (int64_t)blockIdx.x * waves + w;
   if (slot >= p.n_rows) return;
@@ -419,14 +419,24 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   const int incl = wave_incl_scan(cnt, l);
   const int base = __shfl(incl, 63, 64);  // number of selected positions (K_t)
   int off = incl - cnt;
+  // Each lane's positions form a contiguous run of the row: they go to the wave's
+  // LDS staging first and leave in coalesced stores (written straight from each
+  // lane, 64 runs would scatter every store instruction over ~36 cache lines).
+  uint32_t* sbuf = bm + p.bitmap_words;
+  const bool stage = base <= p.sbuf_words;  // wave-uniform
   for (int i = wb; i < we; i++) {
     uint32_t mm = bm[i];
     while (mm) {
       const int b = __ffs(mm) - 1;
       mm &= mm - 1;
-      if (off < KW) row[off] = i * 32 + b;
+      if (stage) sbuf[off] = (uint32_t)(i * 32 + b);
+      else if (off < KW) row[off] = i * 32 + b;
       off++;
     }
+  }
+  if (stage) {
+    wave_lds_fence();
+    for (int o = l; o < base; o += 64) row[o] = (int32_t)sbuf[o];
   }
   for (int j = n_c + l; j <= r.t; j += 64) {
     const int o = base + (j - n_c);
@@ -640,7 +650,8 @@ hipError_t launch_decode_select(int G, const DecodeParams& p, size_t lds_bytes, 
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s) {
   (void)G;
   if (n_rows <= 0) return hipSuccess;
-  const size_t lds = (size_t)rows_per_block * (256 + p.bitmap_words) * sizeof(uint32_t);
+  const size_t lds =
+      (size_t)rows_per_block * (256 + p.bitmap_words + p.sbuf_words) * sizeof(uint32_t);
   const dim3 grid((n_rows + rows_per_block - 1) / rows_per_block), block(64 * rows_per_block);
   const int nreg = p.cand_cap / 64;
   if (nreg <= 32) {
