@@ -104,8 +104,8 @@ def main():
                     help="also run a 1 GiB device-to-device copy (known bytes) for counter scaling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the work shards by KV group with no exchange; see the design notes).",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the work would shard by KV group, with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -4,7 +4,7 @@
  * smoke check and the benchmark's CPU-baseline leg may load this library; the
  * GPU library never calls it and shares no code with it.
  *
- * What it computes (sources are the pages this build is written from):
+ * What it computes (each point cites the page it follows):
  *  - A hybrid module is one full-attention layer followed by sparse layers that
  *    reuse the full layer's KV cache and its token-selection result
  *    ("KV Reuse"; HySparse2 news summary of the MiMo-V3 architecture, the

@@ -2,14 +2,14 @@
 //
 // Each sparse layer of a hybrid module reuses the full layer's KV cache and its
 // token selection (HySparse2 news summary, KV Reuse paragraph; token-granularity
-// paragraph: "subsequent sparse layers keep reusing these positions and their
-// cache"), with its own queries. Attention over a subset is the softmax with
+// paragraph: the later sparse layers go on using the same positions and cache),
+// with its own queries. Attention over a subset is the softmax with
 // every other logit at -inf, i.e. renormalised over the subset (SHARP
 // walkthrough, section 2.3):
 //   o[t,h] = sum_{j in I_t} exp(y_j - mu) v[j,g] / sum_{j in I_t} exp(y_j - mu),
 //   y_j = scale * <q'[t,h], k[j,g]>, g = h / G.
 //
-// One wavefront per (token, KV group), 32 index entries per step: the step's K
+// One wavefront per (token, KV group), CH index entries per step: the step's K
 // and V rows are gathered with full-row coalesced loads (16 lanes per 256-byte
 // row) into registers one step ahead, staged in the wave's LDS slice, and read
 // back as the A operands of S^T = K_sel Q'^T (keys x heads; all G heads of the
