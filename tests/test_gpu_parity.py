@@ -99,6 +99,16 @@ def test_ragged_varlen_every_group_size(G):
     run_case(w)
 
 
+@pytest.mark.parametrize("K,W", [(0, 32), (256, 0), (1, 1), (3000, 16), (6000, 64)])
+def test_budget_edges(K, W):
+    """K = 0 (the window only), W = 0 (no window), K = W = 1, K above the
+    register-ranked limit (every ranked row takes the exact path) and K + W above
+    every length (all causal keys: dense)."""
+    w = synthgen.custom([1, 2, 33, 700, 2100, 4500], Hq=8, Hkv=2, K=K, W=W, n_sparse=1,
+                        seed=170 + K % 97 + W)
+    run_case(w)
+
+
 def test_exact_flag_path():
     import token_level_sparse_hs2_amd as hs2
     w = synthgen.custom([300, 5000], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=77)
