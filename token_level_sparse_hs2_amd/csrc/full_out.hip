@@ -4,12 +4,12 @@
 // summary, two-level KV sharing paragraph: the full-attention layers keep their
 // own projections and outputs; its scores also pick the sparse layers' tokens):
 //   o[t,h] = sum_{j <= t} P[t,h,j] v[j,g],  P = softmax_j(scale <q[t,h], k[j,g]>)
-// (attention as in the SHARP walkthrough, section 1.1). The selection's first
-// sweep already produced each row's log2-domain log-sum-exp lse2, so here
-// P = exp2(c q.k - lse2) is known outright: a single sweep over the causal keys
-// with no running maximum and no rescaling. The output is still divided by the
-// sum of the P values it accumulated (~1), which cancels the fp32 rounding of
-// lse2 itself.
+// (attention as in the SHARP walkthrough, section 1.1). One sweep over the causal
+// keys with a running maximum per row (log2 domain, moved lazily: only when a
+// 64-key tile passes it by 2^8, which rescales the row's sum and output), and
+// the row's log2-domain log-sum-exp lse2 = m + log2(sum) written as a by-product:
+// the selection then takes its row statistics from here and skips its own
+// statistics sweep, so the full layer's output costs one QK^T pass, not two.
 //
 // One workgroup owns TOK tokens of one sequence and one KV group: 4 wavefronts
 // x 32 MFMA rows (token-major, head-minor). Each 64-key tile of K and of V
@@ -17,7 +17,7 @@
 // XOR-swizzled by which chunk each lane fetches). Per wave and tile:
 //   S^T = K Q^T (keys x rows), v_mfma_f32_16x16x32_bf16, A = K from LDS, B = Q
 //   in registers;
-//   P^T = exp2(c S^T - lse2) in the accumulator layout, which is the B-operand
+//   P^T = exp2(c S^T - m) in the accumulator layout, which is the B-operand
 //   layout of v_mfma_f32_16x16x16_bf16;
 //   O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16).
 // P enters as one bf16 part for bf16 output and three (~24 bits) for fp32.
@@ -59,10 +59,9 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
   const int Hq = p.Hq, Hkv = p.Hkv;
   const float c = p.c;
 
-  // B operand Q^T: column = row (lc) of row tile rt, k = d chunk 4 ks + lq; and the
-  // row's lse2 (+inf for rows past the sequence: P = 0 there)
+  // B operand Q^T: column = row (lc) of row tile rt, k = d chunk 4 ks + lq (rows
+  // past the sequence take zero queries and are not written)
   bf16x8 qb[kOutRT][4];
-  float lse[kOutRT];
   {
     u32x4 v[kOutRT][4];
 #pragma unroll
@@ -73,14 +72,12 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
       for (int ks = 0; ks < 4; ks++)
         v[rt][ks] = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
                                     32 * ks + 8 * lq));
-      lse[rt] = p.lse2[(size_t)(base + t0 + ta) * Hq + g * G + ha];
     }
 #pragma unroll
     for (int rt = 0; rt < kOutRT; rt++) {
       const bool live = (w * kOutRowsW + 16 * rt + lc) / G < ntok;
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) qb[rt][ks] = as_bf16x8(live ? v[rt][ks] : u32x4{0u, 0u, 0u, 0u});
-      if (!live) lse[rt] = INFINITY;
     }
   }
 
@@ -110,8 +107,10 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
+  constexpr float kRescaleSlack = 8.f;  // log2 units the running maximum may lag behind
   f32x4 o[8][kOutRT];
   float lsum[kOutRT] = {};
+  float m[kOutRT] = {};  // set from the first tile
 #pragma unroll
   for (int dt = 0; dt < 8; dt++)
 #pragma unroll
@@ -126,26 +125,62 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
     lds_barrier();
     if (kt + 1 < n_kt) dma_tile(kt + 1, buf ^ 1);
     const bool diag = kt * kKeyTile + kKeyTile - 1 > t0;
+    // S^T of the tile's four 16-key subtiles (keys 16 kk + 4 lq + i, row lc of each
+    // row tile) in the log2 domain relative to the row's running maximum m:
+    // z = c S - m (keys past a row's token at -inf)
+    f32x4 z[4][kOutRT];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) {  // 16-key subtiles
-      // S^T for keys 16 kk + 4 lq + i, rows lc of each row tile
-      const int kr = 16 * kk + lc;     // A operand row (key) of this lane
+    for (int kk = 0; kk < 4; kk++) {
+      const int kr = 16 * kk + lc;  // A operand row (key) of this lane
       bf16x8 ka[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) ka[ks] = as_bf16x8(to_u32x4(sm.k[buf][kr][(4 * ks + lq) ^ (kr & 15)]));
+#pragma unroll
+      for (int rt = 0; rt < kOutRT; rt++) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) acc = mfma16x16x32(ka[ks], qb[rt][ks], acc);
+        const int t = t0 + (w * kOutRowsW + 16 * rt + lc) / G;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          z[kk][rt][i] = fmaf(acc[i], c, -m[rt]);
+          if (diag && kt * kKeyTile + 16 * kk + 4 * lq + i > t) z[kk][rt][i] = -INFINITY;
+        }
+      }
+    }
+    // the row's maximum over the tile relative to m (16 values per lane, then its 4
+    // lane groups). The first tile sets m to the row's exact maximum there (key 0 is
+    // in it for every row, so that is finite); later tiles move m only when a score
+    // passes it by the slack, rescaling the row's sum and output.
+#pragma unroll
+    for (int rt = 0; rt < kOutRT; rt++) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++)
+        mx = fmaxf(mx, fmaxf(fmaxf(z[kk][rt][0], z[kk][rt][1]), fmaxf(z[kk][rt][2], z[kk][rt][3])));
+      mx = max_xor32(max_xor16(mx));
+      const bool first = kt == 0;
+      if (first || __any(mx > kRescaleSlack)) {
+        const float dm = first ? mx : fmaxf(mx, 0.f);
+        if (!first) {
+          const float alpha = fast_exp2(-dm);
+          lsum[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; dt++) o[dt][rt] *= alpha;
+        }
+        m[rt] += dm;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) z[kk][rt] -= dm;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {  // 16-key subtiles
       s16x4 pb[kOutRT][NSPLIT];
 #pragma unroll
       for (int rt = 0; rt < kOutRT; rt++) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) s = mfma16x16x32(ka[ks], qb[rt][ks], s);
-        const int t = t0 + (w * kOutRowsW + 16 * rt + lc) / G;
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          pv[i] = fast_exp2(fmaf(s[i], c, -lse[rt]));
-          if (diag && kt * kKeyTile + 16 * kk + 4 * lq + i > t) pv[i] = 0.f;
-        }
+        for (int i = 0; i < 4; i++) pv[i] = fast_exp2(z[kk][rt][i]);
         lsum[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
 #pragma unroll
         for (int part = 0; part < NSPLIT; part++) {
@@ -188,6 +223,10 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) o[dt][rt] *= inv;
+    // the row's log2-domain log-sum-exp, for the selection
+    const int row = w * kOutRowsW + 16 * rt + lc;
+    if (p.lse2 && lq == 0 && row / G < ntok)
+      p.lse2[(size_t)(base + t0 + row / G) * Hq + g * G + row % G] = m[rt] + fast_log2(ls);
   }
 #pragma unroll
   for (int rt = 0; rt < kOutRT; rt++) {

@@ -198,7 +198,8 @@ float scale_log2(const hs2_dims* d) { return d->softmax_scale * 1.44269504088896
 
 int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
                const void* k, int32_t* idx_out, float* kth_out, void* ws, hipStream_t s,
-               const void* vv = nullptr, float oam_beta = 0.f, int k_end = -1) {
+               const void* vv = nullptr, float oam_beta = 0.f, int k_end = -1,
+               bool lse_given = false) {
   if (geo.T == 0) return HS2_OK;
   if (k_end < 0) k_end = d->top_k;  // no decay
   char* w = static_cast<char*>(ws);
@@ -232,6 +233,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.flags = d->flags | (geo.exact_only ? (uint32_t)HS2_FLAG_EXACT_SELECT : 0u);
   sp.block = geo.block;
   sp.lse2 = lse2;
+  sp.lse_given = lse_given ? 1 : 0;
   sp.cand = cand;
   sp.cand_count = count;
   sp.flag_list = flags;
@@ -265,8 +267,11 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.idx = idx_out;
   tp.kth = kth_out;
 
-  hipError_t ek = hs2::launch_key_norms(sp.k, v->cu_seqlens, v->batch, d->num_kv_heads, geo.T, kmax, s);
-  if (ek != hipSuccess) return hip_fail(ek, "key norm kernel");
+  hipError_t ek = hipSuccess;
+  if (!lse_given) {  // the statistics sweep's reference needs the key norms
+    ek = hs2::launch_key_norms(sp.k, v->cu_seqlens, v->batch, d->num_kv_heads, geo.T, kmax, s);
+    if (ek != hipSuccess) return hip_fail(ek, "key norm kernel");
+  }
   if (oam_beta > 0.f) {
     float* vw = reinterpret_cast<float*>(w + geo.off_vw);
     uint32_t* vwmax = reinterpret_cast<uint32_t*>(w + geo.off_vwmax);
@@ -474,8 +479,8 @@ int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
   st = check_workspace(geo, workspace, workspace_bytes);
   if (st != HS2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace, s);
-  if (st != HS2_OK) return st;
+  // the output sweep first: it also writes every row's log-sum-exp, which the
+  // selection then takes instead of running its own statistics sweep
   const int tok = hs2::full_out_tokens(geo.G);
   int64_t n_tasks = 0;
   for (int i = 0; i < varlen->batch; i++)
@@ -490,11 +495,12 @@ int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
   p.Hkv = dims->num_kv_heads;
   p.max_tiles = std::max(1, hs2::ceil_div(geo.max_len, tok));
   p.c = scale_log2(dims);
-  p.lse2 = reinterpret_cast<const float*>(static_cast<char*>(workspace) + geo.off_lse);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.off_lse);
   p.out = out_full;
   hipError_t e = hs2::launch_full_out(geo.G, out_dtype == HS2_OUT_F32, p, n_tasks, s);
   if (e != hipSuccess) return hip_fail(e, "full-layer output kernel");
-  return HS2_OK;
+  return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace, s, nullptr, 0.f, -1,
+                    true);
 }
 
 }  // extern "C"

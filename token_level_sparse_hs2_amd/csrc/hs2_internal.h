@@ -98,6 +98,7 @@ struct ScoreParams {
   const float* vw;      // [T, Hkv] log2 key weights beta * max(0, log2 |v|), or null (plain score)
   const uint32_t* vwmax;  // [B * Hkv] largest weight of each (sequence, group), float bits
   float* lse2;          // [T, Hq] log2-domain log-sum-exp of each full-layer row
+  int lse_given;        // 1: lse2 holds the rows' statistics already (no statistics sweep)
   uint64_t* cand;       // [chunk rows, C]: (S bits << 32) | position
   int32_t* cand_count;  // [chunk rows]: count, or -1 = exact path
   int32_t* flag_list;   // [chunk rows]: slots sent to the exact path
@@ -189,7 +190,7 @@ struct FullOutParams {
   int B, Hq, Hkv;
   int max_tiles;        // tiles of full_out_tokens(G) tokens in the longest sequence
   float c;              // softmax_scale * log2(e)
-  const float* lse2;    // [T, Hq] from the selection's statistics sweep
+  float* lse2;          // [T, Hq] out: log2-domain log-sum-exp of every row (nullable)
   void* out;            // [T, Hq, 128] bf16 or f32
 };
 

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
       qv[rt][ks] = to_u32x4(ldg128(p.q + ((size_t)(base + t0 + ta) * Hq + g * G + ha) * kHeadDim +
                                    32 * ks + 8 * lq));
   }
-  const float kmax = __uint_as_float(p.kmax[seq * Hkv + g]);
+  const float kmax = p.lse_given ? 0.f : __uint_as_float(p.kmax[seq * Hkv + g]);
 #pragma unroll
   for (int rt = 0; rt < RT; rt++) {
     const int ra = w * ROWS_W + 16 * rt + lc;
@@ -398,66 +398,79 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
         lsum[rt][i] = s;
       }
   };
-  sum_sweep();
-  {
-    bool bad = false;
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) bad |= (row_of(rt, i) / G < ntok) && !(lsum[rt][i] >= 0x1p-60f);
-    if (tid == 0) sm.unsafe = 0;
+  if (p.lse_given) {
+    // the row statistics come with the call (the full layer's output sweep wrote
+    // them): rref = lse2 / c, so exp2(c * acc) is the full layer's probability.
+    // The bound-based references written above must land first.
     __syncthreads();
-    if (bad) sm.unsafe = 1;
-    __syncthreads();
-  }
-  if (sm.unsafe) {
-    // the bound is too loose for some row: rref <- the row's exact maximum of
-    // q . k_j, then the sum again
-    float mx[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) mx[rt][i] = -INFINITY;
-    sweep(n_kt1, 0, 1, kend1, Ring{}, false, [&](int kt, int buf) HS2_INLINE {
-      compute(buf);
-      mask_causal(kt);
-#pragma unroll
-      for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          mx[rt][i] = fmaxf(mx[rt][i], fmaxf(fmaxf(acc[rt][0][i], acc[rt][1][i]),
-                                             fmaxf(acc[rt][2][i], acc[rt][3][i])));
-    });
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float m = mx[rt][i];
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
-        // acc held q . k - rref, so the new reference is rref + m
-        if (lc == 0) sm.nref[row_of(rt, i)] -= m;
-      }
-    sum_sweep();
-  }
-  // lse2 = c * rref + log2(lsum); from here on rref = lse2 / c, so that
-  // exp2(c * acc) is the full layer's probability
-  lds_barrier();
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) lsum[rt][i] = fmaf(-c, nref4[rt][i], fast_log2(lsum[rt][i]));
-  lds_barrier();
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int row = row_of(rt, i);
-      if (lc == 0) {
-        sm.nref[row] = -lsum[rt][i] / c;
-        if (row / G < ntok) p.lse2[(size_t)(base + t0 + row / G) * Hq + g * G + row % G] = lsum[rt][i];
-      }
+    for (int row = tid; row < 4 * ROWS_W; row += kSelThreads) {
+      const int tl = row / G;
+      sm.nref[row] =
+          tl < ntok ? -p.lse2[(size_t)(base + t0 + tl) * Hq + g * G + row % G] / c : 0.f;
     }
+    __syncthreads();
+  } else {
+    sum_sweep();
+    {
+      bool bad = false;
+  #pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+  #pragma unroll
+        for (int i = 0; i < 4; i++) bad |= (row_of(rt, i) / G < ntok) && !(lsum[rt][i] >= 0x1p-60f);
+      if (tid == 0) sm.unsafe = 0;
+      __syncthreads();
+      if (bad) sm.unsafe = 1;
+      __syncthreads();
+    }
+    if (sm.unsafe) {
+      // the bound is too loose for some row: rref <- the row's exact maximum of
+      // q . k_j, then the sum again
+      float mx[RT][4];
+  #pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+  #pragma unroll
+        for (int i = 0; i < 4; i++) mx[rt][i] = -INFINITY;
+      sweep(n_kt1, 0, 1, kend1, Ring{}, false, [&](int kt, int buf) HS2_INLINE {
+        compute(buf);
+        mask_causal(kt);
+  #pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+  #pragma unroll
+          for (int i = 0; i < 4; i++)
+            mx[rt][i] = fmaxf(mx[rt][i], fmaxf(fmaxf(acc[rt][0][i], acc[rt][1][i]),
+                                               fmaxf(acc[rt][2][i], acc[rt][3][i])));
+      });
+  #pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+  #pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float m = mx[rt][i];
+  #pragma unroll
+          for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+          // acc held q . k - rref, so the new reference is rref + m
+          if (lc == 0) sm.nref[row_of(rt, i)] -= m;
+        }
+      sum_sweep();
+    }
+    // lse2 = c * rref + log2(lsum); from here on rref = lse2 / c, so that
+    // exp2(c * acc) is the full layer's probability
+    lds_barrier();
+  #pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+  #pragma unroll
+      for (int i = 0; i < 4; i++) lsum[rt][i] = fmaf(-c, nref4[rt][i], fast_log2(lsum[rt][i]));
+    lds_barrier();
+  #pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+  #pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int row = row_of(rt, i);
+        if (lc == 0) {
+          sm.nref[row] = -lsum[rt][i] / c;
+          if (row / G < ntok) p.lse2[(size_t)(base + t0 + row / G) * Hq + g * G + row % G] = lsum[rt][i];
+        }
+      }
+  }
 
   // ===================== per-token selection mode ===========================
   const int cand_end = t0 + ntok - W;  // candidates of the last token are [0, cand_end)
