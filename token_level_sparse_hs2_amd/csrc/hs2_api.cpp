@@ -349,7 +349,7 @@ int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
 
 extern "C" {
 
-int hs2_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int hs2_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 const char* hs2_status_string(int status) {
   switch (status) {
