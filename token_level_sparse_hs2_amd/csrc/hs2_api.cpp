@@ -141,7 +141,8 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
 struct DecodeGeometry {
   Geometry geo;
   int n_split = 0, bitmap_words = 0;
-  size_t off_z2 = 0, off_part = 0, off_dense = 0, bytes = 0, lds = 0;
+  size_t off_z2 = 0, off_part = 0, off_dense = 0, off_lse = 0, off_tau = 0, off_npass = 0,
+         off_cand = 0, bytes = 0, lds = 0;
   // sparse layer: n_part waves per (sequence, group) row and their partials
   int n_part = 1;
   size_t off_po = 0, off_pml = 0, sparse_bytes = 0;
@@ -166,6 +167,15 @@ int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) 
   off = align_up(off + (size_t)v->batch * d->num_kv_heads * dg->n_split * g.G * 2 * sizeof(float));
   dg->off_dense = off;
   off = align_up(off + (size_t)v->batch * d->num_kv_heads * max_len * sizeof(uint32_t));
+  const size_t rows_kv = (size_t)v->batch * d->num_kv_heads;
+  dg->off_lse = off;
+  off = align_up(off + (size_t)v->batch * d->num_q_heads * sizeof(float));
+  dg->off_tau = off;
+  off = align_up(off + rows_kv * sizeof(uint32_t));
+  dg->off_npass = off;
+  off = align_up(off + rows_kv * sizeof(int32_t));
+  dg->off_cand = off;
+  off = align_up(off + rows_kv * 2 * hs2::kDecodeCandCap * sizeof(uint32_t));
   dg->bytes = off;
   // histogram, scratch words, two bitmaps of the row's candidates, compacted candidates
   dg->lds = (hs2::kTopkBins + 16 + 2 * (size_t)dg->bitmap_words + 2 * (size_t)hs2::kDecodeCandCap) *
@@ -537,6 +547,10 @@ int run_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
   p.z2 = reinterpret_cast<float*>(w + dg.off_z2);
   p.part = reinterpret_cast<float2*>(w + dg.off_part);
   p.dense = reinterpret_cast<uint32_t*>(w + dg.off_dense);
+  p.lse2 = reinterpret_cast<float*>(w + dg.off_lse);
+  p.tau = reinterpret_cast<uint32_t*>(w + dg.off_tau);
+  p.n_pass = reinterpret_cast<int32_t*>(w + dg.off_npass);
+  p.cand = reinterpret_cast<uint32_t*>(w + dg.off_cand);
   p.idx = idx_out;
   p.kth = kth_score_out;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -175,6 +175,10 @@ struct DecodeParams {
   float* z2;            // [Hkv, T, G]: c * q.k of every cached key and the group's heads
   float2* part;         // [B, Hkv, n_split, G]: per split (max, sum of exp2(z2 - max))
   uint32_t* dense;      // [B * Hkv, max_seqlen] S bits
+  float* lse2;          // [B * Hkv, G] log-sum-exp (log2 domain) of each head over the cache
+  uint32_t* tau;        // [B * Hkv] sampled threshold (S bits)
+  int32_t* n_pass;      // [B * Hkv] scores reaching tau
+  uint32_t* cand;       // [B * Hkv, 2, kDecodeCandCap] S bits, then positions, of those scores
   int32_t* idx;         // [B, Hkv, K+W]
   float* kth;           // [B, Hkv] or null
 };

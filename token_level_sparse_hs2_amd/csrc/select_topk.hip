@@ -509,113 +509,212 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode step, selection: one workgroup per (KV group, sequence). The split
-// partials give each head's log-sum-exp over all cached keys; S[j] for every
-// candidate j <= t - W (t = L_b - 1) goes to a scratch row. A threshold tau is
-// read off a 1-in-16 sample of the row (the sample's r-th largest value); if at
-// least K scores reach it, the top K all do, so only those (compacted into LDS)
-// go through the exact radix select; otherwise the whole row does. Either way
-// the result is the exact top K, ties to the lower position.
+// Decode step, selection: three launches per step, so that the pass over every
+// cached score runs on many workgroups instead of one per row.
+//  decode_tau_kernel (one workgroup per (KV group, sequence) row): each head's
+//    log-sum-exp over all cached keys, from the split partials, and a threshold
+//    tau, the r-th largest S of a 1-in-stride sample of the candidates
+//    j <= t - W (t = L_b - 1).
+//  decode_dense_kernel (a grid of chunks per row): S[j] of every candidate into
+//    a scratch row; the scores that reach tau are appended to the row's
+//    candidate list (one counter per row; slot order is arbitrary).
+//  decode_rank_kernel (one workgroup per row): if at least K and at most
+//    kDecodeCandCap scores reach tau, the top K all do, so only the list goes
+//    through the exact radix select; otherwise the whole scratch row does. The
+//    positions are marked in a bitmap, so the result is the exact top K, ties to
+//    the lower position, in whatever order the list was filled.
 // ---------------------------------------------------------------------------
-constexpr int kDecodeSampleStride = 16;
+constexpr int kDecodeSampleStride = 16;   // densest sampling
+constexpr int kDecodeSampleCap = 8192;    // sampled scores held in LDS
+
+// S bits of one candidate: the sum over the group's heads of exp2(z2 - lse2).
+template <int G>
+__device__ __forceinline__ uint32_t decode_score(const float (&z)[G], const float (&lse)[G]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; h++) sum += fast_exp2(z[h] - lse[h]);
+  return __float_as_uint(sum);
+}
+
+// candidates handled per thread and pass: enough independent loads in flight
+template <int G>
+constexpr int decode_batch() { return G >= 16 ? 2 : 32 / G; }
+
+// rows with nothing to rank: [0, t] (all candidates fit) or the window only
+__device__ __forceinline__ bool decode_trivial(const DecodeParams& p, int n_c) {
+  return p.K == 0 || n_c <= p.K;
+}
 
 template <int G>
-__global__ __launch_bounds__(kSelThreads) void decode_select_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kSelThreads) void decode_tau_kernel(DecodeParams p) {
   extern __shared__ uint32_t smem[];
-  __shared__ float lse_s[16];
-  TopkShared sh;
+  __shared__ float lse_s[G];
+  TopkShared sh{};
   sh.hist = smem;
   sh.misc = reinterpret_cast<int32_t*>(smem + kTopkBins);
-  sh.sel = smem + kTopkBins + 16;
-  sh.tie = sh.sel + p.bitmap_words;
-  sh.keys = sh.tie + p.bitmap_words;                   // [kDecodeCandCap] compacted S bits
-  uint32_t* cpos = sh.keys + kDecodeCandCap;           // [kDecodeCandCap] their positions
-  sh.qf = nullptr;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int base = p.cu[b], L = p.cu[b + 1] - base;
-  const int t = L - 1, n_c = t - p.W + 1, KW = p.K + p.W;
-  int32_t* row = p.idx + ((size_t)b * p.Hkv + g) * KW;
-  float* kth_out = p.kth ? p.kth + (size_t)b * p.Hkv + g : nullptr;
-  if (p.K == 0 || n_c <= p.K) {  // nothing to rank: [0, t] or the window only
-    write_trivial_row(n_c, p.K, t, KW, row);
-    if (kth_out && tid == 0) *kth_out = -1.f;
-    return;
-  }
-  if (tid < G) {
-    const float2* pr = p.part + ((size_t)b * p.Hkv + g) * p.n_split * G + tid;
+  sh.keys = smem + kTopkBins + 16;  // [kDecodeSampleCap] the sample
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int base = p.cu[b], L = p.cu[b + 1] - base, n_c = L - p.W;
+  const size_t rowi = (size_t)b * p.Hkv + g;
+  if (decode_trivial(p, n_c)) return;
+  // log-sum-exp of each head: one wave per head, lanes over the splits
+  const int n_sp = ceil_div(L, kDecodeSplit);
+  for (int h = w; h < G; h += kSelThreads / 64) {
+    const float2* pr = p.part + rowi * p.n_split * G + h;
     float m = -INFINITY, s = 0.f;
-    const int n_sp = ceil_div(L, kDecodeSplit);
-    for (int i = 0; i < n_sp; i++) {
+    for (int i = l; i < n_sp; i += 64) {
       const float2 v = pr[(size_t)i * G];
       const float mn = fmaxf(m, v.x);
       s = s * fast_exp2(m - mn) + v.y * fast_exp2(v.x - mn);
       m = mn;
     }
-    lse_s[tid] = m + fast_log2(s);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float mo = shfl_xor_f(m, off), so = shfl_xor_f(s, off);
+      const float mn = fmaxf(m, mo);
+      s = mn == -INFINITY ? 0.f : s * fast_exp2(m - mn) + so * fast_exp2(mo - mn);
+      m = mn;
+    }
+    if (l == 0) {
+      const float v = m + fast_log2(s);
+      lse_s[h] = v;
+      p.lse2[rowi * G + h] = v;
+    }
   }
   __syncthreads();
   float lse[G];
 #pragma unroll
   for (int h = 0; h < G; h++) lse[h] = lse_s[h];
-  uint32_t* dense = p.dense + ((size_t)b * p.Hkv + g) * p.max_seqlen;
-  // the strided loops below take kBatch elements per thread per round, every load
-  // issued before the first use (one load in flight per thread would wait out a
-  // memory latency per element); indices past the end are clamped and discarded
-  constexpr int kBatch = 8;
+  // the sample: every stride-th candidate, at most kDecodeSampleCap of them
+  const int stride = max(kDecodeSampleStride, ceil_div(n_c, kDecodeSampleCap));
+  const int n_s = ceil_div(n_c, stride);
   const float* zg = p.z2 + ((size_t)g * p.T + base) * G;
-  for (int j0 = 0; j0 < n_c; j0 += kBatch * kSelThreads) {
-    float zb[kBatch][G];
+  constexpr int E = decode_batch<G>();
+  for (int i0 = 0; i0 < n_s; i0 += E * kSelThreads) {
+    float z[E][G];
 #pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int j = min(j0 + u * kSelThreads + tid, n_c - 1);
+    for (int u = 0; u < E; u++) {  // every load issued before the first use
+      const size_t j = (size_t)min(i0 + u * kSelThreads + tid, n_s - 1) * stride;
 #pragma unroll
-      for (int h = 0; h < G; h++) zb[u][h] = zg[(size_t)j * G + h];
+      for (int h = 0; h < G; h++) z[u][h] = zg[j * G + h];
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int j = j0 + u * kSelThreads + tid;
-      float sum = 0.f;
-#pragma unroll
-      for (int h = 0; h < G; h++) sum += fast_exp2(zb[u][h] - lse[h]);
-      if (j < n_c) dense[j] = __float_as_uint(sum);
+    for (int u = 0; u < E; u++) {
+      const int i = i0 + u * kSelThreads + tid;
+      if (i < n_s) sh.keys[i] = decode_score<G>(z[u], lse);
     }
   }
   __syncthreads();
-  auto batched = [&](auto&& fn) {  // fn(j, S bits) for every j < n_c, batched loads
-    for (int j0 = 0; j0 < n_c; j0 += kBatch * kSelThreads) {
-      uint32_t v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; u++) v[u] = dense[min(j0 + u * kSelThreads + tid, n_c - 1)];
-#pragma unroll
-      for (int u = 0; u < kBatch; u++) {
-        const int j = j0 + u * kSelThreads + tid;
-        if (j < n_c) fn(j, v[u]);
-      }
-    }
-  };
-  // threshold from the sample: its r-th largest, r ~ 1.5 K n_s / n_c + 16
-  const int n_s = ceil_div(n_c, kDecodeSampleStride);
+  // r ~ 1.5 K n_s / n_c + 16: about 1.5 K scores of the row are expected to reach tau
   const int r = min(n_s, (int)ceilf(1.5f * (float)p.K * (float)n_s / (float)n_c) + 16);
-  int krem_s;
-  const uint32_t tau = radix_kth([&](int i) { return dense[i * kDecodeSampleStride]; }, n_s, r, sh,
-                                 &krem_s);
-  // how many reach tau (a plain block sum, no contended atomics)
+  int krem;
+  const uint32_t tau = radix_kth([&](int i) { return sh.keys[i]; }, n_s, r, sh, &krem);
+  if (tid == 0) {
+    p.tau[rowi] = tau;
+    p.n_pass[rowi] = 0;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void decode_dense_kernel(DecodeParams p) {
+  __shared__ int32_t misc[16];
+  constexpr int E = decode_batch<G>();
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int base = p.cu[b], L = p.cu[b + 1] - base, n_c = L - p.W;
+  const int j0 = blockIdx.x * (E * kSelThreads);
+  if (decode_trivial(p, n_c) || j0 >= n_c) return;
+  const size_t rowi = (size_t)b * p.Hkv + g;
+  float lse[G];
+#pragma unroll
+  for (int h = 0; h < G; h++) lse[h] = p.lse2[rowi * G + h];
+  const uint32_t tau = p.tau[rowi];
+  const float* zg = p.z2 + ((size_t)g * p.T + base) * G;
+  float z[E][G];
+#pragma unroll
+  for (int u = 0; u < E; u++) {  // every load issued before the first use
+    const size_t j = (size_t)min(j0 + u * kSelThreads + tid, n_c - 1);
+#pragma unroll
+    for (int h = 0; h < G; h++) z[u][h] = zg[j * G + h];
+  }
+  uint32_t* dense = p.dense + rowi * p.max_seqlen;
+  uint32_t sv[E];
   int cnt = 0;
-  batched([&](int, uint32_t x) { cnt += x >= tau ? 1 : 0; });
-  int n_pass;
-  const int off = block_excl_scan(cnt, sh.misc, &n_pass);
+#pragma unroll
+  for (int u = 0; u < E; u++) {
+    const int j = j0 + u * kSelThreads + tid;
+    sv[u] = decode_score<G>(z[u], lse);
+    if (j < n_c) {
+      dense[j] = sv[u];
+      cnt += sv[u] >= tau ? 1 : 0;
+    }
+  }
+  int total;
+  const int off = block_excl_scan(cnt, misc, &total);
+  if (total == 0) return;
+  if (tid == 0) misc[0] = atomicAdd(&p.n_pass[rowi], total);
+  __syncthreads();
+  int o = misc[0] + off;
+  uint32_t* ck = p.cand + rowi * (2 * kDecodeCandCap);
+#pragma unroll
+  for (int u = 0; u < E; u++) {
+    const int j = j0 + u * kSelThreads + tid;
+    if (j < n_c && sv[u] >= tau) {
+      if (o < kDecodeCandCap) {
+        ck[o] = sv[u];
+        ck[kDecodeCandCap + o] = (uint32_t)j;
+      }
+      o++;
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void decode_rank_kernel(DecodeParams p) {
+  extern __shared__ uint32_t smem[];
+  TopkShared sh{};
+  sh.hist = smem;
+  sh.misc = reinterpret_cast<int32_t*>(smem + kTopkBins);
+  sh.sel = smem + kTopkBins + 16;
+  sh.tie = sh.sel + p.bitmap_words;
+  sh.keys = sh.tie + p.bitmap_words;                   // [kDecodeCandCap] candidate S bits
+  uint32_t* cpos = sh.keys + kDecodeCandCap;           // [kDecodeCandCap] their positions
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int base = p.cu[b], L = p.cu[b + 1] - base;
+  const int t = L - 1, n_c = t - p.W + 1, KW = p.K + p.W;
+  const size_t rowi = (size_t)b * p.Hkv + g;
+  int32_t* row = p.idx + rowi * KW;
+  float* kth_out = p.kth ? p.kth + rowi : nullptr;
+  if (decode_trivial(p, n_c)) {
+    write_trivial_row(n_c, p.K, t, KW, row);
+    if (kth_out && tid == 0) *kth_out = -1.f;
+    return;
+  }
+  const int n_pass = p.n_pass[rowi];
   int krem;
   uint32_t kth;
   if (n_pass >= p.K && n_pass <= kDecodeCandCap) {
-    int o = off;  // compact the passing scores and positions (same order as the count)
-    batched([&](int j, uint32_t x) {
-      if (x >= tau) { sh.keys[o] = x; cpos[o] = (uint32_t)j; o++; }
-    });
+    const uint32_t* ck = p.cand + rowi * (2 * kDecodeCandCap);
+    constexpr int kB = 4;
+    for (int i0 = 0; i0 < n_pass; i0 += kB * kSelThreads) {
+      uint32_t kv[kB], pv[kB];
+#pragma unroll
+      for (int u = 0; u < kB; u++) {  // every load issued before the first store
+        const int i = min(i0 + u * kSelThreads + tid, n_pass - 1);
+        kv[u] = ck[i];
+        pv[u] = ck[kDecodeCandCap + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kB; u++) {
+        const int i = i0 + u * kSelThreads + tid;
+        if (i < n_pass) { sh.keys[i] = kv[u]; cpos[i] = pv[u]; }
+      }
+    }
     __syncthreads();
     kth = radix_kth([&](int i) { return sh.keys[i]; }, n_pass, p.K, sh, &krem);
     mark_selected([&](int i) { return sh.keys[i]; }, [&](int i) { return cpos[i]; }, n_pass, kth,
                   krem, ceil_div(n_c, 32), sh);
   } else {  // the sample misled: rank the whole row
+    const uint32_t* dense = p.dense + rowi * p.max_seqlen;
     kth = radix_kth([&](int i) { return dense[i]; }, n_c, p.K, sh, &krem);
     mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth,
                   krem, ceil_div(n_c, 32), sh);
@@ -624,14 +723,25 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(DecodeParams
   if (kth_out && tid == 0) *kth_out = __uint_as_float(kth);
 }
 
+template <class Kern>
+static hipError_t allow_lds(Kern k, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
 template <int G>
 static hipError_t launch_decode_select_g(const DecodeParams& p, size_t lds, hipStream_t s) {
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_select_kernel<G>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(decode_select_kernel<G>, dim3(p.Hkv, p.B), dim3(kSelThreads), lds, s, p);
+  constexpr int E = decode_batch<G>();
+  const size_t lds_tau = (size_t)(kTopkBins + 16 + kDecodeSampleCap) * sizeof(uint32_t);
+  hipError_t e = allow_lds(decode_tau_kernel<G>, lds_tau);
+  if (e != hipSuccess) return e;
+  e = allow_lds(decode_rank_kernel<G>, lds);
+  if (e != hipSuccess) return e;
+  const dim3 rows(p.Hkv, p.B), block(kSelThreads);
+  hipLaunchKernelGGL(decode_tau_kernel<G>, rows, block, lds_tau, s, p);
+  const dim3 chunks(ceil_div(p.max_seqlen, E * kSelThreads), p.Hkv, p.B);
+  hipLaunchKernelGGL(decode_dense_kernel<G>, chunks, block, 0, s, p);
+  hipLaunchKernelGGL(decode_rank_kernel<G>, rows, block, lds, s, p);
   return hipGetLastError();
 }
 
