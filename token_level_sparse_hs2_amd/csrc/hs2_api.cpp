@@ -158,7 +158,8 @@ int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) 
     if (v->cu_seqlens_host[i + 1] - v->cu_seqlens_host[i] < 1) return HS2_ERR_INVALID_ARG;
   if (v->batch > 65535 || d->num_kv_heads > 65535) return HS2_ERR_UNSUPPORTED;  // grid y/z
   const int max_len = std::max(1, g.max_len);
-  dg->n_split = hs2::ceil_div(max_len, hs2::kDecodeSplit);
+  // the bf16 cache's (shorter) split sizes the partials for both caches
+  dg->n_split = hs2::ceil_div(max_len, hs2::decode_split_len(false));
   dg->bitmap_words = hs2::ceil_div(max_len, 32);
   size_t off = 0;
   dg->off_z2 = off;
@@ -541,7 +542,8 @@ int run_decode_select(const hs2_dims* dims, const hs2_varlen* cache, const void*
   p.W = dims->window;
   p.max_seqlen = std::max(1, dg.geo.max_len);
   p.T = dg.geo.T;
-  p.n_split = dg.n_split;
+  p.split_len = hs2::decode_split_len(k8 != nullptr);
+  p.n_split = hs2::ceil_div(p.max_seqlen, p.split_len);
   p.bitmap_words = dg.bitmap_words;
   p.c = scale_log2(dims) * (k8 ? k_scale : 1.f);
   p.z2 = reinterpret_cast<float*>(w + dg.off_z2);

@@ -158,7 +158,11 @@ struct SparseParams {
 };
 
 // Decode step: one query per sequence at its last cached position.
-constexpr int kDecodeSplit = 1024;    // cached keys per logits workgroup
+// cached key bytes per logits workgroup: 256 bf16 or 512 FP8 rows of 128 elements
+constexpr int kDecodeSplitBytes = 65536;
+__host__ __device__ constexpr int decode_split_len(bool fp8) {
+  return kDecodeSplitBytes / (kHeadDim * (fp8 ? 1 : 2));
+}
 constexpr int kDecodeCandCap = 4096;  // candidates ranked in LDS per decode row
 
 struct DecodeParams {
@@ -168,7 +172,8 @@ struct DecodeParams {
   const int32_t* cu;    // [B+1] cache offsets
   int B, Hq, Hkv, K, W;
   int max_seqlen;
-  int n_split;          // ceil(max_seqlen / kDecodeSplit)
+  int split_len;        // cached keys per logits workgroup, decode_split_len
+  int n_split;          // ceil(max_seqlen / split_len)
   int bitmap_words;     // ceil(max_seqlen / 32)
   float c;              // softmax_scale * log2(e)
   int64_t T;            // cached tokens

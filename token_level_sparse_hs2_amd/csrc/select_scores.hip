@@ -723,9 +723,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 // Decode step, logits. Sequence b's query (its newest token, at position
 // L_b - 1) against every cached key: z2[j, h] = c * <q[b,h], k[j,g]> for the
 // group's heads, written to p.z2 in the [Hkv, T, G] layout (each group's run
-// is contiguous for the select kernel's reads), and per split the
-// (max, sum of exp2(z2 - max)) of each head, from which the select kernel forms
-// the full layer's log-sum-exp. Grid (split, g, b): kDecodeSplit keys per
+// is contiguous for the selection kernels' reads), and per split the
+// (max, sum of exp2(z2 - max)) of each head, from which decode_tau_kernel forms
+// the full layer's log-sum-exp. Grid (split, g, b): p.split_len keys per
 // workgroup, 4 waves x 16 keys per step on v_mfma_f32_16x16x32_bf16 with the
 // group's G heads as the 16-row A operand (rows >= G are zero).
 // ---------------------------------------------------------------------------
@@ -741,9 +741,9 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeParams p) {
   __shared__ float2 red[4][16];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int base = p.cu[b], L = p.cu[b + 1] - base;
-  const int j0 = split * kDecodeSplit;
+  const int j0 = split * p.split_len;
   if (j0 >= L) return;  // the whole workgroup: this split is past the sequence
-  const int j1 = min(L, j0 + kDecodeSplit);
+  const int j1 = min(L, j0 + p.split_len);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l >> 4, lc = l & 15;
   const int Hq = p.Hq, Hkv = p.Hkv;
   const float c = p.c;

@@ -558,7 +558,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_tau_kernel(DecodeParams p)
   const size_t rowi = (size_t)b * p.Hkv + g;
   if (decode_trivial(p, n_c)) return;
   // log-sum-exp of each head: one wave per head, lanes over the splits
-  const int n_sp = ceil_div(L, kDecodeSplit);
+  const int n_sp = ceil_div(L, p.split_len);
   for (int h = w; h < G; h += kSelThreads / 64) {
     const float2* pr = p.part + rowi * p.n_split * G + h;
     float m = -INFINITY, s = 0.f;
