@@ -132,6 +132,22 @@ def test_decode_long_caches():
     run_decode(w)
 
 
+def test_decode_sparser_sample_on_long_caches():
+    """Caches longer than 8192 x 16 candidates: the threshold sample thins out
+    (every ceil(n_c / 8192)-th candidate), and the compacted candidate list must
+    still hold the exact top K."""
+    w = synthgen.custom([200001, 150000, 5], Hq=8, Hkv=2, K=1024, W=128, n_sparse=1, seed=1203)
+    run_decode(w)
+
+
+def test_decode_candidate_list_overflow_takes_full_row():
+    """K = 3000: about 1.5 K scores reach the sampled threshold, more than the
+    4096 the compacted list holds, so these rows are ranked over the whole
+    scratch row (the 3050 cache has no more candidates than K and is trivial)."""
+    w = synthgen.custom([9000, 20000, 3050], Hq=8, Hkv=2, K=3000, W=64, n_sparse=1, seed=1204)
+    run_decode(w)
+
+
 def test_decode_zero_queries_tie_rule_bit_exact():
     """q = 0: every score ties, so the lowest positions win. The 9000-token cache
     overflows the compacted candidate path (all scores reach the sampled
