@@ -34,6 +34,25 @@ namespace hs2 {
 
 constexpr int kMaxParts = 32;  // partials merged per row (split rows of a decode step)
 
+// DPP row rotates between the 4-lane banks of each 16-lane row (lanes 4a .. 4a+3
+// form bank a). to_bank<A>: the lanes of bank A take src from lane - 4A of their
+// row (bank 0); the other lanes keep old. from_bank<A>: the lanes of bank 0 take
+// src from lane + 4A (bank A); the other lanes keep old.
+template <int A>
+__device__ __forceinline__ float to_bank(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                    0x120 + 4 * A, 0xF, 1 << A, false));
+}
+template <int A>
+__device__ __forceinline__ uint32_t from_bank(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x120 + ((16 - 4 * A) & 15), 0xF,
+                                               0x1, false);
+}
+// every lane takes the value of lane (lane & ~12) (its row's bank-0 lane of the same position)
+__device__ __forceinline__ float bank_bcast(float x) {
+  return to_bank<3>(to_bank<2>(to_bank<1>(x, x), x), x);
+}
+
 // CH index entries per step: 32 for a bf16 cache; 16 for an FP8 one, which halves
 // the LDS slice and the staging registers so that four waves per SIMD fit (measured
 // 5% faster there; a bf16 cache at 16 entries and three waves was 1.6% slower).
@@ -78,7 +97,16 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     }
   }
 
-  float m = -INFINITY, lsum = 0.f;
+  // Compact softmax (G <= 4, 32-entry steps): the step's valid scores sit in lanes
+  // (lq, h < 4) of the S^T tiles, 8 per lane. Bank a of each row takes the pair
+  // (2a, 2a + 1) of lane (lq, h) with a DPP row rotate, so the exponentials and
+  // the bf16 split run on 2 values per lane instead of 8; the packed pairs return
+  // to lanes (lq, h), the B operand of P.V, the same way. lsum then holds each
+  // lane's share (reduced over the banks at the end) and mc the reference m of
+  // head (lane & 3). (16-entry steps keep the plain layout: there the saving is
+  // smaller and the extra registers spill under four waves per SIMD.)
+  constexpr bool kCompact = G <= 4 && MT == 2;
+  float m = -INFINITY, mc = -INFINITY, lsum = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -202,19 +230,16 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     if (__any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
-      lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < 8; i++) o[i] *= alpha;
       m = m_new;
+      if constexpr (kCompact) {
+        lsum *= bank_bcast(alpha);
+        mc = bank_bcast(m);
+      } else {
+        lsum *= alpha;
+      }
     }
-    float pv[4 * MT];
-    float psum = 0.f;
-#pragma unroll
-    for (int sidx = 0; sidx < 4 * MT; sidx++) {
-      pv[sidx] = fast_exp2(fmaf(s[sidx >> 2][sidx & 3], c, -m));
-      psum += pv[sidx];
-    }
-    lsum += psum;
 
     // P^T operand (B): column = head, k slot s <-> key (s < 4 ? 4lq + s : 16 + 4lq + s - 4).
     // P is split into bf16 parts p = p0 + p1 (+ p2 in the precise mode), each the
@@ -222,15 +247,46 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     // mantissa bits of P; V is bf16 already, so every product is exact.
     // (MT = 1: 16x16x16 MFMA, k slot s <-> key 4lq + s.)
     uint32_t pk[NSPLIT][2 * MT];
+    if constexpr (kCompact) {
+      // bank a <- pair a: (s[0][0], s[0][1]), (s[0][2], s[0][3]), (s[1][0], s[1][1]), ...
+      float t0 = to_bank<1>(s[0][0], s[0][2]), t1 = to_bank<1>(s[0][1], s[0][3]);
+      t0 = to_bank<2>(t0, s[MT - 1][0]);
+      t1 = to_bank<2>(t1, s[MT - 1][1]);
+      t0 = to_bank<3>(t0, s[MT - 1][2]);
+      t1 = to_bank<3>(t1, s[MT - 1][3]);
+      float p0 = fast_exp2(fmaf(t0, c, -mc)), p1 = fast_exp2(fmaf(t1, c, -mc));
+      lsum += p0 + p1;
 #pragma unroll
-    for (int part = 0; part < NSPLIT; part++) {
+      for (int part = 0; part < NSPLIT; part++) {
+        const uint32_t pc = pack_bf16x2(p0, p1);
+        if (part + 1 < NSPLIT) {
+          p0 -= bf16_bits_to_f32(pc & 0xFFFFu);
+          p1 -= __uint_as_float(pc & 0xFFFF0000u);
+        }
+        pk[part][0] = pc;
+        pk[part][1] = from_bank<1>(pc, pc);
+        pk[part][MT] = from_bank<2>(pc, pc);
+        pk[part][2 * MT - 1] = from_bank<3>(pc, pc);
+      }
+    } else {
+      float pv[4 * MT];
+      float psum = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2 * MT; u++) pk[part][u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
-      if (part + 1 < NSPLIT) {
+      for (int sidx = 0; sidx < 4 * MT; sidx++) {
+        pv[sidx] = fast_exp2(fmaf(s[sidx >> 2][sidx & 3], c, -m));
+        psum += pv[sidx];
+      }
+      lsum += psum;
 #pragma unroll
-        for (int u = 0; u < 2 * MT; u++) {
-          pv[2 * u] -= bf16_bits_to_f32(pk[part][u] & 0xFFFFu);
-          pv[2 * u + 1] -= __uint_as_float(pk[part][u] & 0xFFFF0000u);
+      for (int part = 0; part < NSPLIT; part++) {
+#pragma unroll
+        for (int u = 0; u < 2 * MT; u++) pk[part][u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
+        if (part + 1 < NSPLIT) {
+#pragma unroll
+          for (int u = 0; u < 2 * MT; u++) {
+            pv[2 * u] -= bf16_bits_to_f32(pk[part][u] & 0xFFFFu);
+            pv[2 * u + 1] -= __uint_as_float(pk[part][u] & 0xFFFF0000u);
+          }
         }
       }
     }
@@ -296,6 +352,10 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     gather(ja, ga);
     load_raw(c + 4, r2);
     consume(jb, gb);
+  }
+  if constexpr (kCompact) {  // the banks' shares of each head
+    lsum += shfl_xor_f(lsum, 4);
+    lsum += shfl_xor_f(lsum, 8);
   }
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
