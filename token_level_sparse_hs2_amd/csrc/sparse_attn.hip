@@ -391,43 +391,42 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
 
 // Merges the n_part (<= kMaxParts) partials of each (row, group): per head and d,
 // o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s (0 if no part
-// saw a valid entry). One workgroup per (row, group): the parts' (m, l) go to LDS,
-// one thread per head turns them into weights, then every output element sums its
-// parts with all loads in flight.
+// saw a valid entry). One workgroup per (row, group, head), one thread per d: the
+// parts' outputs and their (m, l) are all loaded before the first use, so the
+// merge waits out one memory round trip.
 template <int G, bool PRECISE>
-__global__ __launch_bounds__(256) void sparse_combine_kernel(SparseParams p) {
-  __shared__ float2 ml[kMaxParts * G];
-  __shared__ float wgt[kMaxParts * G];
-  const int64_t tg = blockIdx.x / p.Hkv;
-  const int g = (int)(blockIdx.x % p.Hkv);
-  const int tid = threadIdx.x, np = p.n_part;
+__global__ __launch_bounds__(kHeadDim) void sparse_combine_kernel(SparseParams p) {
+  __shared__ float2 ml[kMaxParts];
+  const int64_t row = blockIdx.x / G;  // (query row, group)
+  const int h = (int)(blockIdx.x % G);
+  const int64_t tg = row / p.Hkv;
+  const int g = (int)(row % p.Hkv);
+  const int d = threadIdx.x, np = p.n_part;
   auto slot = [&](int s) { return (size_t)(tg * np + s) * p.Hkv + g; };
-  for (int i = tid; i < np * G; i += 256) ml[i] = p.part_ml[slot(i / G) * G + i % G];
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int s = 0; s < np; s++) M = fmaxf(M, ml[s * G + tid].x);
-    float den = 0.f;
-    if (M > -INFINITY)
-      for (int s = 0; s < np; s++) den += ml[s * G + tid].y * fast_exp2(ml[s * G + tid].x - M);
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int s = 0; s < np; s++)
-      wgt[s * G + tid] = M > -INFINITY ? fast_exp2(ml[s * G + tid].x - M) * inv : 0.f;
-  }
-  __syncthreads();
-  for (int i = tid; i < G * kHeadDim; i += 256) {
-    const int h = i / kHeadDim, d = i % kHeadDim;
-    float v[kMaxParts];
+  float v[kMaxParts];
 #pragma unroll
-    for (int s = 0; s < kMaxParts; s++)
-      v[s] = s < np ? p.part_o[(slot(s) * G + h) * kHeadDim + d] : 0.f;
-    float val = 0.f;
+  for (int s = 0; s < kMaxParts; s++)
+    v[s] = s < np ? p.part_o[(slot(s) * G + h) * kHeadDim + d] : 0.f;
+  if (d < np) ml[d] = p.part_ml[slot(d) * G + h];
+  __syncthreads();
+  float M = -INFINITY;
+  for (int s = 0; s < np; s++) M = fmaxf(M, ml[s].x);
+  float den = 0.f, val = 0.f;
+  if (M > -INFINITY) {
 #pragma unroll
-    for (int s = 0; s < kMaxParts; s++) val += s < np ? v[s] * wgt[s * G + h] : 0.f;
-    const size_t o = ((size_t)tg * p.Hq + g * G + h) * kHeadDim + d;
-    if constexpr (PRECISE) static_cast<float*>(p.out)[o] = val;
-    else static_cast<__bf16*>(p.out)[o] = (__bf16)val;
+    for (int s = 0; s < kMaxParts; s++) {
+      if (s < np) {
+        const float2 e = ml[s];
+        const float wgt = fast_exp2(e.x - M);  // 0 for a part without valid entries
+        den += e.y * wgt;
+        val = fmaf(v[s], wgt, val);
+      }
+    }
   }
+  val = den > 0.f ? val / den : 0.f;
+  const size_t o = ((size_t)tg * p.Hq + g * G + h) * kHeadDim + d;
+  if constexpr (PRECISE) static_cast<float*>(p.out)[o] = val;
+  else static_cast<__bf16*>(p.out)[o] = (__bf16)val;
 }
 
 template <int G>
@@ -445,12 +444,11 @@ static hipError_t launch_sparse_g(bool precise, bool fp8, const SparseParams& p,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_part <= 1) return e;
-  const int64_t rows = p.T * p.Hkv;
-  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (precise)
-    hipLaunchKernelGGL((sparse_combine_kernel<G, true>), dim3((unsigned)rows), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((sparse_combine_kernel<G, false>), dim3((unsigned)rows), dim3(256), 0, s, p);
+  const int64_t blocks_c = p.T * p.Hkv * G;  // (row, group, head)
+  if (blocks_c > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid_c((unsigned)blocks_c), block_c(kHeadDim);
+  if (precise) hipLaunchKernelGGL((sparse_combine_kernel<G, true>), grid_c, block_c, 0, s, p);
+  else hipLaunchKernelGGL((sparse_combine_kernel<G, false>), grid_c, block_c, 0, s, p);
   return hipGetLastError();
 }
 
