@@ -74,9 +74,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // K-th largest key among key(i), i < n (1 <= k <= n). Returns the key and, in
 // *krem, how many elements equal to it belong to the top k. Radix select on the
-// bits below the keys' common prefix, up to 11 bits (2048 bins) per pass.
+// bits below the keys' common prefix, up to 11 bits (2048 bins) per pass. With
+// max_passes, it stops early and returns the lower edge of the bin that holds the
+// K-th largest key (at least k keys reach it; *krem is then meaningless).
 template <class KeyFn>
-__device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int* krem) {
+__device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int* krem,
+                              int max_passes = 3) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = tid; i < n; i += kSelThreads) {
@@ -108,7 +111,7 @@ __device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int
   uint32_t prefix = mx & mask;
   int kr = k;
   constexpr int kPer = kTopkBins / kSelThreads;  // bins per thread in the scan
-  while (hi >= 0) {
+  for (int pass = 0; hi >= 0 && pass < max_passes; pass++) {
     const int lo = max(0, hi - 10);
     const int nb = hi - lo + 1;
     const uint32_t dmask = (1u << nb) - 1u;
@@ -605,10 +608,12 @@ __global__ __launch_bounds__(kSelThreads) void decode_tau_kernel(DecodeParams p)
     }
   }
   __syncthreads();
-  // r ~ 1.5 K n_s / n_c + 16: about 1.5 K scores of the row are expected to reach tau
+  // r ~ 1.5 K n_s / n_c + 16: about 1.5 K scores of the row are expected to reach
+  // tau. One histogram pass suffices: tau is the lower edge of the 11-bit bin that
+  // holds the sample's r-th largest score (any tau is correct, this one is close)
   const int r = min(n_s, (int)ceilf(1.5f * (float)p.K * (float)n_s / (float)n_c) + 16);
   int krem;
-  const uint32_t tau = radix_kth([&](int i) { return sh.keys[i]; }, n_s, r, sh, &krem);
+  const uint32_t tau = radix_kth([&](int i) { return sh.keys[i]; }, n_s, r, sh, &krem, 1);
   if (tid == 0) {
     p.tau[rowi] = tau;
     p.n_pass[rowi] = 0;
