@@ -163,9 +163,19 @@ def main():
 
     sel_ms = timed(lambda: hs2.hs2_select(case.dims, case.varlen, case.q_full, case.k, idx, None,
                                           case.workspace, stream=stream), args.kernel_reps)
-    sp_ms = timed(lambda: hs2.hs2_sparse_attn(case.dims, case.varlen, case.q_sparse[0], case.k,
-                                              case.v, idx, outs[0], hs2.HS2_OUT_BF16,
-                                              stream=stream), args.kernel_reps)
+    # the step's sparse layers run from one shared-gather plan of idx
+    plan = torch.empty(hs2.hs2_workspace_size(case.dims, case.varlen, hs2.HS2_OP_SPARSE_PLAN),
+                       dtype=torch.uint8, device="cuda")
+    plan_ms = timed(lambda: hs2.hs2_sparse_plan(case.dims, case.varlen, idx, plan, stream=stream),
+                    args.kernel_reps)
+    sp_ms = timed(lambda: hs2.hs2_sparse_attn_planned(case.dims, case.varlen, case.q_sparse[0],
+                                                      case.k, case.v, plan, outs[0],
+                                                      hs2.HS2_OUT_BF16, stream=stream),
+                  args.kernel_reps)
+    sp_tok_ms = timed(lambda: hs2.hs2_sparse_attn(case.dims, case.varlen, case.q_sparse[0], case.k,
+                                                  case.v, idx, outs[0], hs2.HS2_OUT_BF16,
+                                                  stream=stream), args.kernel_reps)
+    union_rows, pair_rows = plan_rows(plan, case.T, Hq // Hkv, Hkv, K + W, idx)
     oam_ms = timed(lambda: hs2.hs2_select_ex(case.dims, case.varlen, case.q_full, case.k, idx, None,
                                              v=case.v, oam_beta=0.5, workspace=case.workspace,
                                              stream=stream), args.kernel_reps)
@@ -179,9 +189,14 @@ def main():
     quant_ms = timed(lambda: (hs2.hs2_quantize_fp8(case.k, k8, 1.0 / ks, stream=stream),
                               hs2.hs2_quantize_fp8(case.v, v8, 1.0 / vs, stream=stream)),
                      args.kernel_reps)
-    sp8_ms = timed(lambda: hs2.hs2_sparse_attn_fp8(case.dims, case.varlen, case.q_sparse[0], k8, v8,
-                                                   ks, vs, idx, outs[0], hs2.HS2_OUT_BF16,
-                                                   stream=stream), args.kernel_reps)
+    sp8_ms = timed(lambda: hs2.hs2_sparse_attn_planned_fp8(case.dims, case.varlen,
+                                                           case.q_sparse[0], k8, v8, ks, vs, plan,
+                                                           outs[0], hs2.HS2_OUT_BF16,
+                                                           stream=stream), args.kernel_reps)
+    sp8_tok_ms = timed(lambda: hs2.hs2_sparse_attn_fp8(case.dims, case.varlen, case.q_sparse[0],
+                                                       k8, v8, ks, vs, idx, outs[0],
+                                                       hs2.HS2_OUT_BF16, stream=stream),
+                       args.kernel_reps)
     full_out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
     full_ms = timed(lambda: hs2.hs2_select_full(case.dims, case.varlen, case.q_full, case.k, case.v,
                                                 idx, full_out, hs2.HS2_OUT_BF16,
@@ -195,8 +210,13 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(sp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(sp_gbs / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic("sparse_attn.hip", args.workload),
-                "kernel": "sparse_attn_kernel (one sparse layer)",
-                "algorithmic_bytes_per_launch": b_sp, "avg_launch_ms": round(sp_ms, 4)}
+                "kernel": "sparse_attn_kernel, planned (one sparse layer)",
+                "algorithmic_bytes_per_launch": b_sp, "avg_launch_ms": round(sp_ms, 4),
+                "plan_ms": round(plan_ms, 4), "per_token_layer_ms": round(sp_tok_ms, 4),
+                "rows_gathered_per_launch": union_rows, "rows_selected_per_launch": pair_rows,
+                "note": "algorithmic bytes count every (token, group) row once; the planned "
+                        "layer gathers each row of a token group's union once "
+                        "(rows_gathered / rows_selected); plan_ms once per selection"}
     f_out = f_sel  # one QK^T and one PV pass over the causal pairs: 2 * 2 * d * Hq * pairs
     out_ms = max(full_ms - sel_ms, 1e-9)
     full_roof = {"bound": "mfma", "achieved": round(f_out / (out_ms * 1e-3) / 1e12, 1),
@@ -209,12 +229,14 @@ def main():
     q_bytes = 2 * T * Hkv * d * (2 + 1)  # K and V: bf16 read, codes written
     fp8_roof = {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
                 "sparse_layer_ms": round(sp8_ms, 4),
+                "per_token_layer_ms": round(sp8_tok_ms, 4),
                 "sparse_achieved": round(b_sp8 / (sp8_ms * 1e-3) / 1e9, 1),
                 "sparse_algorithmic_bytes": b_sp8,
                 "quantize_ms": round(quant_ms, 4),
                 "quantize_achieved": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1),
-                "note": "FP8 (E4M3) KV cache: hs2_quantize_fp8 of K and V, then one sparse layer "
-                        "over the codes (hs2_sparse_attn_fp8); bf16 layer: roofline.avg_launch_ms"}
+                "note": "FP8 (E4M3) KV cache: hs2_quantize_fp8 of K and V, then one planned "
+                        "sparse layer over the codes (hs2_sparse_attn_planned_fp8); bf16 layer: "
+                        "roofline.avg_launch_ms"}
     select_roof = {"bound": "mfma", "achieved": round(sel_tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
                    "unit": "TFLOP/s", "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4),
                    "algorithmic_flops": f_sel, "avg_call_ms": round(sel_ms, 4),
@@ -274,6 +296,18 @@ def decode_work(lengths, Hq, Hkv, d, K, W, n_sparse, elem_bytes=2):
     n = sum(min(L, KW) for L in lengths)
     sp = Hkv * n * 2 * d * elem_bytes + B * Hkv * KW * 4 + 2 * B * Hq * d * 2
     return sel, sp
+
+
+def plan_rows(plan, T, G, Hkv, KW, idx):
+    """(rows the planned layer gathers, rows the (token, group) rows select): the sum of
+    the plan's union counts (one word per entry, [n_grp * Hkv, NT * KW], then the counts at
+    the next 256-byte boundary) and of the valid index entries."""
+    import torch
+    nt = 16 // G if G >= 2 else 8
+    lists = (T + nt - 1) // nt * Hkv
+    off = (lists * nt * KW * 4 + 255) // 256 * 256
+    counts = plan[off:off + lists * 4].view(torch.int32)
+    return int(counts.sum().item()), int((idx >= 0).sum().item())
 
 
 def main_decode(args):

@@ -77,7 +77,8 @@ enum {
   HS2_OP_SPARSE = 2,
   HS2_OP_PREFILL_BLOCK = 3,
   HS2_OP_DECODE_SELECT = 4,
-  HS2_OP_DECODE_SPARSE = 5
+  HS2_OP_DECODE_SPARSE = 5,
+  HS2_OP_SPARSE_PLAN = 6  /* the plan buffer of hs2_sparse_plan */
 };
 
 /* Flags of hs2_dims.flags. */
@@ -149,10 +150,46 @@ int hs2_sparse_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
                     size_t workspace_bytes, void* stream);
 
 /*
+ * Shared-gather plan of a selection's index rows, for the sparse layers that
+ * reuse them (HySparse2 news summary, KV Reuse paragraph: every sparse layer of
+ * the module attends over the same positions of the same cache). Consecutive
+ * tokens select largely the same rows -- the forced window, and keys that score
+ * high for all of them -- so the tokens t0 .. t0 + NT - 1 of the packed batch
+ * (NT = 16 / G, at most 8; G = Hq / Hkv) are served together: for each such
+ * group and KV group the plan
+ * holds the sorted union of their rows, each with the set of tokens that hold
+ * it, and a planned layer gathers every union row once for all of them.
+ * idx [T,Hkv,K+W] int32 in the selection's format (hs2_select, hs2_select_ex,
+ * hs2_select_full): each row ascending, no repeats, then -1 padding; entries
+ * past t are skipped, and rows in another order are not supported (entries
+ * below an earlier one are dropped). plan: device buffer of
+ * hs2_workspace_size(HS2_OP_SPARSE_PLAN) bytes, owned by the caller, written
+ * here and read by the planned layers (its layout is internal); it stays valid
+ * while idx and cu_seqlens are unchanged. Errors: HS2_ERR_INVALID_ARG (idx NULL),
+ * HS2_ERR_WORKSPACE (plan NULL or too small), HS2_ERR_UNSUPPORTED (sequences so
+ * long that (max_seqlen + 16) * Hkv * 256 >= 2^32).
+ */
+int hs2_sparse_plan(const hs2_dims* dims, const hs2_varlen* varlen, const int32_t* idx,
+                    void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * hs2_sparse_attn over a plan from hs2_sparse_plan (the same dims, varlen and
+ * rows): the same outputs (to fp32 rounding order), each union row gathered
+ * once per token group. q, k, v, out, out_dtype as for hs2_sparse_attn.
+ */
+int hs2_sparse_attn_planned(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
+                            const void* k, const void* v, const void* plan, size_t plan_bytes,
+                            void* out, int out_dtype, void* stream);
+
+/*
  * One hybrid module in prefill: hs2_select on (q_full, k) into idx_out, then
  * n_sparse sparse layers, layer i reading q_sparse_host_array[i] (device
  * pointer) and writing out_sparse_host_array[i], all sharing k, v and idx.
- * The two pointer arrays live on the host and are read during the call.
+ * The two pointer arrays live on the host and are read during the call. With a
+ * workspace of hs2_workspace_size(HS2_OP_PREFILL_BLOCK) bytes the layers run
+ * from one shared-gather plan (as hs2_sparse_plan + hs2_sparse_attn_planned,
+ * the plan written over the selection's scratch); a workspace of only the
+ * HS2_OP_SELECT size runs them as hs2_sparse_attn.
  */
 int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void* q_full,
                       const void* k, const void* v, int n_sparse,
@@ -251,6 +288,13 @@ int hs2_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const vo
                         const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
                         const int32_t* idx, void* out, int out_dtype, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* hs2_sparse_attn_planned over an FP8 cache (same plan, q, out and errors; scales
+ * as for hs2_sparse_attn_fp8). */
+int hs2_sparse_attn_planned_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
+                                const uint8_t* k8, const uint8_t* v8, float k_scale,
+                                float v_scale, const void* plan, size_t plan_bytes, void* out,
+                                int out_dtype, void* stream);
 
 /* hs2_decode_select over an FP8 key cache: the full layer's decode queries
  * against k = k_scale * E4M3(k8) (same idx, kth, workspace and errors). */

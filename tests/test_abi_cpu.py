@@ -148,9 +148,44 @@ def test_empty_batch_is_a_noop(lib):
 def test_workspace_sizes_are_bounded(lib):
     d = hs2.make_dims(32, 8, 1024, 128)
     for lengths in ([1024], [32768], [131072], [196608, 4096, 50000]):
-        n = hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_PREFILL_BLOCK)
-        assert 0 < n < 6 * (1 << 30)
+        T = sum(lengths)
+        idx_bytes = T * 8 * (1024 + 128) * 4
+        sel = hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_SELECT)
+        assert 0 < sel < 6 * (1 << 30)
+        # the shared-gather plan: one 4-byte word per index entry, plus a count per union
+        plan = hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_SPARSE_PLAN)
+        assert idx_bytes <= plan <= idx_bytes + T * 8 + 4096
+        assert hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_PREFILL_BLOCK) == max(sel, plan)
         assert hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_SPARSE) == 0
+
+
+def test_sparse_plan_validation(lib):
+    d = hs2.make_dims(32, 8, 1024, 128)
+    v = varlen([5000, 70])
+    L = hs2.load_library()
+    need = hs2.hs2_workspace_size(d, v, hs2.HS2_OP_SPARSE_PLAN)
+    dv, vv = ctypes.byref(d), ctypes.byref(v.struct)
+    assert L.hs2_sparse_plan(dv, vv, None, 1, need, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_sparse_plan(dv, vv, 1, None, need, None) == hs2.HS2_ERR_WORKSPACE
+    assert L.hs2_sparse_plan(dv, vv, 1, 1, need - 1, None) == hs2.HS2_ERR_WORKSPACE
+    # planned layers: bad dtype, null output, short plan, bad FP8 scale
+    assert L.hs2_sparse_attn_planned(dv, vv, 1, 1, 1, 1, need, 1, 7, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_sparse_attn_planned(dv, vv, 1, 1, 1, 1, need, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_sparse_attn_planned(dv, vv, 1, 1, 1, 1, need - 1, 1, 0, None) == hs2.HS2_ERR_WORKSPACE
+    assert L.hs2_sparse_attn_planned(dv, vv, 1, 1, 1, None, need, 1, 0, None) == hs2.HS2_ERR_WORKSPACE
+    assert (L.hs2_sparse_attn_planned_fp8(dv, vv, 1, 8, 8, -1.0, 1.0, 1, need, 1, 0, None)
+            == hs2.HS2_ERR_INVALID_ARG)
+    # empty batch: nothing to plan
+    e = hs2.VarlenArgs(FakeDev(0), [0])
+    assert hs2.hs2_workspace_size(d, e, hs2.HS2_OP_SPARSE_PLAN) == 0
+    assert L.hs2_sparse_plan(dv, ctypes.byref(e.struct), None, None, 0, None) == hs2.HS2_OK
+    # rows past 2^32 bytes from a group's base: no plan (the per-token layer still runs)
+    d64 = hs2.make_dims(64, 64, 1024, 128)
+    v64 = varlen([262130])
+    with pytest.raises(hs2.HS2Error):
+        hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_SPARSE_PLAN)
+    assert (hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_PREFILL_BLOCK)
+            == hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_SELECT))
 
 
 @pytest.mark.parametrize("lengths,tok", [

@@ -160,18 +160,6 @@ def test_peaked_softmax_rows():
     assert rel.max() <= 1e-3
 
 
-def test_prefill_block_equals_components():
-    import torch
-    w = synthgen.custom([1000, 3000], Hq=8, Hkv=2, K=256, W=32, n_sparse=2, seed=9)
-    inp = synthgen.make_inputs(w)
-    case = GpuCase(w, inp)
-    idx_b, outs = case.prefill_block()
-    idx_s, _ = case.select()
-    assert torch.equal(idx_b, idx_s)
-    for qs, ob in zip(case.q_sparse, outs):
-        assert torch.equal(case.sparse(qs, idx_s), ob)
-
-
 def test_sparse_ignores_invalid_entries():
     """Entries outside [0, t] are skipped; a row with none left gives zeros (oracle agrees)."""
     import oracle

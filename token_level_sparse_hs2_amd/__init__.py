@@ -35,6 +35,7 @@ HS2_OP_SPARSE = 2
 HS2_OP_PREFILL_BLOCK = 3
 HS2_OP_DECODE_SELECT = 4
 HS2_OP_DECODE_SPARSE = 5
+HS2_OP_SPARSE_PLAN = 6
 HS2_FLAG_EXACT_SELECT = 1
 HS2_FLAG_BLOCK_SELECT = 2
 HS2_MAX_SEQLEN = 262144
@@ -100,6 +101,12 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_quantize_fp8.argtypes = [vp, vp, i64, f32, vp]
     lib.hs2_quantize_fp8.restype = i32
     lib.hs2_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp, sz, vp]
+    lib.hs2_sparse_plan.argtypes = [D, V, vp, vp, sz, vp]
+    lib.hs2_sparse_plan.restype = i32
+    lib.hs2_sparse_attn_planned.argtypes = [D, V, vp, vp, vp, vp, sz, vp, i32, vp]
+    lib.hs2_sparse_attn_planned.restype = i32
+    lib.hs2_sparse_attn_planned_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, sz, vp, i32, vp]
+    lib.hs2_sparse_attn_planned_fp8.restype = i32
     lib.hs2_sparse_attn_fp8.restype = i32
     lib.hs2_decode_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp, sz, vp]
     lib.hs2_decode_sparse_attn_fp8.restype = i32
@@ -188,6 +195,32 @@ def hs2_sparse_attn(dims: Dims, varlen: VarlenArgs, q, k, v, idx, out, out_dtype
     _check(load_library().hs2_sparse_attn(ctypes.byref(dims), ctypes.byref(varlen.struct), _ptr(q),
                                           _ptr(k), _ptr(v), _ptr(idx), _ptr(out), out_dtype,
                                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def hs2_sparse_plan(dims: Dims, varlen: VarlenArgs, idx, plan, stream=None) -> None:
+    _check(load_library().hs2_sparse_plan(ctypes.byref(dims), ctypes.byref(varlen.struct),
+                                          _ptr(idx), _ptr(plan), _nbytes(plan), _stream(stream)))
+
+
+def hs2_sparse_attn_planned(dims: Dims, varlen: VarlenArgs, q, k, v, plan, out,
+                            out_dtype: int = HS2_OUT_BF16, stream=None) -> None:
+    _check(load_library().hs2_sparse_attn_planned(ctypes.byref(dims), ctypes.byref(varlen.struct),
+                                                  _ptr(q), _ptr(k), _ptr(v), _ptr(plan),
+                                                  _nbytes(plan), _ptr(out), out_dtype,
+                                                  _stream(stream)))
+
+
+def hs2_sparse_attn_planned_fp8(dims: Dims, varlen: VarlenArgs, q, k8, v8, k_scale: float,
+                                v_scale: float, plan, out, out_dtype: int = HS2_OUT_BF16,
+                                stream=None) -> None:
+    _check(load_library().hs2_sparse_attn_planned_fp8(
+        ctypes.byref(dims), ctypes.byref(varlen.struct), _ptr(q), _ptr(k8), _ptr(v8),
+        float(k_scale), float(v_scale), _ptr(plan), _nbytes(plan), _ptr(out), out_dtype,
+        _stream(stream)))
 
 
 def hs2_prefill_block(dims: Dims, varlen: VarlenArgs, q_full, k, v, q_sparse: Sequence,

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 
@@ -42,6 +43,11 @@ struct Geometry {
   int sbuf_words = 0;
   bool exact_only = false;  // K above the register-ranked limit: every row takes the exact path
   int block = 0;            // block selection: tokens per block
+  // shared-gather plan of the sparse layers (usable when plan_ok)
+  bool plan_ok = false;
+  int64_t n_grp = 0;        // token groups of plan_tokens(G)
+  int plan_cap = 0;         // union entries per (group, KV group)
+  size_t off_pcount = 0, plan_bytes = 0;
 };
 
 bool g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
@@ -134,6 +140,19 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   const size_t per_wave =
       (256 + (size_t)geo->bitmap_words + (size_t)geo->sbuf_words) * sizeof(uint32_t);
   geo->topk_rows_per_block = (int)std::max<size_t>(1, std::min<size_t>(4, 40960 / per_wave));
+  // shared-gather plan: union rows are relative to a group's first sequence and lie
+  // below its last token, so they stay under max_len + 16 (32-bit byte offsets)
+  const int nt = hs2::plan_tokens(geo->G);
+  const int64_t kw = (int64_t)d->top_k + d->window;
+  geo->n_grp = (geo->T + nt - 1) / nt;
+  geo->plan_cap = (int)std::min<int64_t>(kw * nt, INT32_MAX);
+  geo->plan_ok = kw * nt <= INT32_MAX &&
+                 ((int64_t)max_len + 16) * d->num_kv_heads * hs2::kHeadDim * 2 < (1LL << 32);
+  if (geo->plan_ok) {
+    const size_t lists = (size_t)geo->n_grp * d->num_kv_heads;
+    geo->off_pcount = align_up(lists * (size_t)geo->plan_cap * sizeof(uint32_t));
+    geo->plan_bytes = align_up(geo->off_pcount + lists * sizeof(int32_t));
+  }
   return HS2_OK;
 }
 
@@ -334,11 +353,38 @@ int check_fp8(const void* k8, const void* v8, float k_scale, float v_scale) {
   return HS2_OK;
 }
 
+// The shared-gather plan of idx (rows as written by the selection) into plan.
+int run_plan(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const int32_t* idx,
+             void* plan, hipStream_t s) {
+  hs2::PlanParams pp{};
+  pp.idx = idx;
+  pp.cu = v->cu_seqlens;
+  pp.B = v->batch;
+  pp.Hkv = d->num_kv_heads;
+  pp.KW = d->top_k + d->window;
+  pp.T = geo.T;
+  pp.n_grp = geo.n_grp;
+  pp.cap = geo.plan_cap;
+  pp.list = static_cast<uint32_t*>(plan);
+  pp.count = reinterpret_cast<int32_t*>(static_cast<char*>(plan) + geo.off_pcount);
+  hipError_t e = hs2::launch_sparse_plan(geo.G, pp, s);
+  if (e != hipSuccess) return hip_fail(e, "sparse plan kernel");
+  return HS2_OK;
+}
+
+// One sparse layer: one wave per (token, KV group) over idx, or, with a plan
+// (from run_plan), one wave per (token group, KV group) over the plan's unions.
 int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
                const void* k, const void* vv, const int32_t* idx, void* out, int out_dtype,
-               hipStream_t s, const float* fp8_scales = nullptr) {
+               hipStream_t s, const float* fp8_scales = nullptr, const void* plan = nullptr) {
   if (geo.T == 0) return HS2_OK;
   hs2::SparseParams p{};
+  if (plan) {
+    p.plist = static_cast<const uint32_t*>(plan);
+    p.pcount = reinterpret_cast<const int32_t*>(static_cast<const char*>(plan) + geo.off_pcount);
+    p.pcap = geo.plan_cap;
+    p.n_grp = geo.n_grp;
+  }
   p.q = static_cast<const uint16_t*>(q);
   set_kv(&p, k, vv, fp8_scales);
   p.idx = idx;
@@ -356,11 +402,28 @@ int run_sparse(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   return HS2_OK;
 }
 
+int run_planned(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                const void* v, const void* plan, size_t plan_bytes, void* out, int out_dtype,
+                void* stream, const float* fp8_scales) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (fp8_scales && check_fp8(k, v, fp8_scales[0], fp8_scales[1]) != HS2_OK)
+    return HS2_ERR_INVALID_ARG;
+  if (geo.T == 0) return HS2_OK;
+  if (!geo.plan_ok) return HS2_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return HS2_ERR_INVALID_ARG;
+  if (!plan || plan_bytes < geo.plan_bytes) return HS2_ERR_WORKSPACE;
+  return run_sparse(dims, varlen, geo, q, k, v, nullptr, out, out_dtype,
+                    static_cast<hipStream_t>(stream), fp8_scales, plan);
+}
+
 }  // namespace
 
 extern "C" {
 
-int hs2_version(void) { return 1 * 10000 + 2 * 100 + 0; }
+int hs2_version(void) { return 1 * 10000 + 3 * 100 + 0; }
 
 const char* hs2_status_string(int status) {
   switch (status) {
@@ -384,12 +447,22 @@ int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, i
     *bytes_out = dg.geo.B == 0 ? 0 : (op == HS2_OP_DECODE_SPARSE ? dg.sparse_bytes : dg.bytes);
     return HS2_OK;
   }
-  if (op != HS2_OP_SELECT && op != HS2_OP_SPARSE && op != HS2_OP_PREFILL_BLOCK)
+  if (op != HS2_OP_SELECT && op != HS2_OP_SPARSE && op != HS2_OP_PREFILL_BLOCK &&
+      op != HS2_OP_SPARSE_PLAN)
     return HS2_ERR_INVALID_ARG;
   Geometry geo;
   int st = validate(dims, varlen, &geo);
   if (st != HS2_OK) return st;
-  *bytes_out = (op == HS2_OP_SPARSE || geo.T == 0) ? 0 : geo.select_bytes;
+  if (geo.T == 0 || op == HS2_OP_SPARSE) {
+    *bytes_out = 0;
+  } else if (op == HS2_OP_SPARSE_PLAN) {
+    if (!geo.plan_ok) return HS2_ERR_UNSUPPORTED;
+    *bytes_out = geo.plan_bytes;
+  } else if (op == HS2_OP_PREFILL_BLOCK) {
+    *bytes_out = std::max(geo.select_bytes, geo.plan_ok ? geo.plan_bytes : 0);
+  } else {
+    *bytes_out = geo.select_bytes;
+  }
   return HS2_OK;
 }
 
@@ -422,6 +495,33 @@ int hs2_sparse_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
                     static_cast<hipStream_t>(stream));
 }
 
+int hs2_sparse_plan(const hs2_dims* dims, const hs2_varlen* varlen, const int32_t* idx,
+                    void* plan, size_t plan_bytes, void* stream) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (geo.T == 0) return HS2_OK;
+  if (!geo.plan_ok) return HS2_ERR_UNSUPPORTED;
+  if (!idx) return HS2_ERR_INVALID_ARG;
+  if (!plan || plan_bytes < geo.plan_bytes) return HS2_ERR_WORKSPACE;
+  return run_plan(dims, varlen, geo, idx, plan, static_cast<hipStream_t>(stream));
+}
+
+
+int hs2_sparse_attn_planned(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
+                            const void* k, const void* v, const void* plan, size_t plan_bytes,
+                            void* out, int out_dtype, void* stream) {
+  return run_planned(dims, varlen, q, k, v, plan, plan_bytes, out, out_dtype, stream, nullptr);
+}
+
+int hs2_sparse_attn_planned_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
+                                const uint8_t* k8, const uint8_t* v8, float k_scale,
+                                float v_scale, const void* plan, size_t plan_bytes, void* out,
+                                int out_dtype, void* stream) {
+  const float scales[2] = {k_scale, v_scale};
+  return run_planned(dims, varlen, q, k8, v8, plan, plan_bytes, out, out_dtype, stream, scales);
+}
+
 int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void* q_full,
                       const void* k, const void* v, int n_sparse,
                       const void* const* q_sparse_host_array, void* const* out_sparse_host_array,
@@ -442,9 +542,17 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_select(dims, varlen, geo, q_full, k, idx_out, nullptr, workspace, s);
   if (st != HS2_OK) return st;
+  // the sparse layers share one gather plan, written over the selection's scratch
+  // (stream order: the selection is done with it) when the workspace holds it
+  const void* plan = nullptr;
+  if (n_sparse > 0 && geo.plan_ok && workspace_bytes >= geo.plan_bytes) {
+    st = run_plan(dims, varlen, geo, idx_out, workspace, s);
+    if (st != HS2_OK) return st;
+    plan = workspace;
+  }
   for (int i = 0; i < n_sparse; i++) {
     st = run_sparse(dims, varlen, geo, q_sparse_host_array[i], k, v, idx_out,
-                    out_sparse_host_array[i], out_dtype, s);
+                    out_sparse_host_array[i], out_dtype, s, nullptr, plan);
     if (st != HS2_OK) return st;
   }
   return HS2_OK;

@@ -76,6 +76,19 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trip):
+// scans within each 16-lane row, then row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int x, int l) {
+  (void)l;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Order LDS traffic of one wavefront (its own writes become visible to its own
 // later reads); a barrier for the compiler and the memory model, not a
 // workgroup barrier.

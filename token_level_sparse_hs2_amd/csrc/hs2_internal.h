@@ -155,6 +155,34 @@ struct SparseParams {
   int n_part;           // 1 = one wave per row, output written directly
   float* part_o;        // [T * n_part * Hkv, G, 128] partial P.V (fp32)
   float2* part_ml;      // [T * n_part * Hkv, G] (reference, sum) of each partial
+  // shared-gather plan (prefill): one wave per (token group, g) walks the union of
+  // the group's index rows (see SparsePlan); plist null = one wave per (token, g)
+  const uint32_t* plist;  // [n_grp * Hkv, pcap] row - base0 | token mask << 24
+  const int32_t* pcount;  // [n_grp * Hkv] entries of each union
+  int pcap;
+  int64_t n_grp;
+};
+
+// Shared-gather plan. Consecutive query tokens select largely the same rows (the
+// forced window, and keys that score high for all of them), so the NT = 16 / G
+// (at most 8) tokens t0 .. t0 + NT - 1 of the packed batch are served by one wave:
+// the sorted union of their index rows is gathered once, and the S^T tiles take
+// the NT * G (token, head) columns. An entry is one word: the row relative to the
+// sequence base of token t0 (below max_seqlen + 16 < 2^24) in bits 0-23 and the
+// mask of the tokens whose row holds it in bits 24-31.
+__host__ __device__ constexpr int plan_tokens(int G) { return G >= 2 ? 16 / G : 8; }
+constexpr uint32_t kPlanRowMask = 0xFFFFFFu;
+constexpr int kPlanChunk = 4096;  // row positions per bitmap pass of the plan kernel
+
+struct PlanParams {
+  const int32_t* idx;   // [T, Hkv, KW] rows as written by the selection
+  const int32_t* cu;
+  int B, Hkv, KW;
+  int64_t T;
+  int64_t n_grp;        // ceil(T / NT)
+  int cap;              // NT * KW entries per union
+  uint32_t* list;       // [n_grp * Hkv, cap]
+  int32_t* count;       // [n_grp * Hkv]
 };
 
 // Decode step: one query per sequence at its last cached position.
@@ -213,6 +241,7 @@ hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t 
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, hipStream_t s);
+hipError_t launch_sparse_plan(int G, const PlanParams& p, hipStream_t s);
 // dst[i] = E4M3(float(src[i]) * inv_scale), round to nearest even, saturating at +-448
 hipError_t launch_quantize_fp8(const uint16_t* src, uint8_t* dst, int64_t n, float inv_scale,
                                hipStream_t s);

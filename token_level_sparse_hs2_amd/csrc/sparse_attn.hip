@@ -56,11 +56,14 @@ __device__ __forceinline__ float bank_bcast(float x) {
 // CH index entries per step: 32 for a bf16 cache; 16 for an FP8 one, which halves
 // the LDS slice and the staging registers so that four waves per SIMD fit (measured
 // 5% faster there; a bf16 cache at 16 entries and three waves was 1.6% slower).
-// MT = CH / 16 key tiles per step.
-template <int G, bool PRECISE, bool FP8, int CH>
-__global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn_kernel(
+// MT = CH / 16 key tiles per step. PLAN: one wave per (token group, g) over the
+// group's shared-gather union (SparseParams::plist); the S^T columns are the NT
+// tokens' G heads, and an entry counts for the tokens in its mask only.
+template <int G, bool PRECISE, bool FP8, int CH, bool PLAN>
+__global__ __launch_bounds__(256, CH == 16 ? (FP8 && !PLAN ? 4 : 3) : 2) void sparse_attn_kernel(
     SparseParams p) {
   constexpr int MT = CH / 16, NR = CH / 4;
+  constexpr int NT = PLAN ? plan_tokens(G) : 1;  // query tokens per wave
   __shared__ uint4 klds[4][CH][16];  // per wave: CH K rows x 256 B, swizzled 16-byte chunks
   __shared__ uint4 vlds[4][CH][16];  // per wave: CH V rows
   // the wave index is uniform: row, sequence and K/V row pointers live in SGPRs,
@@ -69,30 +72,36 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   const int lq = l >> 4, lc = l & 15;
   const int Hkv = p.Hkv, Hq = p.Hq, KW = p.KW;
   const int g = blockIdx.x % Hkv;
-  const int64_t vr = (int64_t)(blockIdx.x / Hkv) * 4 + w;  // row x part
-  if (vr >= p.T * p.n_part) return;
-  const int64_t tg = vr / p.n_part;
-  const int part = (int)(vr % p.n_part);
+  const int64_t vr = (int64_t)(blockIdx.x / Hkv) * 4 + w;  // row x part, or token group
+  if (vr >= (PLAN ? p.n_grp : p.T * p.n_part)) return;
+  const int64_t tg = PLAN ? vr * NT : vr / p.n_part;  // the (first) query row
+  const int part = PLAN ? 0 : (int)(vr % p.n_part);
   // query row tg: a token of the packed batch, or (decode) sequence tg at its
-  // last cached position
+  // last cached position (PLAN: rows of the union are relative to this base)
   const int seq = p.decode ? (int)tg : find_seq(p.cu, p.B, tg);
   const int base = p.cu[seq];
   const int t = p.decode ? p.cu[seq + 1] - base - 1 : (int)(tg - base);
   const int32_t* irow = p.idx + ((size_t)tg * Hkv + g) * KW;
+  const uint32_t* prow = PLAN ? p.plist + ((size_t)vr * Hkv + g) * p.pcap : nullptr;
+  const int n_ent = PLAN ? p.pcount[(size_t)vr * Hkv + g] : KW;  // index entries of the wave
   const float c = p.c;
+  // S^T column lc: head lc < G of token tg, or (PLAN) head lc % G of token tg + lc / G
+  const int col_tok = PLAN ? lc / G : 0;
+  const bool col_ok = PLAN ? lc < NT * G && tg + col_tok < p.T : lc < G;
 
-  // Q'^T operand (B): column = head (lane & 15) < G, k = d slice (loads first,
-  // columns >= G zeroed afterwards)
+  // Q'^T operand (B): column lc, k = d slice (loads first, columns without a
+  // (token, head) zeroed afterwards)
   bf16x8 qb[4];
   {
+    const int64_t qrow = PLAN ? min(tg + min(col_tok, NT - 1), p.T - 1) : tg;
+    const int qh = PLAN ? lc % G : min(lc, G - 1);
     u32x4 v[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
-      v[ks] = to_u32x4(ldg128(p.q + ((size_t)tg * Hq + g * G + min(lc, G - 1)) * kHeadDim +
-                              32 * ks + 8 * lq));
+      v[ks] = to_u32x4(ldg128(p.q + ((size_t)qrow * Hq + g * G + qh) * kHeadDim + 32 * ks + 8 * lq));
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-      if (lc >= G) v[ks] = u32x4{0u, 0u, 0u, 0u};
+      if (!col_ok) v[ks] = u32x4{0u, 0u, 0u, 0u};
       qb[ks] = as_bf16x8(v[ks]);
     }
   }
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   // lane's share (reduced over the banks at the end) and mc the reference m of
   // head (lane & 3). (16-entry steps keep the plain layout: there the saving is
   // smaller and the extra registers spill under four waves per SIMD.)
-  constexpr bool kCompact = G <= 4 && MT == 2;
+  constexpr bool kCompact = !PLAN && G <= 4 && MT == 2;
   float m = -INFINITY, mc = -INFINITY, lsum = 0.f;
   f32x4 o[8];
 #pragma unroll
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   vseq += ((size_t)base * Hkv + g) * kHeadDim * kElemBytes;
   const uint32_t row_stride = (uint32_t)Hkv * kHeadDim * kElemBytes;
   uint4(*vl)[16] = vlds[w];
-  const int n_chunks = (KW + CH - 1) / CH;
+  const int n_chunks = (n_ent + CH - 1) / CH;
   // this wave's steps: all of them, or its part's share
   const int per_part = (n_chunks + p.n_part - 1) / p.n_part;
   const int c_begin = part * per_part, c_end = min(n_chunks, c_begin + per_part);
@@ -128,17 +137,30 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   // load is unconditional (clamped to a valid entry) and its value is only used
   // two chunks later by valid_idx(); loads skipped on some path, or consumed at
   // once, would make the compiler drain the gather in flight behind them.
-  auto load_raw = [&](int c, int (&r)[MT]) {
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) r[mt] = irow[min(c * CH + 16 * mt + lc, KW - 1)];
-  };
-  auto valid_idx = [&](int c, const int (&r)[MT], int (&j)[MT]) {
+  // (PLAN: an entry is (row, token mask); mk gets the mask, 0 for no entry)
+  using Raw = std::conditional_t<PLAN, uint32_t, int>;
+  auto load_raw = [&](int c, Raw (&r)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
-      const int e = c * CH + 16 * mt + lc;
-      j[mt] = (c < c_end && e < KW) ? r[mt] : -1;
+      if constexpr (PLAN) r[mt] = prow[max(0, min(c * CH + 16 * mt + lc, n_ent - 1))];
+      else r[mt] = irow[min(c * CH + 16 * mt + lc, KW - 1)];
     }
   };
+  auto valid_idx = [&](int c, const Raw (&r)[MT], int (&j)[MT], uint32_t (&mk)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const bool ok = c < c_end && c * CH + 16 * mt + lc < n_ent;
+      if constexpr (PLAN) {
+        j[mt] = ok ? (int)(r[mt] & kPlanRowMask) : -1;
+        mk[mt] = ok ? r[mt] >> 24 : 0u;
+      } else {
+        j[mt] = ok ? r[mt] : -1;
+        mk[mt] = 0u;
+      }
+    }
+  };
+  // an entry to gather: PLAN rows are valid by construction, others lie in [0, t]
+  auto entry_ok = [&](int j) HS2_INLINE { return PLAN ? j >= 0 : (j >= 0 && j <= t); };
   // gather the chunk's K and V rows, fully coalesced: load r covers keys
   // 4r .. 4r+3, 16 lanes per row (lane: key 4r + lq, elements 8 lc .. 8 lc + 7:
   // 16 bytes of a bf16 row, 8 bytes of an FP8 one)
@@ -152,7 +174,7 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     int roff[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
-      roff[mt] = (int)((uint32_t)(j[mt] >= 0 && j[mt] <= t ? j[mt] : 0) * row_stride);
+      roff[mt] = (int)((uint32_t)(entry_ok(j[mt]) ? j[mt] : 0) * row_stride);
 #pragma unroll
     for (int r = 0; r < NR; r++) {
       const int key = 4 * r + lq;  // entry of the chunk; its offset is held by lane (key & 15)
@@ -180,11 +202,11 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   constexpr int NSPLIT = PRECISE ? 3 : 2;
   constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
 
-  auto consume = [&](const int (&j)[MT], const Gather& gb) {
+  auto consume = [&](const int (&j)[MT], const uint32_t (&mk)[MT], const Gather& gb) {
     uint64_t bal[MT], any = 0, all = ~0ull;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
-      bal[mt] = __ballot(j[mt] >= 0 && j[mt] <= t);
+      bal[mt] = __ballot(entry_ok(j[mt]));
       any |= bal[mt];
       all &= bal[mt];
     }
@@ -212,7 +234,23 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
         s[mt] = mfma16x16x32(ka, qb[ks], s[mt]);
       }
     }
-    if (!full) {  // entry 16*mt + 4*lq + i is valid iff bit (4*lq + i) of the ballot
+    if constexpr (PLAN) {
+      // entry 16*mt + 4*lq + i counts for column lc iff its mask holds token col_tok:
+      // bit (4*lq + i) of that token's ballot
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        uint64_t mine = 0;
+#pragma unroll
+        for (int a = 0; a < NT; a++) {
+          const uint64_t b = __ballot(entry_ok(j[mt]) && ((mk[mt] >> a) & 1u));
+          mine = col_tok == a ? b : mine;
+        }
+        const uint32_t bits = (uint32_t)(mine >> (4 * lq)) & 0xFu;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (!((bits >> i) & 1u)) s[mt][i] = -INFINITY;
+      }
+    } else if (!full) {  // entry 16*mt + 4*lq + i is valid iff bit (4*lq + i) of the ballot
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
@@ -224,12 +262,13 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     if constexpr (MT == 2)
       mx = fmaxf(mx, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = max_xor32(max_xor16(mx));
-    mx *= c;  // finite: the chunk has a valid entry
+    mx *= c;  // finite when the column has an entry in the chunk (always, unless PLAN)
     // the reference m only moves when a score passes it by the slack (never
-    // overflows: terms stay below 2^slack); moving it rescales l and O
+    // overflows: terms stay below 2^slack); moving it rescales l and O. (PLAN: a
+    // column without entries so far keeps m = -inf, alpha 1.)
     if (__any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
+      const float alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
 #pragma unroll
       for (int i = 0; i < 8; i++) o[i] *= alpha;
       m = m_new;
@@ -269,11 +308,13 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
         pk[part][2 * MT - 1] = from_bank<3>(pc, pc);
       }
     } else {
+      // (PLAN: a column still at m = -inf has only -inf scores here; weight 0)
+      const float mref = PLAN ? (m > -INFINITY ? m : 0.f) : m;
       float pv[4 * MT];
       float psum = 0.f;
 #pragma unroll
       for (int sidx = 0; sidx < 4 * MT; sidx++) {
-        pv[sidx] = fast_exp2(fmaf(s[sidx >> 2][sidx & 3], c, -m));
+        pv[sidx] = fast_exp2(fmaf(s[sidx >> 2][sidx & 3], c, -mref));
         psum += pv[sidx];
       }
       lsum += psum;
@@ -330,28 +371,30 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   // software pipeline: while chunk c computes, the gather of chunk c+1 and the
   // index entries of chunks c+2 and c+3 are in flight. Entries past the row are
   // -1: their gathers read row 0 and are skipped.
-  int r1[MT], r2[MT], ja[MT], jb[MT];
+  Raw r0[MT], r1[MT], r2[MT];
+  int ja[MT], jb[MT];
+  uint32_t ma[MT], mb[MT];
   Gather ga, gb;
-  load_raw(c_begin, ja);
+  load_raw(c_begin, r0);
   load_raw(c_begin + 1, r1);
   load_raw(c_begin + 2, r2);
   // keep this issue order (as in the loop body: idx entries older than the gather
   // behind them), so the loop's waits can leave the gather in flight
   __builtin_amdgcn_sched_barrier(0);
-  valid_idx(c_begin, ja, ja);
+  valid_idx(c_begin, r0, ja, ma);
   gather(ja, ga);
   for (int c = c_begin; c < c_end; c += 2) {
-    valid_idx(c + 1, r1, jb);
+    valid_idx(c + 1, r1, jb, mb);
     gather(jb, gb);
     load_raw(c + 3, r1);
-    consume(ja, ga);
+    consume(ja, ma, ga);
     // no early exit here: a chunk past the row has no valid entry and is skipped
     // by consume(), and one exit keeps every path through the loop issuing the
     // same loads in the same order
-    valid_idx(c + 2, r2, ja);
+    valid_idx(c + 2, r2, ja, ma);
     gather(ja, ga);
     load_raw(c + 4, r2);
-    consume(jb, gb);
+    consume(jb, mb, gb);
   }
   if constexpr (kCompact) {  // the banks' shares of each head
     lsum += shfl_xor_f(lsum, 4);
@@ -360,7 +403,7 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
   const float osc = FP8 ? p.v_scale : 1.f;  // the value scale, outside the sums
-  if (p.n_part > 1) {  // unnormalised partial of this part (m = -inf, sum 0 if it had none)
+  if (!PLAN && p.n_part > 1) {  // unnormalised partial of this part (m = -inf, sum 0 if it had none)
     if (lc < G) {
       const size_t slot = (size_t)vr * Hkv + g;
       float* po = p.part_o + (slot * G + lc) * kHeadDim;
@@ -371,9 +414,9 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 ? 4 : 3) : 2) void sparse_attn
     }
     return;
   }
-  if (lc < G) {
+  if (col_ok) {
     const float inv = lsum > 0.f ? osc / lsum : 0.f;
-    const size_t ob = ((size_t)tg * Hq + g * G + lc) * kHeadDim;
+    const size_t ob = ((size_t)(tg + col_tok) * Hq + g * G + (PLAN ? lc % G : lc)) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
       const int d0 = 16 * dt + 4 * lq;
@@ -429,19 +472,33 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine_kernel(SparseParams p
   else static_cast<__bf16*>(p.out)[o] = (__bf16)val;
 }
 
+template <int G, bool PLAN>
+static void launch_sparse_kernel(bool precise, bool fp8, dim3 grid, const SparseParams& p,
+                                 hipStream_t s) {
+  const dim3 block(256);
+  if (fp8) {
+    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, true, 16, PLAN>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, true, 16, PLAN>), grid, block, 0, s, p);
+  } else {
+    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, false, 32, PLAN>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, false, 32, PLAN>), grid, block, 0, s, p);
+  }
+}
+
 template <int G>
 static hipError_t launch_sparse_g(bool precise, bool fp8, const SparseParams& p, hipStream_t s) {
+  if (p.plist) {  // shared-gather plan: 4 token groups per workgroup, one KV group each
+    if (p.n_part != 1) return hipErrorInvalidValue;
+    const int64_t blocks = ((p.n_grp + 3) / 4) * p.Hkv;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    launch_sparse_kernel<G, true>(precise, fp8, dim3((unsigned)blocks), p, s);
+    return hipGetLastError();
+  }
   const int64_t blocks = ((p.T * p.n_part + 3) / 4) * p.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (fp8) {
-    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, true, 16>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, true, 16>), grid, block, 0, s, p);
-  } else {
-    if (precise) hipLaunchKernelGGL((sparse_attn_kernel<G, true, false, 32>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_attn_kernel<G, false, false, 32>), grid, block, 0, s, p);
-  }
+  launch_sparse_kernel<G, false>(precise, fp8, dim3((unsigned)blocks), p, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_part <= 1) return e;
   const int64_t blocks_c = p.T * p.Hkv * G;  // (row, group, head)
@@ -459,6 +516,126 @@ hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, h
     case 4: return launch_sparse_g<4>(precise, fp8, p, s);
     case 8: return launch_sparse_g<8>(precise, fp8, p, s);
     case 16: return launch_sparse_g<16>(precise, fp8, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Shared-gather plan: one wavefront per (token group, KV group g). The group's
+// rows are walked in windows of kPlanChunk positions (relative to base0, the
+// sequence base of its first token): each token's entries of the window set bits
+// in its LDS bitmap (its row is ascending, so a cursor marks where the next window
+// starts; -1 ends a row, entries past t are skipped), then the union of the bitmaps is
+// compacted in ascending order with one wave scan, each entry carrying the mask of
+// the tokens that hold it.
+template <int NT>
+__global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
+  constexpr int kWords = kPlanChunk / 32;
+  __shared__ uint32_t bms[4][NT][kWords];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint32_t(*bm)[kWords] = bms[w];
+  const int64_t wid = (int64_t)blockIdx.x * 4 + w;  // grp * Hkv + g
+  if (wid >= p.n_grp * p.Hkv) return;
+  const int64_t grp = wid / p.Hkv;
+  const int g = (int)(wid % p.Hkv);
+  const int64_t tg0 = grp * NT;
+  const int nt = (int)min<int64_t>(NT, p.T - tg0);
+  const int base0 = p.cu[find_seq(p.cu, p.B, tg0)];
+  // token a: its row, its position t and its sequence base relative to base0
+  const int32_t* row[NT];
+  int t_of[NT], off[NT], cur[NT];
+#pragma unroll
+  for (int a = 0; a < NT; a++) {
+    const int64_t tg = tg0 + min(a, nt - 1);
+    const int base = p.cu[find_seq(p.cu, p.B, tg)];
+    row[a] = p.idx + ((size_t)tg * p.Hkv + g) * p.KW;
+    t_of[a] = (int)(tg - base);
+    off[a] = base - base0;
+    cur[a] = a < nt ? 0 : p.KW;  // tokens past the batch hold nothing
+  }
+  const int rel_max = (int)(tg0 + nt - 1 - base0);  // no entry lies past the last token
+  uint32_t* list = p.list + (size_t)wid * p.cap;
+  int out = 0;
+  for (int lo = 0; lo <= rel_max; lo += kPlanChunk) {
+    const int hi = lo + kPlanChunk;
+#pragma unroll
+    for (int a = 0; a < NT; a++)
+      for (int i = l; i < kWords; i += 64) bm[a][i] = 0u;
+    wave_lds_fence();
+#pragma unroll
+    for (int a = 0; a < NT; a++) {
+      while (cur[a] < p.KW) {
+        const int e = cur[a] + l;
+        const int j = e < p.KW ? row[a][e] : -1;
+        const bool valid = e < p.KW && j >= 0 && j <= t_of[a];
+        const int rel = off[a] + j;
+        const bool in = valid && rel < hi;
+        if (in && rel >= lo) atomicOr(&bm[a][(rel - lo) >> 5], 1u << ((rel - lo) & 31));
+        // the row is ascending: the entries below hi lead. The first other one is at
+        // or past hi (kept for a later window), -1 (the padding that ends the row) or
+        // past t (stepped over)
+        const uint64_t lead = __ballot(in);
+        const int n_lead = lead == ~0ull ? 64 : __builtin_ctzll(~lead);
+        const int stop = e - l + n_lead;  // the entry that ended the run (uniform)
+        if (n_lead == 64) { cur[a] = stop; continue; }
+        const int js = stop < p.KW ? row[a][stop] : -1;
+        if (js < 0) { cur[a] = p.KW; break; }
+        if (js <= t_of[a]) { cur[a] = stop; break; }
+        cur[a] = stop + 1;
+      }
+    }
+    wave_lds_fence();
+    // lane l owns words [l * per, l * per + per) of the union
+    constexpr int per = kWords / 64;
+    uint32_t u[per];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < per; q++) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int a = 0; a < NT; a++) x |= bm[a][per * l + q];
+      u[q] = x;
+      cnt += __popc(x);
+    }
+    const int incl = wave_incl_scan(cnt, l);
+    const int total = __shfl(incl, 63, 64);
+    int o = out + incl - cnt;
+#pragma unroll
+    for (int q = 0; q < per; q++) {
+      const int wi = per * l + q;
+      uint32_t m = u[q];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1;
+        uint32_t mask = 0u;
+#pragma unroll
+        for (int a = 0; a < NT; a++) mask |= ((bm[a][wi] >> b) & 1u) << a;
+        if (o < p.cap) list[o] = (uint32_t)(lo + 32 * wi + b) | mask << 24;
+        o++;
+      }
+    }
+    out += total;
+    wave_lds_fence();
+  }
+  if (l == 0) p.count[wid] = min(out, p.cap);
+}
+
+template <int NT>
+static hipError_t launch_plan_nt(const PlanParams& p, hipStream_t s) {
+  const int64_t waves = p.n_grp * p.Hkv;
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sparse_plan_kernel<NT>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_plan(int G, const PlanParams& p, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_plan_nt<8>(p, s);
+    case 2: return launch_plan_nt<8>(p, s);
+    case 4: return launch_plan_nt<4>(p, s);
+    case 8: return launch_plan_nt<2>(p, s);
+    case 16: return launch_plan_nt<1>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
