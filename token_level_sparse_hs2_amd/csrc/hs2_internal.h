@@ -172,7 +172,7 @@ struct SparseParams {
 // mask of the tokens whose row holds it in bits 24-31.
 __host__ __device__ constexpr int plan_tokens(int G) { return G >= 2 ? 16 / G : 8; }
 constexpr uint32_t kPlanRowMask = 0xFFFFFFu;
-constexpr int kPlanChunk = 4096;  // row positions per bitmap pass of the plan kernel
+constexpr int kPlanChunk = 8192;  // row positions per bitmap pass of the plan kernel
 
 struct PlanParams {
   const int32_t* idx;   // [T, Hkv, KW] rows as written by the selection

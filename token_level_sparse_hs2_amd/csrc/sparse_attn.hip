@@ -523,16 +523,25 @@ hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, h
 // Shared-gather plan: one wavefront per (token group, KV group g). The group's
 // rows are walked in windows of kPlanChunk positions (relative to base0, the
 // sequence base of its first token): each token's entries of the window set bits
-// in its LDS bitmap (its row is ascending, so a cursor marks where the next window
-// starts; -1 ends a row, entries past t are skipped), then the union of the bitmaps is
-// compacted in ascending order with one wave scan, each entry carrying the mask of
-// the tokens that hold it.
+// in its LDS bitmap, then the union of the bitmaps is compacted in ascending
+// order with one wave scan, each entry carrying the mask of the tokens that hold
+// it. A row is ascending, so a cursor per token marks where the next window
+// starts; -1 ends a row, entries past t are stepped over. Each round loads the
+// next 256 entries of every unfinished row (4 per lane, all issued before any
+// use), so a window costs about one memory round trip. The union is written by
+// rank: lane l takes entries l, l + 64, ... (its word by a binary search over the
+// words' prefix counts, its bit by a popcount select), so the work is balanced
+// over the lanes however the entries cluster, and the stores are coalesced.
 template <int NT>
 __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
   constexpr int kWords = kPlanChunk / 32;
   __shared__ uint32_t bms[4][NT][kWords];
+  __shared__ uint32_t uws[4][kWords];   // union words of the window
+  __shared__ int32_t pres[4][kWords];   // entries of the union in the words before
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint32_t(*bm)[kWords] = bms[w];
+  uint32_t* uw = uws[w];
+  int32_t* pre = pres[w];
   const int64_t wid = (int64_t)blockIdx.x * 4 + w;  // grp * Hkv + g
   if (wid >= p.n_grp * p.Hkv) return;
   const int64_t grp = wid / p.Hkv;
@@ -540,6 +549,7 @@ __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
   const int64_t tg0 = grp * NT;
   const int nt = (int)min<int64_t>(NT, p.T - tg0);
   const int base0 = p.cu[find_seq(p.cu, p.B, tg0)];
+  const int KW = p.KW;
   // token a: its row, its position t and its sequence base relative to base0
   const int32_t* row[NT];
   int t_of[NT], off[NT], cur[NT];
@@ -547,10 +557,10 @@ __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
   for (int a = 0; a < NT; a++) {
     const int64_t tg = tg0 + min(a, nt - 1);
     const int base = p.cu[find_seq(p.cu, p.B, tg)];
-    row[a] = p.idx + ((size_t)tg * p.Hkv + g) * p.KW;
+    row[a] = p.idx + ((size_t)tg * p.Hkv + g) * KW;
     t_of[a] = (int)(tg - base);
     off[a] = base - base0;
-    cur[a] = a < nt ? 0 : p.KW;  // tokens past the batch hold nothing
+    cur[a] = a < nt ? 0 : KW;  // tokens past the batch hold nothing
   }
   const int rel_max = (int)(tg0 + nt - 1 - base0);  // no entry lies past the last token
   uint32_t* list = p.list + (size_t)wid * p.cap;
@@ -561,26 +571,63 @@ __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
     for (int a = 0; a < NT; a++)
       for (int i = l; i < kWords; i += 64) bm[a][i] = 0u;
     wave_lds_fence();
+    bool pending[NT];
 #pragma unroll
-    for (int a = 0; a < NT; a++) {
-      while (cur[a] < p.KW) {
-        const int e = cur[a] + l;
-        const int j = e < p.KW ? row[a][e] : -1;
-        const bool valid = e < p.KW && j >= 0 && j <= t_of[a];
-        const int rel = off[a] + j;
-        const bool in = valid && rel < hi;
-        if (in && rel >= lo) atomicOr(&bm[a][(rel - lo) >> 5], 1u << ((rel - lo) & 31));
-        // the row is ascending: the entries below hi lead. The first other one is at
-        // or past hi (kept for a later window), -1 (the padding that ends the row) or
-        // past t (stepped over)
-        const uint64_t lead = __ballot(in);
-        const int n_lead = lead == ~0ull ? 64 : __builtin_ctzll(~lead);
-        const int stop = e - l + n_lead;  // the entry that ended the run (uniform)
-        if (n_lead == 64) { cur[a] = stop; continue; }
-        const int js = stop < p.KW ? row[a][stop] : -1;
-        if (js < 0) { cur[a] = p.KW; break; }
-        if (js <= t_of[a]) { cur[a] = stop; break; }
-        cur[a] = stop + 1;
+    for (int a = 0; a < NT; a++) pending[a] = cur[a] < KW;
+    for (;;) {
+      bool any = false;
+#pragma unroll
+      for (int a = 0; a < NT; a++) any |= pending[a];
+      if (!any) break;
+      // entries cur + 64 i + l of every pending row
+      int j[NT][4];
+#pragma unroll
+      for (int a = 0; a < NT; a++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int e = cur[a] + 64 * i + l;
+          j[a][i] = pending[a] && e < KW ? row[a][e] : -1;
+        }
+#pragma unroll
+      for (int a = 0; a < NT; a++) {
+        if (!pending[a]) continue;
+        int n_lead = 0;
+        bool stopped = false;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int jj = j[a][i];
+          const int rel = off[a] + jj;
+          const bool in = jj >= 0 && jj <= t_of[a] && rel < hi;
+          if (in && rel >= lo) atomicOr(&bm[a][(rel - lo) >> 5], 1u << ((rel - lo) & 31));
+          const uint64_t lead = __ballot(in);
+          if (!stopped) {
+            if (lead == ~0ull) {
+              n_lead += 64;
+            } else {
+              n_lead += __builtin_ctzll(~lead);
+              stopped = true;
+            }
+          }
+        }
+        const int stop = cur[a] + n_lead;  // the entry that ended the run (uniform)
+        if (!stopped) {  // all 256 below hi: another round
+          cur[a] = stop;
+          continue;
+        }
+        // the stopping entry was loaded: entry n_lead of this round
+        const int si = n_lead >> 6;
+        const int sv = si == 0 ? j[a][0] : si == 1 ? j[a][1] : si == 2 ? j[a][2] : j[a][3];
+        const int js = __shfl(sv, n_lead & 63, 64);
+        if (js < 0) {  // -1 padding (or the end): the row is done
+          cur[a] = KW;
+          pending[a] = false;
+        } else if (js <= t_of[a]) {  // at or past hi: the next window starts here
+          cur[a] = stop;
+          pending[a] = false;
+        } else {  // past t: step over it
+          cur[a] = stop + 1;
+          pending[a] = cur[a] < KW;
+        }
       }
     }
     wave_lds_fence();
@@ -598,20 +645,38 @@ __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
     }
     const int incl = wave_incl_scan(cnt, l);
     const int total = __shfl(incl, 63, 64);
-    int o = out + incl - cnt;
+    {
+      int o = incl - cnt;
 #pragma unroll
-    for (int q = 0; q < per; q++) {
-      const int wi = per * l + q;
-      uint32_t m = u[q];
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1;
-        uint32_t mask = 0u;
-#pragma unroll
-        for (int a = 0; a < NT; a++) mask |= ((bm[a][wi] >> b) & 1u) << a;
-        if (o < p.cap) list[o] = (uint32_t)(lo + 32 * wi + b) | mask << 24;
-        o++;
+      for (int q = 0; q < per; q++) {
+        uw[per * l + q] = u[q];
+        pre[per * l + q] = o;
+        o += __popc(u[q]);
       }
+    }
+    wave_lds_fence();
+    for (int r = l; r < total; r += 64) {
+      // the last word whose prefix is <= r holds entry r
+      int wlo = 0, whi = kWords - 1;
+      while (wlo < whi) {
+        const int mid = (wlo + whi + 1) >> 1;
+        if (pre[mid] <= r) wlo = mid; else whi = mid - 1;
+      }
+      uint32_t x = uw[wlo];
+      int k = r - pre[wlo], b = 0;  // the k-th set bit of x
+#pragma unroll
+      for (int width = 16; width >= 1; width >>= 1) {
+        const int c = __popc(x & ((1u << width) - 1u));
+        if (k >= c) {
+          k -= c;
+          x >>= width;
+          b += width;
+        }
+      }
+      uint32_t mask = 0u;
+#pragma unroll
+      for (int a = 0; a < NT; a++) mask |= ((bm[a][wlo] >> b) & 1u) << a;
+      if (out + r < p.cap) list[out + r] = (uint32_t)(lo + 32 * wlo + b) | mask << 24;
     }
     out += total;
     wave_lds_fence();
