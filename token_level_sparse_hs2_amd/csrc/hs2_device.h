@@ -89,6 +89,18 @@ __device__ __forceinline__ int wave_incl_scan(int x, int l) {
   return x;
 }
 
+// Inclusive max scan over the 64 lanes (values >= -1), the DPP moves of
+// wave_incl_scan with -1 where a move brings nothing.
+__device__ __forceinline__ int wave_incl_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return x;
+}
+
 // Order LDS traffic of one wavefront (its own writes become visible to its own
 // later reads); a barrier for the compiler and the memory model, not a
 // workgroup barrier.

@@ -529,19 +529,23 @@ hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, h
 // starts; -1 ends a row, entries past t are stepped over. Each round loads the
 // next 256 entries of every unfinished row (4 per lane, all issued before any
 // use), so a window costs about one memory round trip. The union is written by
-// rank: lane l takes entries l, l + 64, ... (its word by a binary search over the
-// words' prefix counts, its bit by a popcount select), so the work is balanced
-// over the lanes however the entries cluster, and the stores are coalesced.
+// rank, 64 entries at a time: lane l takes entry base + l (its word: the words
+// whose first entry falls in the block mark their slot, and a max scan over the
+// slots gives every rank the last word started at or before it; its bit by a
+// popcount select), so the work is balanced over the lanes however the entries
+// cluster, and the stores are coalesced.
 template <int NT>
 __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
   constexpr int kWords = kPlanChunk / 32;
   __shared__ uint32_t bms[4][NT][kWords];
   __shared__ uint32_t uws[4][kWords];   // union words of the window
   __shared__ int32_t pres[4][kWords];   // entries of the union in the words before
+  __shared__ int32_t slots[4][64];      // word starting at each rank of a block, or -1
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint32_t(*bm)[kWords] = bms[w];
   uint32_t* uw = uws[w];
   int32_t* pre = pres[w];
+  int32_t* slot = slots[w];
   const int64_t wid = (int64_t)blockIdx.x * 4 + w;  // grp * Hkv + g
   if (wid >= p.n_grp * p.Hkv) return;
   const int64_t grp = wid / p.Hkv;
@@ -645,38 +649,46 @@ __global__ __launch_bounds__(256) void sparse_plan_kernel(PlanParams p) {
     }
     const int incl = wave_incl_scan(cnt, l);
     const int total = __shfl(incl, 63, 64);
+    int pq[per];
     {
       int o = incl - cnt;
 #pragma unroll
       for (int q = 0; q < per; q++) {
         uw[per * l + q] = u[q];
         pre[per * l + q] = o;
+        pq[q] = o;
         o += __popc(u[q]);
       }
     }
-    wave_lds_fence();
-    for (int r = l; r < total; r += 64) {
-      // the last word whose prefix is <= r holds entry r
-      int wlo = 0, whi = kWords - 1;
-      while (wlo < whi) {
-        const int mid = (wlo + whi + 1) >> 1;
-        if (pre[mid] <= r) wlo = mid; else whi = mid - 1;
-      }
-      uint32_t x = uw[wlo];
-      int k = r - pre[wlo], b = 0;  // the k-th set bit of x
+    int carry = -1;  // the last word started before the block
+    for (int base = 0; base < total; base += 64) {
+      slot[l] = -1;
+      wave_lds_fence();
 #pragma unroll
-      for (int width = 16; width >= 1; width >>= 1) {
-        const int c = __popc(x & ((1u << width) - 1u));
-        if (k >= c) {
-          k -= c;
-          x >>= width;
-          b += width;
+      for (int q = 0; q < per; q++)
+        if (u[q] != 0u && pq[q] >= base && pq[q] < base + 64) slot[pq[q] - base] = per * l + q;
+      wave_lds_fence();
+      const int wlo = max(wave_incl_max(slot[l]), carry);  // the word holding entry base + l
+      carry = __shfl(wlo, 63, 64);
+      const int r = base + l;
+      if (r < total) {
+        uint32_t x = uw[wlo];
+        int k = r - pre[wlo], b = 0;  // the k-th set bit of x
+#pragma unroll
+        for (int width = 16; width >= 1; width >>= 1) {
+          const int c = __popc(x & ((1u << width) - 1u));
+          if (k >= c) {
+            k -= c;
+            x >>= width;
+            b += width;
+          }
         }
-      }
-      uint32_t mask = 0u;
+        uint32_t mask = 0u;
 #pragma unroll
-      for (int a = 0; a < NT; a++) mask |= ((bm[a][wlo] >> b) & 1u) << a;
-      if (out + r < p.cap) list[out + r] = (uint32_t)(lo + 32 * wlo + b) | mask << 24;
+        for (int a = 0; a < NT; a++) mask |= ((bm[a][wlo] >> b) & 1u) << a;
+        if (out + r < p.cap) list[out + r] = (uint32_t)(lo + 32 * wlo + b) | mask << 24;
+      }
+      wave_lds_fence();  // the slots are read before the next block resets them
     }
     out += total;
     wave_lds_fence();
