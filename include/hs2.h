@@ -188,8 +188,11 @@ int hs2_sparse_attn_planned(const hs2_dims* dims, const hs2_varlen* varlen, cons
  * The two pointer arrays live on the host and are read during the call. With a
  * workspace of hs2_workspace_size(HS2_OP_PREFILL_BLOCK) bytes the layers run
  * from one shared-gather plan (as hs2_sparse_plan + hs2_sparse_attn_planned,
- * the plan written over the selection's scratch); a workspace of only the
- * HS2_OP_SELECT size runs them as hs2_sparse_attn.
+ * the plan written over the selection's scratch) when n_sparse >= 2 or no
+ * sequence is longer than 32768 tokens (the plan's cost grows with the row
+ * positions; a single layer over longer rows does not recover it); otherwise,
+ * or with a workspace of only the HS2_OP_SELECT size, they run as
+ * hs2_sparse_attn.
  */
 int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void* q_full,
                       const void* k, const void* v, int n_sparse,

@@ -21,6 +21,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kPlanShortRows = 32768;  // hs2_prefill_block plans one layer up to this length
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Geometry {
@@ -543,9 +544,12 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
   st = run_select(dims, varlen, geo, q_full, k, idx_out, nullptr, workspace, s);
   if (st != HS2_OK) return st;
   // the sparse layers share one gather plan, written over the selection's scratch
-  // (stream order: the selection is done with it) when the workspace holds it
+  // (stream order: the selection is done with it) when the workspace holds it. The
+  // plan's cost grows with row positions: on rows up to kPlanShortRows it pays for
+  // itself within one layer, on longer ones it takes two
   const void* plan = nullptr;
-  if (n_sparse > 0 && geo.plan_ok && workspace_bytes >= geo.plan_bytes) {
+  const bool plan_pays = n_sparse >= 2 || geo.max_len <= kPlanShortRows;
+  if (plan_pays && geo.plan_ok && workspace_bytes >= geo.plan_bytes) {
     st = run_plan(dims, varlen, geo, idx_out, workspace, s);
     if (st != HS2_OK) return st;
     plan = workspace;
