@@ -148,6 +148,13 @@ def test_plan_ragged_varlen_every_group_size(G):
     run_plan_case(w)
 
 
+@pytest.mark.parametrize("lengths", [[1], [3], [1, 1, 1], [2, 1, 70]])
+def test_plan_batches_smaller_than_a_group(lengths):
+    """Fewer tokens than a group holds (4 at G = 4), several sequences in one group."""
+    w = synthgen.custom(lengths, Hq=8, Hkv=2, K=16, W=4, n_sparse=1, seed=320 + len(lengths))
+    run_plan_case(w)
+
+
 @pytest.mark.parametrize("K,W", [(0, 32), (256, 0), (1, 1)])
 def test_plan_budget_edges(K, W):
     w = synthgen.custom([5, 64, 65, 1500], Hq=8, Hkv=2, K=K, W=W, n_sparse=1, seed=310)
