@@ -228,17 +228,16 @@ def test_prefill_block_runs_the_plan():
         assert torch.equal(planned(case, plan, qs, False), ob)
 
 
-def test_32k_workload_planned_sampled():
-    """The bench configuration: the plan of every row checked against the host
-    union on a sample of token groups, the planned layer on sampled tokens."""
-    w = synthgen.workload("32k")
+def run_sampled_workload(name, head, tail, stride):
+    """A bench configuration: the unions of the groups holding sampled tokens checked
+    against the host union, the planned layer on the sampled tokens."""
+    w = synthgen.workload(name)
     w.n_sparse = 1
-    toks = sample_tokens(w.lengths, w.K, w.W, head=128, tail=16, stride=1021)
+    toks = sample_tokens(w.lengths, w.K, w.W, head=head, tail=tail, stride=stride)
     inp = synthgen.make_inputs(w)
     case = GpuCase(w, inp)
     idx_t, _ = case.select()
     plan = gpu_plan(case, idx_t)
-    # unions of the groups holding the sampled tokens
     G = w.Hq // w.Hkv
     NT = plan_tokens(G)
     T, KW = case.T, case.KW
@@ -250,7 +249,7 @@ def test_32k_workload_planned_sampled():
     counts = raw[off_count:off_count + lists * 4].view(np.int32)
     idx = idx_t.cpu().numpy()
     grps = np.unique(toks // NT)
-    for grp in grps:
+    for grp in grps:  # one sequence: rows relative to base 0 are the positions
         sub = idx[grp * NT:min(T, grp * NT + NT)]
         for g in range(w.Hkv):
             rows = sub[:, g]
@@ -262,5 +261,14 @@ def test_32k_workload_planned_sampled():
             assert counts[wid] == len(u)
             got = words[wid, :len(u)]
             assert (got & 0xFFFFFF == u).all() and (got >> 24 == um).all()
-    log(f"  {len(grps)} groups' unions exact; mean union {counts.mean():.0f} of {NT * KW}")
+    log(f"  {name}: {len(grps)} groups' unions exact; mean union {counts.mean():.0f} of {NT * KW}")
     check_planned_layers(case, idx_t, plan, tokens=toks)
+
+
+def test_32k_workload_planned_sampled():
+    run_sampled_workload("32k", head=128, tail=16, stride=1021)
+
+
+def test_128k_workload_planned_sampled():
+    """G = 8: two tokens per group."""
+    run_sampled_workload("128k", head=64, tail=8, stride=4093)
