@@ -17,6 +17,13 @@
 // the matrix product as a sum of bf16 parts (two parts: ~16 mantissa bits; three
 // in the precise mode: ~24 bits), so rounding P to bf16 adds no visible error.
 //
+// Shared gather (PLAN): consecutive tokens select largely the same rows (the
+// forced window, and keys that score high for all of them), so a wave can serve
+// the NT = min(16 / G, 8) tokens of a group over the sorted union of their rows,
+// built once per selection by sparse_plan_kernel: each union row is gathered once
+// and the S^T tiles take all NT * G (token, head) columns, an entry counting only
+// for the tokens whose row holds it, so each token's attention is unchanged.
+//
 // FP8 KV cache (HySparse2 news summary, cost paragraph: the cache kept in FP8):
 // E4M3 codes with one fp32 scale per tensor. A lane gathers its 8 codes of a
 // 128-byte row (the elements of its 16-byte chunk of the bf16 layout) and widens
