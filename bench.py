@@ -3,7 +3,9 @@
 One step = one hybrid module over the whole prompt: hs2_prefill_block, i.e. the
 full layer's token selection (row statistics, group scores, top-K + forced
 recent window, index rows) followed by every sparse layer reusing K/V and the
-index rows. Inputs are seeded synthetic bf16 tensors already resident in HBM.
+index rows (from one shared-gather plan of the rows where that pays: two or more
+layers, or rows up to 32768 tokens). Inputs are seeded synthetic bf16 tensors
+already resident in HBM.
 
 Default workload: B=1, L=32768, Hq=32, Hkv=8, d=128, K=1024, W=128, needle keys,
 1 select + 3 sparse layers. Prints one JSON line.
