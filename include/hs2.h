@@ -119,10 +119,12 @@ typedef struct {
 
 /*
  * Bytes of workspace an operation needs for these dimensions.
- * op: HS2_OP_SELECT, HS2_OP_SPARSE, HS2_OP_PREFILL_BLOCK, HS2_OP_DECODE_SELECT or
- * HS2_OP_DECODE_SPARSE (for the decode ops `varlen` describes the cache;
- * n_sparse is unused by the size). Returns HS2_OK and writes *bytes_out, or a
- * validation error.
+ * op: HS2_OP_SELECT, HS2_OP_SPARSE (0: the per-token layer needs none),
+ * HS2_OP_PREFILL_BLOCK (the larger of the selection's scratch and the plan),
+ * HS2_OP_SPARSE_PLAN (the plan buffer of hs2_sparse_plan; HS2_ERR_UNSUPPORTED
+ * when no plan is possible), HS2_OP_DECODE_SELECT or HS2_OP_DECODE_SPARSE (for
+ * the decode ops `varlen` describes the cache; n_sparse is unused by the size).
+ * Returns HS2_OK and writes *bytes_out, or a validation error.
  */
 int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, int n_sparse,
                        size_t* bytes_out);
