@@ -178,6 +178,25 @@ def test_plan_padded_rows_of_a_decaying_budget():
     assert (idx_t.cpu().numpy() < 0).any()
 
 
+@pytest.mark.parametrize("flag", ["block", "exact"])
+def test_plan_of_block_and_exact_rows(flag):
+    """Rows from the 64-token block selection (runs of 64 positions: dense bitmap
+    words) and from the exact path (every row ranked over its whole candidate range)."""
+    import torch
+
+    def select_flag(case):
+        hs2 = case.hs2
+        f = hs2.HS2_FLAG_BLOCK_SELECT if flag == "block" else hs2.HS2_FLAG_EXACT_SELECT
+        dims = hs2.make_dims(case.w.Hq, case.w.Hkv, case.w.K, case.w.W, case.w.scale, flags=f)
+        idx = case.new_idx()
+        hs2.hs2_select(dims, case.varlen, case.q_full, case.k, idx, None, case.workspace)
+        torch.cuda.synchronize()
+        return idx
+
+    w = synthgen.custom([70, 1500, 2600], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=313)
+    run_plan_case(w, select_fn=select_flag)
+
+
 def test_plan_fp8_cache():
     import oracle
     import torch
