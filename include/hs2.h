@@ -78,7 +78,8 @@ enum {
   HS2_OP_PREFILL_BLOCK = 3,
   HS2_OP_DECODE_SELECT = 4,
   HS2_OP_DECODE_SPARSE = 5,
-  HS2_OP_SPARSE_PLAN = 6  /* the plan buffer of hs2_sparse_plan */
+  HS2_OP_SPARSE_PLAN = 6, /* the plan buffer of hs2_sparse_plan */
+  HS2_OP_SELECT_MIN = 7   /* the smallest workspace the selection accepts (see below) */
 };
 
 /* Flags of hs2_dims.flags. */
@@ -119,37 +120,66 @@ typedef struct {
 
 /*
  * Bytes of workspace an operation needs for these dimensions.
- * op: HS2_OP_SELECT, HS2_OP_SPARSE (0: the per-token layer needs none),
- * HS2_OP_PREFILL_BLOCK (the larger of the selection's scratch and the plan),
- * HS2_OP_SPARSE_PLAN (the plan buffer of hs2_sparse_plan; HS2_ERR_UNSUPPORTED
- * when no plan is possible), HS2_OP_DECODE_SELECT or HS2_OP_DECODE_SPARSE (for
- * the decode ops `varlen` describes the cache; n_sparse is unused by the size).
- * Returns HS2_OK and writes *bytes_out, or a validation error.
+ * op:
+ *   HS2_OP_SELECT       the selection (hs2_select, hs2_select_ex, hs2_select_full):
+ *                       per-row statistics, candidate rows of one chunk of tasks
+ *                       (at most 4 GiB of candidates), exact-path scratch. A smaller
+ *                       workspace, down to HS2_OP_SELECT_MIN bytes, is accepted too:
+ *                       the selection then runs in more, smaller chunks with the
+ *                       same results.
+ *   HS2_OP_SELECT_MIN   the smallest selection workspace (one task per chunk).
+ *   HS2_OP_SPARSE       0: the per-token sparse layer needs no workspace.
+ *   HS2_OP_PREFILL_BLOCK  for hs2_prefill_block with n_sparse layers (n_sparse >= 0):
+ *                       the selection's size, or the plan's when larger and the
+ *                       block will plan its layers (n_sparse >= 2, or n_sparse == 1
+ *                       and no sequence longer than 32768 tokens).
+ *   HS2_OP_SPARSE_PLAN  the plan buffer of hs2_sparse_plan (HS2_ERR_UNSUPPORTED when
+ *                       no plan is possible for these dimensions).
+ *   HS2_OP_DECODE_SELECT, HS2_OP_DECODE_SPARSE  the decode ops (`varlen` describes
+ *                       the cache).
+ * n_sparse is read for HS2_OP_PREFILL_BLOCK only. Returns HS2_OK and writes
+ * *bytes_out, or a validation error (nothing written).
  */
 int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, int n_sparse,
                        size_t* bytes_out);
 
 /*
- * Token selection of the full-attention layer (steps: per-head row statistics,
- * group probability score, top-K outside the window, window forcing, index
- * assembly). q [T,Hq,128] bf16, k [T,Hkv,128] bf16 in; idx_out [T,Hkv,K+W]
- * int32 out. kth_score_out (nullable, device [T,Hkv] float): the score S of the
- * lowest-ranked selected global candidate, or -1 when every candidate was taken.
+ * Token selection of the full-attention layer. HySparse2 news summary: the
+ * paragraph on two-level KV sharing (the full layer's complete attention scores
+ * pick the tokens the sparse layers attend to), the token-granularity paragraph
+ * (single tokens, not blocks: 1024 global tokens plus the 128 most recent) and
+ * the forced-recent paragraph (the recent window is always kept); scores as the
+ * softmax of the SHARP walkthrough, section 1.1. Steps: per-head row statistics
+ * (m, l), group probability score S, top-K of the candidates [0, t-W], window
+ * forcing, ascending index row (definitions at the top of this file).
+ * q [T,Hq,128] bf16 (the full layer's queries), k [T,Hkv,128] bf16 in;
+ * idx_out [T,Hkv,K+W] int32 out. kth_score_out (nullable, device [T,Hkv] float):
+ * the score S of the lowest-ranked selected global candidate, or -1 when every
+ * candidate was taken. workspace: at least hs2_workspace_size(HS2_OP_SELECT_MIN)
+ * bytes, caller-owned, no initialisation needed. Errors: HS2_ERR_INVALID_ARG
+ * (a NULL q, k or idx_out with T > 0, or invalid dims / varlen),
+ * HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP.
  */
 int hs2_select(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
                int32_t* idx_out, float* kth_score_out, void* workspace, size_t workspace_bytes,
                void* stream);
 
 /*
- * One sparse attention layer over given index rows: q [T,Hq,128] bf16 (the
- * layer's own queries), k, v [T,Hkv,128] bf16 (the shared cache), idx
- * [T,Hkv,K+W] int32. Entries outside [0, t] are ignored; a row with no valid
- * entry gives a zero output. out [T,Hq,128]: bf16 (HS2_OUT_BF16) or float
- * (HS2_OUT_F32). Needs no workspace (workspace may be NULL, size 0).
+ * One sparse attention layer over given index rows. HySparse2 news summary, the
+ * KV Reuse paragraph: a sparse layer keeps no cache of its own and attends, with
+ * its own queries, over the positions the full layer selected in the full
+ * layer's K/V; the softmax is renormalised over those positions only (masking
+ * before the softmax, SHARP walkthrough section 2.3).
+ * q [T,Hq,128] bf16 (the layer's own queries), k, v [T,Hkv,128] bf16 (the
+ * shared cache), idx [T,Hkv,K+W] int32 (any order; repeats count twice).
+ * Entries outside [0, t] are ignored; a row with no valid entry gives a zero
+ * output. out [T,Hq,128]: bf16 (HS2_OUT_BF16) or float (HS2_OUT_F32), written
+ * for every token. Needs no workspace. Errors: HS2_ERR_INVALID_ARG (a NULL
+ * pointer with T > 0, a bad out_dtype, invalid dims / varlen),
+ * HS2_ERR_UNSUPPORTED, HS2_ERR_HIP.
  */
 int hs2_sparse_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
-                    const void* v, const int32_t* idx, void* out, int out_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    const void* v, const int32_t* idx, void* out, int out_dtype, void* stream);
 
 /*
  * Shared-gather plan of a selection's index rows, for the sparse layers that
@@ -184,17 +214,21 @@ int hs2_sparse_attn_planned(const hs2_dims* dims, const hs2_varlen* varlen, cons
                             void* out, int out_dtype, void* stream);
 
 /*
- * One hybrid module in prefill: hs2_select on (q_full, k) into idx_out, then
- * n_sparse sparse layers, layer i reading q_sparse_host_array[i] (device
- * pointer) and writing out_sparse_host_array[i], all sharing k, v and idx.
- * The two pointer arrays live on the host and are read during the call. With a
- * workspace of hs2_workspace_size(HS2_OP_PREFILL_BLOCK) bytes the layers run
- * from one shared-gather plan (as hs2_sparse_plan + hs2_sparse_attn_planned,
- * the plan written over the selection's scratch) when n_sparse >= 2 or no
- * sequence is longer than 32768 tokens (the plan's cost grows with the row
- * positions; a single layer over longer rows does not recover it); otherwise,
- * or with a workspace of only the HS2_OP_SELECT size, they run as
- * hs2_sparse_attn.
+ * One hybrid module in prefill (HySparse2 news summary, paragraph on two-level
+ * KV sharing: one full-attention layer followed by sparse layers that reuse its
+ * KV cache and its token selection): hs2_select on (q_full, k) into idx_out,
+ * then n_sparse >= 0 sparse layers, layer i reading q_sparse_host_array[i]
+ * (device pointer) and writing out_sparse_host_array[i], all sharing k, v and
+ * idx. The two pointer arrays live on the host and are read during the call.
+ * With a workspace of hs2_workspace_size(HS2_OP_PREFILL_BLOCK, n_sparse) bytes
+ * the layers run from one shared-gather plan (as hs2_sparse_plan +
+ * hs2_sparse_attn_planned, the plan written over the selection's scratch) when
+ * n_sparse >= 2, or n_sparse == 1 and no sequence is longer than 32768 tokens
+ * (the plan's cost grows with the row positions; a single layer over longer
+ * rows does not recover it); otherwise, or with a workspace too small for the
+ * plan, they run as hs2_sparse_attn. Errors as hs2_select and hs2_sparse_attn
+ * (HS2_ERR_INVALID_ARG also for n_sparse < 0 or a NULL layer pointer); all are
+ * detected before anything is enqueued.
  */
 int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void* q_full,
                       const void* k, const void* v, int n_sparse,
@@ -245,6 +279,22 @@ int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
                     int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The full layer's own attention output alone, without the selection (the
+ * first sweep of hs2_select_full; the full layer's softmax as in the SHARP
+ * walkthrough, section 1.1):
+ *   out[t,h] = sum_{j <= t} softmax_j(softmax_scale <q[t,h], k[j,g]>) v[j,g]
+ * q [T,Hq,128], k, v [T,Hkv,128] bf16; out [T,Hq,128] bf16 (HS2_OUT_BF16, P as
+ * one bf16 part) or float (HS2_OUT_F32, P as three parts). lse2_out (nullable,
+ * device [T,Hq] float): each row's base-2 log-sum-exp of the scaled logits,
+ * log2 sum_{j <= t} 2^(c <q[t,h], k[j,g]>) with c = softmax_scale * log2(e)
+ * (the natural-log value times 1/ln 2). Needs no workspace. Errors:
+ * HS2_ERR_INVALID_ARG (a NULL q, k, v or out with T > 0, a bad out_dtype,
+ * invalid dims / varlen), HS2_ERR_UNSUPPORTED, HS2_ERR_HIP.
+ */
+int hs2_full_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                  const void* v, void* out, int out_dtype, float* lse2_out, void* stream);
+
+/*
  * Decode step: one new token per sequence after the prompt (the cross-decoder
  * work HySparse2 moves to generation: HySparse2 news summary, early-exit
  * paragraph). `cache` describes the KV cache: sequence b holds L_b >= 1
@@ -288,11 +338,10 @@ int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const 
  */
 int hs2_quantize_fp8(const void* src, uint8_t* dst, int64_t n, float inv_scale, void* stream);
 
-/* hs2_sparse_attn over an FP8 cache (same q, idx, out, workspace and errors). */
+/* hs2_sparse_attn over an FP8 cache (same q, idx, out and errors; no workspace). */
 int hs2_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
                         const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
-                        const int32_t* idx, void* out, int out_dtype, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const int32_t* idx, void* out, int out_dtype, void* stream);
 
 /* hs2_sparse_attn_planned over an FP8 cache (same plan, q, out and errors; scales
  * as for hs2_sparse_attn_fp8). */

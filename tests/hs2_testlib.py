@@ -40,8 +40,16 @@ def from_dev_bf16(t) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+GUARD_BYTES = 4096
+GUARD_FILL = 0xA5
+
+
 class GpuCase:
-    """Device copies of one workload plus the library arguments."""
+    """Device copies of one workload plus the library arguments.
+
+    Every output buffer it hands out (index rows, K-th scores, sparse outputs) sits
+    between two 4 KiB guard regions filled with 0xA5; each library call made through
+    the case checks afterwards that no guard byte changed (a write out of bounds)."""
 
     def __init__(self, w: synthgen.Workload, inputs: dict, flags: int = 0):
         import torch
@@ -62,10 +70,30 @@ class GpuCase:
                                         len(self.q_sparse))
         self.workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
         self.KW = w.K + w.W
+        self._guarded = []
 
-    def new_idx(self):
+    def guarded_empty(self, shape, dtype):
+        """An uninitialised device tensor between two guard regions (checked by check_guards)."""
         import torch
-        return torch.empty((self.T, self.w.Hkv, self.KW), dtype=torch.int32, device="cuda")
+        n = 1
+        for x in shape:
+            n *= int(x)
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        buf = torch.full((nbytes + 2 * GUARD_BYTES,), GUARD_FILL, dtype=torch.uint8, device="cuda")
+        self._guarded.append(buf)
+        return buf[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(*shape)
+
+    def check_guards(self):
+        import torch
+        torch.cuda.synchronize()
+        for buf in self._guarded:
+            head, tail = buf[:GUARD_BYTES], buf[buf.numel() - GUARD_BYTES:]
+            assert bool((head == GUARD_FILL).all()) and bool((tail == GUARD_FILL).all()), \
+                "a library call wrote outside its output buffer"
+
+    def new_idx(self, kw=None):
+        import torch
+        return self.guarded_empty((self.T, self.w.Hkv, kw or self.KW), torch.int32)
 
     def select(self, flags=None):
         import torch
@@ -74,32 +102,36 @@ class GpuCase:
             dims = self.hs2.make_dims(self.w.Hq, self.w.Hkv, self.w.K, self.w.W, self.w.scale,
                                       flags=flags)
         idx = self.new_idx()
-        kth = torch.empty((self.T, self.w.Hkv), dtype=torch.float32, device="cuda")
+        kth = self.guarded_empty((self.T, self.w.Hkv), torch.float32)
         self.hs2.hs2_select(dims, self.varlen, self.q_full, self.k, idx, kth, self.workspace)
-        torch.cuda.synchronize()
+        self.check_guards()
         return idx, kth
 
     def sparse(self, q, idx, precise=False):
         import torch
         dt = torch.float32 if precise else torch.bfloat16
-        out = torch.empty((self.T, self.w.Hq, self.w.d), dtype=dt, device="cuda")
+        out = self.guarded_empty((self.T, self.w.Hq, self.w.d), dt)
         self.hs2.hs2_sparse_attn(self.dims, self.varlen, q, self.k, self.v, idx, out,
                                  self.hs2.HS2_OUT_F32 if precise else self.hs2.HS2_OUT_BF16)
-        torch.cuda.synchronize()
+        self.check_guards()
         return out
 
     def prefill_block(self, precise=False):
         import torch
         dt = torch.float32 if precise else torch.bfloat16
-        outs = [torch.empty((self.T, self.w.Hq, self.w.d), dtype=dt, device="cuda")
-                for _ in self.q_sparse]
+        outs = [self.guarded_empty((self.T, self.w.Hq, self.w.d), dt) for _ in self.q_sparse]
         idx = self.new_idx()
         self.hs2.hs2_prefill_block(self.dims, self.varlen, self.q_full, self.k, self.v,
                                    self.q_sparse, outs, idx,
                                    self.hs2.HS2_OUT_F32 if precise else self.hs2.HS2_OUT_BF16,
                                    self.workspace)
-        torch.cuda.synchronize()
+        self.check_guards()
         return idx, outs
+
+    def release_guarded(self):
+        """Drop the guarded buffers handed out so far (after a final check)."""
+        self.check_guards()
+        self._guarded = []
 
 
 def local_t(cu: np.ndarray, tg: np.ndarray) -> np.ndarray:

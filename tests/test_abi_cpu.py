@@ -115,15 +115,16 @@ def test_null_pointers_and_workspace(lib):
     assert call_select(d, v, q=None) == hs2.HS2_ERR_INVALID_ARG
     assert call_select(d, v, idx=None) == hs2.HS2_ERR_INVALID_ARG
     assert call_select(d, v, ws=None) == hs2.HS2_ERR_WORKSPACE
-    need = hs2.hs2_workspace_size(d, v, hs2.HS2_OP_SELECT)
+    # a workspace below the full size runs in smaller chunks; below one task's it is refused
+    need_min = hs2.hs2_workspace_size(d, v, hs2.HS2_OP_SELECT_MIN)
     small = FakeDev()
-    small.numel = lambda: need - 1
+    small.numel = lambda: need_min - 1
     assert call_select(d, v, ws=small) == hs2.HS2_ERR_WORKSPACE
     L = hs2.load_library()
     # sparse: bad dtype, null output
-    r = L.hs2_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, 1, 7, None, 0, None)
+    r = L.hs2_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, 1, 7, None)
     assert r == hs2.HS2_ERR_INVALID_ARG
-    r = L.hs2_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, None, 0, None, 0, None)
+    r = L.hs2_sparse_attn(ctypes.byref(d), ctypes.byref(v.struct), 1, 1, 1, 1, None, 0, None)
     assert r == hs2.HS2_ERR_INVALID_ARG
     # prefill block: negative layer count, null layer pointer
     arr = (ctypes.c_void_p * 1)(None)
@@ -155,8 +156,20 @@ def test_workspace_sizes_are_bounded(lib):
         # the shared-gather plan: one 4-byte word per index entry, plus a count per union
         plan = hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_SPARSE_PLAN)
         assert idx_bytes <= plan <= idx_bytes + T * 8 + 4096
-        assert hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_PREFILL_BLOCK) == max(sel, plan)
-        assert hs2.hs2_workspace_size(d, varlen(lengths), hs2.HS2_OP_SPARSE) == 0
+        # the block's size covers the plan only when the block will plan its layers:
+        # two or more, or one over rows up to 32768 tokens
+        vl = varlen(lengths)
+        for n_sparse in (0, 1, 2, 3):
+            plans = n_sparse >= 2 or (n_sparse == 1 and max(lengths) <= 32768)
+            assert (hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_PREFILL_BLOCK, n_sparse)
+                    == (max(sel, plan) if plans else sel))
+        with pytest.raises(hs2.HS2Error):
+            hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_PREFILL_BLOCK, -1)
+        assert hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_SPARSE) == 0
+        # the smallest selection workspace holds one task's candidate rows
+        smin = hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_SELECT_MIN)
+        assert 0 < smin <= sel
+        assert sel - smin <= 4 * (1 << 30)
 
 
 def test_sparse_plan_validation(lib):
@@ -184,7 +197,7 @@ def test_sparse_plan_validation(lib):
     v64 = varlen([262130])
     with pytest.raises(hs2.HS2Error):
         hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_SPARSE_PLAN)
-    assert (hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_PREFILL_BLOCK)
+    assert (hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_PREFILL_BLOCK, 3)
             == hs2.hs2_workspace_size(d64, v64, hs2.HS2_OP_SELECT))
 
 
@@ -307,9 +320,9 @@ def test_fp8_entry_point_validation(lib):
     assert L.hs2_quantize_fp8(None, None, 0, 1.0, None) == hs2.HS2_OK
     for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0)):
         assert L.hs2_sparse_attn_fp8(ctypes.byref(d), ctypes.byref(v.struct), 8, 8, 8, ks, vs, 8, 8,
-                                     0, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
+                                     0, None) == hs2.HS2_ERR_INVALID_ARG
     assert L.hs2_sparse_attn_fp8(ctypes.byref(d), ctypes.byref(v.struct), 8, 12, 8, 1.0, 1.0, 8, 8,
-                                 0, None, 0, None) == hs2.HS2_ERR_INVALID_ARG  # k8 not 8-aligned
+                                 0, None) == hs2.HS2_ERR_INVALID_ARG  # k8 not 8-aligned
     dc = varlen([100, 50])
     assert L.hs2_decode_select_fp8(ctypes.byref(d), ctypes.byref(dc.struct), 8, 8, -2.0, 8, None, 8,
                                    1 << 40, None) == hs2.HS2_ERR_INVALID_ARG

@@ -37,13 +37,12 @@ def run_full(w, tokens=None):
                                 scale=w.scale, tokens=toks)
     idx_ref, _ = case.select()
     for precise in (True, False):
-        out = torch.empty((T, w.Hq, w.d), dtype=torch.float32 if precise else torch.bfloat16,
-                          device="cuda")
+        out = case.guarded_empty((T, w.Hq, w.d), torch.float32 if precise else torch.bfloat16)
         idx = case.new_idx()
         hs2.hs2_select_full(case.dims, case.varlen, case.q_full, case.k, case.v, idx, out,
                             hs2.HS2_OUT_F32 if precise else hs2.HS2_OUT_BF16,
                             workspace=case.workspace)
-        torch.cuda.synchronize()
+        case.check_guards()
         idx_np = idx.cpu().numpy()
         check_structure(idx_np, inp["cu_seqlens"], w.K, w.W)
         same = (idx_np == idx_ref.cpu().numpy()).all(axis=2).mean()

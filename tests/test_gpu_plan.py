@@ -170,7 +170,7 @@ def test_plan_padded_rows_of_a_decaying_budget():
         idx = case.new_idx()
         hs2.hs2_select_ex(case.dims, case.varlen, case.q_full, case.k, idx, decay_mu=0.25,
                           workspace=case.workspace)
-        torch.cuda.synchronize()
+        case.check_guards()
         return idx
 
     w = synthgen.custom([700, 3000], Hq=8, Hkv=2, K=512, W=32, n_sparse=1, seed=311)
@@ -190,7 +190,7 @@ def test_plan_of_block_and_exact_rows(flag):
         dims = hs2.make_dims(case.w.Hq, case.w.Hkv, case.w.K, case.w.W, case.w.scale, flags=f)
         idx = case.new_idx()
         hs2.hs2_select(dims, case.varlen, case.q_full, case.k, idx, None, case.workspace)
-        torch.cuda.synchronize()
+        case.check_guards()
         return idx
 
     w = synthgen.custom([70, 1500, 2600], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=313)

@@ -40,10 +40,10 @@ def run_variant(w, beta=0.0, mu=0.0, flags=0, block=0):
     inp = weighted_inputs(w)
     case = GpuCase(w, inp, flags=flags)
     idx_t = case.new_idx()
-    kth_t = torch.empty((case.T, w.Hkv), dtype=torch.float32, device="cuda")
+    kth_t = case.guarded_empty((case.T, w.Hkv), torch.float32)
     hs2.hs2_select_ex(case.dims, case.varlen, case.q_full, case.k, idx_t, kth_t, v=case.v,
                       oam_beta=beta, decay_mu=mu, workspace=case.workspace)
-    torch.cuda.synchronize()
+    case.check_guards()
     idx = idx_t.cpu().numpy()
     cu = inp["cu_seqlens"]
     o_idx, o_kth = oracle.select(inp["q_full"], inp["k"], cu, w.Hq, w.Hkv, w.K, w.W,

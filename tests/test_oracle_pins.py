@@ -703,3 +703,35 @@ def test_fp8_decode_selection():
             assert list(row[row >= 0]) == want
             if n_c > K:
                 assert abs(kth[bi * Hkv + g] - S[order[K - 1]]) <= 1e-12
+
+
+def test_oracle_results_do_not_depend_on_the_thread_count():
+    """The oracle splits its rows over threads; each row is computed whole by one
+    thread in a fixed order, so every result must be bit-identical for 1 and 16
+    threads (selection in token, block, output-aware and decaying modes; sparse,
+    full and decode attention)."""
+    w = synthgen.custom([1, 37, 300, 901], Hq=8, Hkv=2, K=64, W=16, n_sparse=1, seed=404)
+    inp = synthgen.make_inputs(w)
+    cu = inp["cu_seqlens"]
+    runs = []
+    for nt in (1, 16):
+        r = {}
+        r["sel"] = oracle.select(inp["q_full"], inp["k"], cu, w.Hq, w.Hkv, w.K, w.W,
+                                 scale=w.scale, nthreads=nt)
+        r["blk"] = oracle.select(inp["q_full"], inp["k"], cu, w.Hq, w.Hkv, w.K, w.W,
+                                 scale=w.scale, nthreads=nt, block=16)
+        r["oam"] = oracle.select(inp["q_full"], inp["k"], cu, w.Hq, w.Hkv, w.K, w.W,
+                                 scale=w.scale, nthreads=nt, v=inp["v"], oam_beta=0.7,
+                                 decay_mu=0.5)
+        idx = r["sel"][0].reshape(w.total, w.Hkv, -1)
+        r["sp"] = oracle.sparse_attn(inp["q_sparse"][0], inp["k"], inp["v"], cu, w.Hq, w.Hkv, idx,
+                                     scale=w.scale, nthreads=nt)
+        r["full"] = oracle.full_attn(inp["q_full"], inp["k"], inp["v"], cu, w.Hq, w.Hkv,
+                                     scale=w.scale, nthreads=nt)
+        qd = inp["q_full"][cu[1:] - 1]
+        r["dec"] = oracle.decode_select(qd, inp["k"], cu, w.Hq, w.Hkv, w.K, w.W, scale=w.scale,
+                                        nthreads=nt)
+        runs.append(r)
+    for key in runs[0]:
+        for a, b in zip(runs[0][key], runs[1][key]):
+            assert np.array_equal(a, b), key

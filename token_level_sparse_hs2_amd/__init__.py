@@ -21,7 +21,8 @@ import os
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhs2.so")
+# HS2_LIBRARY: another build of the library (e.g. the host-sanitizer build of its C ABI)
+LIB_PATH = os.environ.get("HS2_LIBRARY") or os.path.join(_PKG, "libhs2.so")
 
 HS2_OK = 0
 HS2_ERR_INVALID_ARG = -1
@@ -36,6 +37,7 @@ HS2_OP_PREFILL_BLOCK = 3
 HS2_OP_DECODE_SELECT = 4
 HS2_OP_DECODE_SPARSE = 5
 HS2_OP_SPARSE_PLAN = 6
+HS2_OP_SELECT_MIN = 7
 HS2_FLAG_EXACT_SELECT = 1
 HS2_FLAG_BLOCK_SELECT = 2
 HS2_MAX_SEQLEN = 262144
@@ -83,7 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_workspace_size.restype = i32
     lib.hs2_select.argtypes = [D, V, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_select.restype = i32
-    lib.hs2_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.hs2_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp]
     lib.hs2_sparse_attn.restype = i32
     lib.hs2_prefill_block.argtypes = [D, V, vp, vp, vp, i32, ctypes.POINTER(vp),
                                       ctypes.POINTER(vp), i32, vp, vp, sz, vp]
@@ -93,6 +95,8 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_select_ex.restype = i32
     lib.hs2_select_full.argtypes = [D, V, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.hs2_select_full.restype = i32
+    lib.hs2_full_attn.argtypes = [D, V, vp, vp, vp, vp, i32, vp, vp]
+    lib.hs2_full_attn.restype = i32
     lib.hs2_decode_select.argtypes = [D, V, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_decode_select.restype = i32
     lib.hs2_decode_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp, sz, vp]
@@ -100,7 +104,7 @@ def load_library(path: str = LIB_PATH):
     f32 = ctypes.c_float
     lib.hs2_quantize_fp8.argtypes = [vp, vp, i64, f32, vp]
     lib.hs2_quantize_fp8.restype = i32
-    lib.hs2_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp, sz, vp]
+    lib.hs2_sparse_attn_fp8.argtypes = [D, V, vp, vp, vp, f32, f32, vp, vp, i32, vp]
     lib.hs2_sparse_plan.argtypes = [D, V, vp, vp, sz, vp]
     lib.hs2_sparse_plan.restype = i32
     lib.hs2_sparse_attn_planned.argtypes = [D, V, vp, vp, vp, vp, sz, vp, i32, vp]
@@ -190,11 +194,10 @@ def hs2_select(dims: Dims, varlen: VarlenArgs, q, k, idx_out, kth_score_out=None
 
 
 def hs2_sparse_attn(dims: Dims, varlen: VarlenArgs, q, k, v, idx, out, out_dtype: int = HS2_OUT_BF16,
-                    workspace=None, stream=None) -> None:
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+                    stream=None) -> None:
     _check(load_library().hs2_sparse_attn(ctypes.byref(dims), ctypes.byref(varlen.struct), _ptr(q),
                                           _ptr(k), _ptr(v), _ptr(idx), _ptr(out), out_dtype,
-                                          _ptr(workspace), ws_bytes, _stream(stream)))
+                                          _stream(stream)))
 
 
 def _nbytes(t) -> int:
@@ -264,6 +267,15 @@ def hs2_select_full(dims: Dims, varlen: VarlenArgs, q, k, v, idx_out, out_full,
                                           _stream(stream)))
 
 
+def hs2_full_attn(dims: Dims, varlen: VarlenArgs, q, k, v, out, out_dtype: int = HS2_OUT_BF16,
+                  lse2_out=None, stream=None) -> None:
+    """The full layer's own attention output out [T,Hq,128] alone (no selection);
+    lse2_out (optional, float32 [T,Hq]): each row's base-2 log-sum-exp of the scaled logits."""
+    _check(load_library().hs2_full_attn(ctypes.byref(dims), ctypes.byref(varlen.struct), _ptr(q),
+                                        _ptr(k), _ptr(v), _ptr(out), out_dtype, _ptr(lse2_out),
+                                        _stream(stream)))
+
+
 def hs2_decode_select(dims: Dims, cache: VarlenArgs, q, k, idx_out, kth_score_out=None,
                       workspace=None, stream=None) -> None:
     """Decode step selection: q [B,Hq,128] (row b = sequence b's newest token, at its
@@ -298,7 +310,7 @@ def hs2_sparse_attn_fp8(dims: Dims, varlen: VarlenArgs, q, k8, v8, k_scale: floa
     _check(load_library().hs2_sparse_attn_fp8(ctypes.byref(dims), ctypes.byref(varlen.struct),
                                               _ptr(q), _ptr(k8), _ptr(v8), float(k_scale),
                                               float(v_scale), _ptr(idx), _ptr(out), out_dtype,
-                                              None, 0, _stream(stream)))
+                                              _stream(stream)))
 
 
 def hs2_decode_select_fp8(dims: Dims, cache: VarlenArgs, q, k8, k_scale: float, idx_out,

@@ -49,7 +49,35 @@ struct Geometry {
   int64_t n_grp = 0;        // token groups of plan_tokens(G)
   int plan_cap = 0;         // union entries per (group, KV group)
   size_t off_pcount = 0, plan_bytes = 0;
+  int Hq = 0, Hkv = 0;
 };
+
+// Selection workspace for `tpc` tasks per chunk: only the candidate rows, their
+// counts and the exact-path row list scale with the chunk.
+void layout_select(Geometry* geo, int64_t tpc) {
+  geo->tasks_per_chunk = tpc;
+  geo->rows_per_chunk = tpc * geo->Hkv * geo->tok;
+  size_t off = 0;
+  geo->off_lse = off;
+  off = align_up(off + (size_t)geo->T * geo->Hq * sizeof(float));
+  geo->off_cand = off;
+  off = align_up(off + (size_t)geo->rows_per_chunk * geo->cand_cap * sizeof(uint64_t));
+  geo->off_count = off;
+  off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
+  geo->off_flags = off;
+  off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
+  geo->off_nflag = off;
+  off = align_up(off + sizeof(int32_t));
+  geo->off_dense = off;
+  off = align_up(off + (size_t)hs2::kFallbackBlocks * std::max(1, geo->max_len) * sizeof(uint32_t));
+  geo->off_kmax = off;
+  off = align_up(off + (size_t)geo->B * geo->Hkv * sizeof(uint32_t));
+  geo->off_vw = off;  // output-aware metric: key weights and their maxima
+  off = align_up(off + (size_t)geo->T * geo->Hkv * sizeof(float));
+  geo->off_vwmax = off;
+  off = align_up(off + (size_t)geo->B * geo->Hkv * sizeof(uint32_t));
+  geo->select_bytes = off;
+}
 
 bool g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
 
@@ -108,30 +136,10 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   const int64_t row_bytes = cap * 8;
   int64_t tpc = hs2::kCandBudgetBytes / (rows_per_task * row_bytes);
   tpc = std::max<int64_t>(1, std::min<int64_t>(tpc, std::max<int64_t>(1, n_tasks)));
-  geo->tasks_per_chunk = tpc;
-  geo->rows_per_chunk = tpc * rows_per_task;
   geo->bitmap_words = hs2::ceil_div(std::max(1, max_len), 32);
-
-  size_t off = 0;
-  geo->off_lse = off;
-  off = align_up(off + (size_t)geo->T * d->num_q_heads * sizeof(float));
-  geo->off_cand = off;
-  off = align_up(off + (size_t)geo->rows_per_chunk * cap * sizeof(uint64_t));
-  geo->off_count = off;
-  off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
-  geo->off_flags = off;
-  off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
-  geo->off_nflag = off;
-  off = align_up(off + sizeof(int32_t));
-  geo->off_dense = off;
-  off = align_up(off + (size_t)hs2::kFallbackBlocks * std::max(1, max_len) * sizeof(uint32_t));
-  geo->off_kmax = off;
-  off = align_up(off + (size_t)v->batch * d->num_kv_heads * sizeof(uint32_t));
-  geo->off_vw = off;  // output-aware metric: key weights and their maxima
-  off = align_up(off + (size_t)geo->T * d->num_kv_heads * sizeof(float));
-  geo->off_vwmax = off;
-  off = align_up(off + (size_t)v->batch * d->num_kv_heads * sizeof(uint32_t));
-  geo->select_bytes = off;
+  geo->Hq = d->num_q_heads;
+  geo->Hkv = d->num_kv_heads;
+  layout_select(geo, tpc);
   // exact path: histogram, scratch words, two bitmaps, G query rows in fp32
   geo->exact_lds =
       (hs2::kTopkBins + 16 + 2 * (size_t)geo->bitmap_words + 16 * hs2::kHeadDim) * sizeof(uint32_t);
@@ -219,10 +227,35 @@ int validate_decode(const hs2_dims* d, const hs2_varlen* v, DecodeGeometry* dg) 
   return HS2_OK;
 }
 
-int check_workspace(const Geometry& geo, void* ws, size_t bytes) {
-  if (geo.select_bytes == 0) return HS2_OK;
-  if (!ws || bytes < geo.select_bytes) return HS2_ERR_WORKSPACE;
-  return HS2_OK;
+// Smallest selection workspace: one task per chunk.
+size_t min_select_bytes(const Geometry& geo) {
+  Geometry g1 = geo;
+  layout_select(&g1, 1);
+  return g1.select_bytes;
+}
+
+// The selection runs in chunks of whole tasks whose candidate rows fit the given
+// workspace: the full size of hs2_workspace_size(HS2_OP_SELECT), or fewer tasks
+// per chunk in a smaller workspace down to min_select_bytes.
+int fit_workspace(Geometry* geo, void* ws, size_t bytes) {
+  if (geo->select_bytes == 0) return HS2_OK;
+  if (!ws) return HS2_ERR_WORKSPACE;
+  if (bytes >= geo->select_bytes) return HS2_OK;
+  const size_t min_bytes = min_select_bytes(*geo);
+  if (bytes < min_bytes) return HS2_ERR_WORKSPACE;
+  const size_t per_task = (size_t)geo->Hkv * geo->tok * ((size_t)geo->cand_cap * 8 + 8);
+  int64_t tpc = std::min<int64_t>(geo->tasks_per_chunk, 1 + (int64_t)((bytes - min_bytes) / per_task));
+  layout_select(geo, tpc);
+  while (tpc > 1 && geo->select_bytes > bytes) layout_select(geo, --tpc);
+  return geo->select_bytes <= bytes ? HS2_OK : HS2_ERR_WORKSPACE;
+}
+
+// hs2_prefill_block runs its layers from one shared-gather plan when the plan pays
+// for itself: two or more layers, or one layer over rows up to kPlanShortRows
+// tokens (the plan's cost grows with row positions; a single layer over longer
+// rows does not recover it).
+bool plan_pays(const Geometry& geo, int n_sparse) {
+  return geo.plan_ok && (n_sparse >= 2 || (n_sparse == 1 && geo.max_len <= kPlanShortRows));
 }
 
 float scale_log2(const hs2_dims* d) { return d->softmax_scale * 1.4426950408889634f; }
@@ -333,6 +366,32 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   return HS2_OK;
 }
 
+// The full layer's own output over all causal keys (one sweep with a running
+// row maximum); lse2 (nullable) receives every row's log2-domain log-sum-exp.
+int run_full_out(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, const void* q,
+                 const void* k, const void* vv, void* out, int out_dtype, float* lse2,
+                 hipStream_t s) {
+  const int tok = hs2::full_out_tokens(geo.G);
+  int64_t n_tasks = 0;
+  for (int i = 0; i < v->batch; i++)
+    n_tasks += hs2::ceil_div(v->cu_seqlens_host[i + 1] - v->cu_seqlens_host[i], tok);
+  hs2::FullOutParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(vv);
+  p.cu = v->cu_seqlens;
+  p.B = v->batch;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.max_tiles = std::max(1, hs2::ceil_div(geo.max_len, tok));
+  p.c = scale_log2(d);
+  p.lse2 = lse2;
+  p.out = out;
+  hipError_t e = hs2::launch_full_out(geo.G, out_dtype == HS2_OUT_F32, p, n_tasks, s);
+  if (e != hipSuccess) return hip_fail(e, "full-layer output kernel");
+  return HS2_OK;
+}
+
 // K/V of a sparse launch: bf16 rows, or (fp8_scales = {k_scale, v_scale}) E4M3 codes
 void set_kv(hs2::SparseParams* p, const void* k, const void* v, const float* fp8_scales) {
   if (fp8_scales) {
@@ -424,7 +483,7 @@ int run_planned(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, c
 
 extern "C" {
 
-int hs2_version(void) { return 1 * 10000 + 3 * 100 + 0; }
+int hs2_version(void) { return 2 * 10000 + 0 * 100 + 0; }
 
 const char* hs2_status_string(int status) {
   switch (status) {
@@ -439,7 +498,6 @@ const char* hs2_status_string(int status) {
 
 int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, int n_sparse,
                        size_t* bytes_out) {
-  (void)n_sparse;
   if (!bytes_out) return HS2_ERR_INVALID_ARG;
   if (op == HS2_OP_DECODE_SELECT || op == HS2_OP_DECODE_SPARSE) {
     DecodeGeometry dg;
@@ -449,8 +507,9 @@ int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, i
     return HS2_OK;
   }
   if (op != HS2_OP_SELECT && op != HS2_OP_SPARSE && op != HS2_OP_PREFILL_BLOCK &&
-      op != HS2_OP_SPARSE_PLAN)
+      op != HS2_OP_SPARSE_PLAN && op != HS2_OP_SELECT_MIN)
     return HS2_ERR_INVALID_ARG;
+  if (op == HS2_OP_PREFILL_BLOCK && n_sparse < 0) return HS2_ERR_INVALID_ARG;
   Geometry geo;
   int st = validate(dims, varlen, &geo);
   if (st != HS2_OK) return st;
@@ -460,7 +519,9 @@ int hs2_workspace_size(const hs2_dims* dims, const hs2_varlen* varlen, int op, i
     if (!geo.plan_ok) return HS2_ERR_UNSUPPORTED;
     *bytes_out = geo.plan_bytes;
   } else if (op == HS2_OP_PREFILL_BLOCK) {
-    *bytes_out = std::max(geo.select_bytes, geo.plan_ok ? geo.plan_bytes : 0);
+    *bytes_out = std::max(geo.select_bytes, plan_pays(geo, n_sparse) ? geo.plan_bytes : 0);
+  } else if (op == HS2_OP_SELECT_MIN) {
+    *bytes_out = min_select_bytes(geo);
   } else {
     *bytes_out = geo.select_bytes;
   }
@@ -475,17 +536,14 @@ int hs2_select(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, co
   if (st != HS2_OK) return st;
   if (geo.T == 0) return HS2_OK;
   if (!q || !k || !idx_out) return HS2_ERR_INVALID_ARG;
-  st = check_workspace(geo, workspace, workspace_bytes);
+  st = fit_workspace(&geo, workspace, workspace_bytes);
   if (st != HS2_OK) return st;
   return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace,
                     static_cast<hipStream_t>(stream));
 }
 
 int hs2_sparse_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
-                    const void* v, const int32_t* idx, void* out, int out_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                    const void* v, const int32_t* idx, void* out, int out_dtype, void* stream) {
   Geometry geo;
   int st = validate(dims, varlen, &geo);
   if (st != HS2_OK) return st;
@@ -538,7 +596,7 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
   if (n_sparse > 0 && (!q_sparse_host_array || !out_sparse_host_array)) return HS2_ERR_INVALID_ARG;
   for (int i = 0; i < n_sparse; i++)
     if (!q_sparse_host_array[i] || !out_sparse_host_array[i]) return HS2_ERR_INVALID_ARG;
-  st = check_workspace(geo, workspace, workspace_bytes);
+  st = fit_workspace(&geo, workspace, workspace_bytes);
   if (st != HS2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_select(dims, varlen, geo, q_full, k, idx_out, nullptr, workspace, s);
@@ -548,8 +606,7 @@ int hs2_prefill_block(const hs2_dims* dims, const hs2_varlen* varlen, const void
   // plan's cost grows with row positions: on rows up to kPlanShortRows it pays for
   // itself within one layer, on longer ones it takes two
   const void* plan = nullptr;
-  const bool plan_pays = n_sparse >= 2 || geo.max_len <= kPlanShortRows;
-  if (plan_pays && geo.plan_ok && workspace_bytes >= geo.plan_bytes) {
+  if (plan_pays(geo, n_sparse) && workspace_bytes >= geo.plan_bytes) {
     st = run_plan(dims, varlen, geo, idx_out, workspace, s);
     if (st != HS2_OK) return st;
     plan = workspace;
@@ -584,7 +641,7 @@ int hs2_select_ex(const hs2_dims* dims, const hs2_varlen* varlen, const hs2_sele
   }
   if (geo.T == 0) return HS2_OK;
   if (!q || !k || !idx_out || (beta > 0.f && !v)) return HS2_ERR_INVALID_ARG;
-  st = check_workspace(geo, workspace, workspace_bytes);
+  st = fit_workspace(&geo, workspace, workspace_bytes);
   if (st != HS2_OK) return st;
   return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace,
                     static_cast<hipStream_t>(stream), v, beta, k_end);
@@ -599,31 +656,28 @@ int hs2_select_full(const hs2_dims* dims, const hs2_varlen* varlen, const void* 
   if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
   if (geo.T == 0) return HS2_OK;
   if (!q || !k || !v || !idx_out || !out_full) return HS2_ERR_INVALID_ARG;
-  st = check_workspace(geo, workspace, workspace_bytes);
+  st = fit_workspace(&geo, workspace, workspace_bytes);
   if (st != HS2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the output sweep first: it also writes every row's log-sum-exp, which the
   // selection then takes instead of running its own statistics sweep
-  const int tok = hs2::full_out_tokens(geo.G);
-  int64_t n_tasks = 0;
-  for (int i = 0; i < varlen->batch; i++)
-    n_tasks += hs2::ceil_div(varlen->cu_seqlens_host[i + 1] - varlen->cu_seqlens_host[i], tok);
-  hs2::FullOutParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.cu = varlen->cu_seqlens;
-  p.B = varlen->batch;
-  p.Hq = dims->num_q_heads;
-  p.Hkv = dims->num_kv_heads;
-  p.max_tiles = std::max(1, hs2::ceil_div(geo.max_len, tok));
-  p.c = scale_log2(dims);
-  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.off_lse);
-  p.out = out_full;
-  hipError_t e = hs2::launch_full_out(geo.G, out_dtype == HS2_OUT_F32, p, n_tasks, s);
-  if (e != hipSuccess) return hip_fail(e, "full-layer output kernel");
+  st = run_full_out(dims, varlen, geo, q, k, v, out_full, out_dtype,
+                    reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.off_lse), s);
+  if (st != HS2_OK) return st;
   return run_select(dims, varlen, geo, q, k, idx_out, kth_score_out, workspace, s, nullptr, 0.f, -1,
                     true);
+}
+
+int hs2_full_attn(const hs2_dims* dims, const hs2_varlen* varlen, const void* q, const void* k,
+                  const void* v, void* out, int out_dtype, float* lse2_out, void* stream) {
+  Geometry geo;
+  int st = validate(dims, varlen, &geo);
+  if (st != HS2_OK) return st;
+  if (out_dtype != HS2_OUT_BF16 && out_dtype != HS2_OUT_F32) return HS2_ERR_INVALID_ARG;
+  if (geo.T == 0) return HS2_OK;
+  if (!q || !k || !v || !out) return HS2_ERR_INVALID_ARG;
+  return run_full_out(dims, varlen, geo, q, k, v, out, out_dtype, lse2_out,
+                      static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -757,10 +811,7 @@ int hs2_decode_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* cache, co
 
 int hs2_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* varlen, const void* q,
                         const uint8_t* k8, const uint8_t* v8, float k_scale, float v_scale,
-                        const int32_t* idx, void* out, int out_dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                        const int32_t* idx, void* out, int out_dtype, void* stream) {
   Geometry geo;
   int st = validate(dims, varlen, &geo);
   if (st != HS2_OK) return st;
