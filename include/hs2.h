@@ -61,7 +61,9 @@ enum {
   HS2_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim != 128, Hq/Hkv not in
                                {1,2,4,8,16}, or one sequence's K (L * Hkv * 256 bytes) >= 4 GiB */
   HS2_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than hs2_workspace_size */
-  HS2_ERR_HIP = -4          /* a HIP runtime call failed */
+  HS2_ERR_HIP = -4,         /* a HIP runtime call failed */
+  HS2_ERR_SCRATCH = -5      /* the call needs more than the library's own scratch holds
+                               (hs2_decode_sparse_attn_noalloc) */
 };
 
 /* Output element type of the sparse attention. */
@@ -355,6 +357,27 @@ int hs2_sparse_attn_planned_fp8(const hs2_dims* dims, const hs2_varlen* varlen, 
 int hs2_decode_select_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
                           const uint8_t* k8, float k_scale, int32_t* idx_out, float* kth_score_out,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hs2_decode_sparse_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (without the workspace), results and errors as
+ * hs2_decode_sparse_attn; the call allocates nothing. The partials of the split
+ * rows go to a library-owned device array of HS2_NOALLOC_SCRATCH_BYTES, one per
+ * GPU, which that GPU keeps until the process ends; its address is looked up
+ * on the first call made on each device (with that device current). The device
+ * current on the calling thread must be the one `stream` belongs to. A call
+ * whose partials would need more (hs2_workspace_size(HS2_OP_DECODE_SPARSE) >
+ * HS2_NOALLOC_SCRATCH_BYTES; no configuration of this library's limits does)
+ * returns HS2_ERR_SCRATCH before anything is enqueued. Every call on one GPU
+ * shares its array and leaves its own partials there (nothing needs clearing:
+ * each call writes every partial it reads): calls on one stream are ordered and
+ * safe, calls that overlap on one GPU (concurrent streams, threads) race.
+ */
+#define HS2_NOALLOC_SCRATCH_BYTES (20u << 20)
+int hs2_decode_sparse_attn_noalloc(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                                   const void* k, const void* v, const int32_t* idx, void* out,
+                                   int out_dtype, void* stream);
 
 /* hs2_decode_sparse_attn over an FP8 cache (same workspace as HS2_OP_DECODE_SPARSE). */
 int hs2_decode_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,

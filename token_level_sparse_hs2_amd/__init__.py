@@ -29,6 +29,8 @@ HS2_ERR_INVALID_ARG = -1
 HS2_ERR_UNSUPPORTED = -2
 HS2_ERR_WORKSPACE = -3
 HS2_ERR_HIP = -4
+HS2_ERR_SCRATCH = -5
+HS2_NOALLOC_SCRATCH_BYTES = 20 << 20
 HS2_OUT_BF16 = 0
 HS2_OUT_F32 = 1
 HS2_OP_SELECT = 1
@@ -101,6 +103,8 @@ def load_library(path: str = LIB_PATH):
     lib.hs2_decode_select.restype = i32
     lib.hs2_decode_sparse_attn.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.hs2_decode_sparse_attn.restype = i32
+    lib.hs2_decode_sparse_attn_noalloc.argtypes = [D, V, vp, vp, vp, vp, vp, i32, vp]
+    lib.hs2_decode_sparse_attn_noalloc.restype = i32
     f32 = ctypes.c_float
     lib.hs2_quantize_fp8.argtypes = [vp, vp, i64, f32, vp]
     lib.hs2_quantize_fp8.restype = i32
@@ -294,6 +298,16 @@ def hs2_decode_sparse_attn(dims: Dims, cache: VarlenArgs, q, k, v, idx, out,
                                                  _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
                                                  out_dtype, _ptr(workspace), ws_bytes,
                                                  _stream(stream)))
+
+
+def hs2_decode_sparse_attn_noalloc(dims: Dims, cache: VarlenArgs, q, k, v, idx, out,
+                                   out_dtype: int = HS2_OUT_BF16, stream=None) -> None:
+    """hs2_decode_sparse_attn without a workspace: the library's own per-GPU scratch holds
+    the split rows' partials (calls that overlap on one GPU race)."""
+    _check(load_library().hs2_decode_sparse_attn_noalloc(ctypes.byref(dims),
+                                                         ctypes.byref(cache.struct), _ptr(q),
+                                                         _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+                                                         out_dtype, _stream(stream)))
 
 
 def hs2_quantize_fp8(src, dst, inv_scale: float, stream=None) -> None:

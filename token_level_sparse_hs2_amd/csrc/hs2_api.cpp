@@ -492,6 +492,7 @@ const char* hs2_status_string(int status) {
     case HS2_ERR_UNSUPPORTED: return "unsupported configuration (head_dim must be 128, Hq/Hkv in {1,2,4,8,16})";
     case HS2_ERR_WORKSPACE: return "workspace missing or too small";
     case HS2_ERR_HIP: return g_hip_msg;
+    case HS2_ERR_SCRATCH: return "the call needs more than the no-allocation scratch holds";
     default: return "unknown status";
   }
 }
@@ -798,6 +799,23 @@ int hs2_decode_sparse_attn(const hs2_dims* dims, const hs2_varlen* cache, const 
                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return run_decode_sparse(dims, cache, q, k, v, idx, out, out_dtype, workspace, workspace_bytes,
                            stream, nullptr);
+}
+
+int hs2_decode_sparse_attn_noalloc(const hs2_dims* dims, const hs2_varlen* cache, const void* q,
+                                   const void* k, const void* v, const int32_t* idx, void* out,
+                                   int out_dtype, void* stream) {
+  static_assert(hs2::kNoAllocScratchBytes == HS2_NOALLOC_SCRATCH_BYTES, "one scratch size");
+  DecodeGeometry dg;
+  int st = validate_decode(dims, cache, &dg);
+  if (st != HS2_OK) return st;
+  if (dg.sparse_bytes > hs2::kNoAllocScratchBytes) return HS2_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (dg.geo.B > 0 && dg.sparse_bytes > 0) {
+    hipError_t e = hs2::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "no-allocation scratch lookup");
+  }
+  return run_decode_sparse(dims, cache, q, k, v, idx, out, out_dtype, scratch,
+                           hs2::kNoAllocScratchBytes, stream, nullptr);
 }
 
 int hs2_decode_sparse_attn_fp8(const hs2_dims* dims, const hs2_varlen* cache, const void* q,

@@ -241,6 +241,10 @@ hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t 
 hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, hipStream_t s);
+// Device address of the no-allocation entry point's scratch array on the current
+// device (looked up once per device and kept).
+constexpr size_t kNoAllocScratchBytes = (size_t)20 << 20;
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_sparse_plan(int G, const PlanParams& p, hipStream_t s);
 // dst[i] = E4M3(float(src[i]) * inv_scale), round to nearest even, saturating at +-448
 hipError_t launch_quantize_fp8(const uint16_t* src, uint8_t* dst, int64_t n, float inv_scale,

@@ -32,6 +32,7 @@
 // cache; the key scale is folded into the softmax constant and the value scale
 // into the output.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "hs2_device.h"
@@ -765,6 +766,35 @@ hipError_t launch_quantize_fp8(const uint16_t* src, uint8_t* dst, int64_t n, flo
   const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 4096));
   hipLaunchKernelGGL(quantize_fp8_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n, inv_scale);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the entry point that allocates nothing (hs2_decode_sparse_attn_noalloc):
+// the split rows' partials (sparse_attn_kernel with n_part > 1, read back by
+// sparse_combine_kernel) live in this file-scope device array instead of a caller
+// workspace. Every GPU holds its own copy at its own address; host code must not
+// pass the array's name to a kernel (that is a host-side stand-in), only the
+// address looked up here, once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace hs2
