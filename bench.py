@@ -85,6 +85,90 @@ def compulsory_bytes(lengths, Hq, Hkv, d, K, W, elem_bytes=2):
     return 2 * T * Hkv * d * elem_bytes + T * Hkv * (K + W) * 4 + 2 * T * Hq * d * 2
 
 
+def read_counters(db_path):
+    """{kernel name: {counter: [value per dispatch]}} from a rocprofv3 --pmc database
+    (counters summed over the hardware instances of each dispatch)."""
+    import collections
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for disp, kname, cname, val in con.execute(
+            "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        per[(kname, disp)][cname] += val
+    con.close()
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (k, _), cs in sorted(per.items(), key=lambda kv: kv[0][1]):
+        for c, v in cs.items():
+            out[k][c].append(v)
+    return out
+
+
+def summarize_profiles(prof_dir, workload, G, keys=None):
+    """Write profiles/counters.json entries for `workload` from the rocprofv3 databases under
+    prof_dir (subdirectories fetch*/write*: FETCH_SIZE / WRITE_SIZE with --copy-calibration;
+    sq*: SQ counters with GRBM_GUI_ACTIVE; tcc*: TCC hit/miss). Each entry records the
+    source hash of its kernel file, so bench.py ignores it once that source changes."""
+    import glob
+    def db(prefix):
+        hits = sorted(glob.glob(os.path.join(prof_dir, prefix + "*", "*_results.db")))
+        return read_counters(hits[0]) if hits else {}
+    fetch, write, sq, tcc = db("fetch"), db("write"), db("sq"), db("tcc")
+    avg = lambda xs: sum(xs) / len(xs)
+    # counter scaling from the 1 GiB device copy (--copy-calibration): the copy dispatch
+    # (the runtime's blit kernel or torch's copy) with the most bytes
+    copies = [k for k in fetch if "copy" in k.lower()]
+    ck = max(copies, key=lambda k: max(fetch[k]["FETCH_SIZE"]))
+    i = fetch[ck]["FETCH_SIZE"].index(max(fetch[ck]["FETCH_SIZE"]))
+    f_factor = (1 << 30) / (fetch[ck]["FETCH_SIZE"][i] * 1024)
+    w_factor = (1 << 30) / (max(write[ck]["WRITE_SIZE"]) * 1024)
+    kernels = {
+        "sparse_planned": (f"sparse_attn_kernel<{G}, false, false, 32, true>", "sparse_attn.hip"),
+        "sparse_per_token": (f"sparse_attn_kernel<{G}, false, false, 32, false>", "sparse_attn.hip"),
+        "sparse_planned_fp8": (f"sparse_attn_kernel<{G}, false, true, 16, true>", "sparse_attn.hip"),
+        "sparse_plan": (f"sparse_plan_kernel<{G}>", "sparse_attn.hip"),
+        "scores": (f"scores_kernel<{G}>", "select_scores.hip"),
+        "topk": ("topk_kernel<", "select_topk.hip"),
+        "full_out": (f"full_out_kernel<{G}, false>", "full_out.hip"),
+    }
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    ent = rec.setdefault(workload, {})
+    for key, (pat, src) in kernels.items():
+        if keys and key not in keys:
+            continue
+        name = next((k for k in fetch if pat in k), None)
+        if name is None:
+            continue
+        e = {"kernel": name, "source_sha256_16": kernel_source_hash(src),
+             "dispatches": len(fetch[name]["FETCH_SIZE"]),
+             "fetch_kib": avg(fetch[name]["FETCH_SIZE"]),
+             "write_kib": avg(write[name]["WRITE_SIZE"]) if name in write else None,
+             "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4)}
+        e["read_bytes"] = int(e["fetch_kib"] * 1024 * f_factor)
+        e["write_bytes"] = int((e["write_kib"] or 0) * 1024 * w_factor)
+        e["hbm_bytes_per_launch"] = e["read_bytes"] + e["write_bytes"]
+        if name in tcc:
+            hit, miss = avg(tcc[name]["TCC_HIT_sum"]), avg(tcc[name]["TCC_MISS_sum"])
+            e.update({"tcc_hit": hit, "tcc_miss": miss, "l2_hit_rate": round(hit / (hit + miss), 4),
+                      "tcc_ea0_rdreq": avg(tcc[name]["TCC_EA0_RDREQ_sum"]),
+                      "tcc_ea0_rdreq_dram": avg(tcc[name]["TCC_EA0_RDREQ_DRAM_sum"])})
+        if name in sq:
+            c = {k: avg(v) for k, v in sq[name].items()}
+            e["sq"] = c
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
+                # GRBM_GUI_ACTIVE sums the 8 XCDs; 1024 SIMDs each carry one matrix core
+                e["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                       (1024 * c["GRBM_GUI_ACTIVE"] / 8), 4)
+            if c.get("SQ_INSTS_MFMA"):
+                e["valu_per_mfma"] = round(c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"], 3)
+                if "SQ_INSTS_VALU_TRANS_F32" in c:
+                    e["trans_per_mfma"] = round(c["SQ_INSTS_VALU_TRANS_F32"] / c["SQ_INSTS_MFMA"], 3)
+        ent[key] = e
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(ent, indent=1))
+
+
 def cpu_baseline(inp, w, n_tokens, threads):
     """The oracle (select for every group + every sparse layer) on a uniform token sample."""
     import numpy as np
@@ -126,7 +210,17 @@ def main():
                     help="time the decode step on this cache workload instead of prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device-to-device copy (known bytes) for counter scaling")
+    ap.add_argument("--summarize-profiles", default=None, metavar="DIR",
+                    help="write profiles/counters.json entries for --workload from the rocprofv3 "
+                         "counter databases under DIR (no GPU needed)")
+    ap.add_argument("--summarize-keys", default=None,
+                    help="comma-separated entries to write (default: every kernel found)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        import synthgen
+        w = synthgen.workload(args.workload)
+        keys = args.summarize_keys.split(",") if args.summarize_keys else None
+        return summarize_profiles(args.summarize_profiles, args.workload, w.Hq // w.Hkv, keys)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the work would shard by KV group, with no exchange between GPUs).",

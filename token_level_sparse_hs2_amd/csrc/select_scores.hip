@@ -653,43 +653,47 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
         const bool emit = owner && tl < TOK && sm.mode[tl] == kModeEmit;
         tau_r[rt][u] = emit ? sm.tau[tl] : INFINITY;
       }
-    uint64_t* cand = p.cand;
+    // per (row tile, token): the last candidate position and the candidate row
+    int lim_r[RT][NT];
+    uint2* dst_r[RT][NT];
     const int C = p.cand_cap;
-    const int nc_min = t0 - W + 1;  // every token's candidates include [0, nc_min)
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int u = 0; u < NT; u++) {
+        const int tl = token_of(rt, u);
+        lim_r[rt][u] = t0 + tl - W;
+        dst_r[rt][u] = reinterpret_cast<uint2*>(p.cand + (size_t)(slot0 + min(tl, TOK - 1)) * C);
+      }
     sweep(n_kt2, 0, 1, cand_end, Ring{}, wts, [&](int kt, int buf) HS2_INLINE {
       read_weights(buf);
       compute(buf);
-      const bool tail = kt * kKeyTile + kKeyTile > nc_min;  // some key may be past a token's range
+      int jc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ct++) jc[ct] = kt * kKeyTile + 16 * ct + lc;
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
         float Sv[4][NT];
-        uint32_t pass[NT];
-#pragma unroll
-        for (int u = 0; u < NT; u++) pass[u] = 0u;
+        bool ok[4][NT];
 #pragma unroll
         for (int ct = 0; ct < 4; ct++) {
           group_scores(rt, ct, Sv[ct]);
-          const int j = kt * kKeyTile + 16 * ct + lc;
+          // both tests always evaluated (no short circuit): S >= tau, key a candidate
 #pragma unroll
-          for (int u = 0; u < NT; u++) {
-            bool ok = Sv[ct][u] >= tau_r[rt][u];
-            if (tail) ok = ok && j <= t0 + token_of(rt, u) - W;
-            pass[u] |= ok ? (1u << ct) : 0u;
-          }
+          for (int u = 0; u < NT; u++)
+            ok[ct][u] = (Sv[ct][u] >= tau_r[rt][u]) & (jc[ct] <= lim_r[rt][u]);
         }
-        // one LDS atomic per lane and token for its (up to 4) passing keys
+        // one LDS atomic per lane and token for its (up to 4) passing keys; an entry is
+        // stored as the words (position, S bits), i.e. (S bits << 32) | position
 #pragma unroll
         for (int u = 0; u < NT; u++) {
-          if (pass[u]) {
-            const int tl = token_of(rt, u);
-            int pos = atomicAdd(&sm.cnt[tl], __popc(pass[u]));
-            uint64_t* dst = cand + (size_t)(slot0 + tl) * C;
+          const int n = (int)ok[0][u] + (int)ok[1][u] + (int)ok[2][u] + (int)ok[3][u];
+          if (n) {
+            int pos = atomicAdd(&sm.cnt[token_of(rt, u)], n);
 #pragma unroll
             for (int ct = 0; ct < 4; ct++) {
-              if ((pass[u] >> ct) & 1u) {
-                if (pos < C)
-                  dst[pos] = ((uint64_t)__float_as_uint(Sv[ct][u]) << 32) |
-                             (uint32_t)(kt * kKeyTile + 16 * ct + lc);
+              if (ok[ct][u]) {
+                if (pos < C) dst_r[rt][u][pos] = make_uint2((uint32_t)jc[ct], __float_as_uint(Sv[ct][u]));
                 pos++;
               }
             }
