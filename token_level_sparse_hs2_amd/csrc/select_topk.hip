@@ -300,10 +300,13 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     ev[s] = 0u;
     if (64 * s < count_u) ev[s] = cand[min(l + 64 * s, p.cand_cap - 1)];
   }
+  // a slot past the row's count holds the key kNoKey, which matches no prefix of a
+  // valid key (scores are >= 0, so their bit 31 is clear) and equals none of them
+  constexpr uint32_t kNoKey = 0xFFFFFFFFu;
 #pragma unroll
   for (int s = 0; s < NREG; s++) {
     const bool in = l + 64 * s < count_u;
-    key[s] = in ? (uint32_t)(ev[s] >> 32) : 0u;
+    key[s] = in ? (uint32_t)(ev[s] >> 32) : kNoKey;
     pos[s] = in ? (uint32_t)ev[s] : 0u;
     if (in) {
       mn = min(mn, key[s]);
@@ -313,10 +316,14 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   // radix select of the K-th largest key below the common prefix, 8 bits per pass
-  // (block mode: the (K / 64)-th largest block score)
+  // (block mode: the (K / 64)-th largest block score). The loops over the lane's
+  // registers stop at the row's count (wave-uniform), and the passes stop once the
+  // bin holding the K-th key is taken whole: then the K-th key is that bin's smallest
+  // and every key equal to it is taken.
   const int k_sel = p.block ? p.K / p.block : Kt;
   uint32_t prefix = mx, mask = 0xFFFFFFFFu;
   int kr = k_sel;
+  bool all_ties = false;
   if (mn != mx) {
     int hi = 31 - __clz(mn ^ mx);
     mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
@@ -328,9 +335,10 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       for (int u = 0; u < 4; u++) hist[l + 64 * u] = 0u;
       wave_lds_fence();
 #pragma unroll
-      for (int s = 0; s < NREG; s++)
-        if (l + 64 * s < count && (key[s] & mask) == prefix)
-          atomicAdd(&hist[(key[s] >> lo) & dmask], 1u);
+      for (int s = 0; s < NREG; s++) {
+        if (64 * s >= count_u) break;
+        if ((key[s] & mask) == prefix) atomicAdd(&hist[(key[s] >> lo) & dmask], 1u);
+      }
       wave_lds_fence();
       // lane l owns bins 4l .. 4l+3; inclusive suffix sums over lanes
       uint32_t h[4];
@@ -343,29 +351,45 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       const uint32_t above = suf - local;
       const bool mine = above < (uint32_t)kr && (uint32_t)kr <= suf;
       int d = 0;
-      uint32_t a = above;
+      uint32_t a = above, hd = 0;
       if (mine) {
-        if (a + h[3] >= (uint32_t)kr) d = 4 * l + 3;
-        else if ((a += h[3]) + h[2] >= (uint32_t)kr) d = 4 * l + 2;
-        else if ((a += h[2]) + h[1] >= (uint32_t)kr) d = 4 * l + 1;
-        else { a += h[1]; d = 4 * l; }
+        if (a + h[3] >= (uint32_t)kr) { d = 4 * l + 3; hd = h[3]; }
+        else if ((a += h[3]) + h[2] >= (uint32_t)kr) { d = 4 * l + 2; hd = h[2]; }
+        else if ((a += h[2]) + h[1] >= (uint32_t)kr) { d = 4 * l + 1; hd = h[1]; }
+        else { a += h[1]; d = 4 * l; hd = h[0]; }
       }
       const int src = max(0, __ffsll((unsigned long long)__ballot(mine)) - 1);
       d = __shfl(d, src, 64);
       a = (uint32_t)__shfl((int)a, src, 64);
+      hd = (uint32_t)__shfl((int)hd, src, 64);
       kr -= (int)a;
       prefix |= (uint32_t)d << lo;
       mask |= dmask << lo;
       hi = lo - 1;
       wave_lds_fence();
+      if (hi >= 0 && hd == (uint32_t)kr) {  // the whole bin is taken: its smallest key
+        uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+        for (int s = 0; s < NREG; s++) {
+          if (64 * s >= count_u) break;
+          if ((key[s] & mask) == prefix) m = min(m, key[s]);
+        }
+        prefix = wave_min_u32(m);
+        all_ties = true;
+        break;
+      }
     }
   }
   const uint32_t kth = prefix;  // K-th largest key; kr of the keys equal to it are taken
   // ties at the boundary: take the kr lowest positions (binary search on position)
   uint32_t n_eq = 0;
 #pragma unroll
-  for (int s = 0; s < NREG; s++) n_eq += (l + 64 * s < count && key[s] == kth) ? 1u : 0u;
+  for (int s = 0; s < NREG; s++) {
+    if (64 * s >= count_u) break;
+    n_eq += (key[s] == kth) ? 1u : 0u;
+  }
   n_eq = wave_sum_u32(n_eq);
+  if (all_ties) kr = (int)n_eq;  // the bin was taken whole: every key equal to its minimum
   uint32_t pos_cut = 0xFFFFFFFFu;  // ties with pos <= pos_cut are taken
   if (n_eq != (uint32_t)kr) {
     // smallest cut with >= kr ties at or below it (positions, or block indices)
@@ -374,8 +398,10 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       const uint32_t mid = (lo + hi) >> 1;
       uint32_t c = 0;
 #pragma unroll
-      for (int s = 0; s < NREG; s++)
-        c += (l + 64 * s < count && key[s] == kth && pos[s] <= mid) ? 1u : 0u;
+      for (int s = 0; s < NREG; s++) {
+        if (64 * s >= count_u) break;
+        c += (key[s] == kth && pos[s] <= mid) ? 1u : 0u;
+      }
       c = wave_sum_u32(c);
       if (c >= (uint32_t)kr) hi = mid; else lo = mid + 1;
     }
@@ -387,7 +413,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   wave_lds_fence();
 #pragma unroll
   for (int s = 0; s < NREG; s++) {
-    if (l + 64 * s < count && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut))) {
+    if (64 * s >= count_u) break;
+    if (key[s] != kNoKey && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut))) {
       if (p.block) {  // the block's candidate tokens [64 b, min(64 b + 64, n_c)): its own two words
         const int j0 = p.block * (int)pos[s], j1 = min(j0 + p.block, n_c);
 #pragma unroll
