@@ -291,3 +291,22 @@ def test_32k_workload_planned_sampled():
 def test_128k_workload_planned_sampled():
     """G = 8: two tokens per group."""
     run_sampled_workload("128k", head=64, tail=8, stride=4093)
+
+
+def test_prefill_block_without_sparse_layers():
+    """n_sparse = 0: the block is the selection alone (no plan is built, and the
+    workspace of hs2_workspace_size(HS2_OP_PREFILL_BLOCK, 0) is the selection's)."""
+    import torch
+    w = synthgen.custom([700, 3000], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=19)
+    inp = synthgen.make_inputs(w)
+    case = GpuCase(w, inp)
+    hs2 = case.hs2
+    n0 = hs2.hs2_workspace_size(case.dims, case.varlen, hs2.HS2_OP_PREFILL_BLOCK, 0)
+    assert n0 == hs2.hs2_workspace_size(case.dims, case.varlen, hs2.HS2_OP_SELECT)
+    ws = torch.empty(n0, dtype=torch.uint8, device="cuda")
+    idx_b = case.new_idx()
+    hs2.hs2_prefill_block(case.dims, case.varlen, case.q_full, case.k, case.v, [], [], idx_b,
+                          hs2.HS2_OUT_BF16, ws)
+    case.check_guards()
+    idx_s, _ = case.select()
+    assert torch.equal(idx_b, idx_s)
