@@ -37,7 +37,7 @@ struct Geometry {
   int bitmap_words = 0;
   // workspace offsets
   size_t off_lse = 0, off_cand = 0, off_count = 0, off_flags = 0, off_nflag = 0, off_dense = 0,
-         off_kmax = 0, off_vw = 0, off_vwmax = 0;
+         off_kmax = 0, off_vw = 0, off_vwmax = 0, off_tmap = 0;
   size_t select_bytes = 0;
   size_t exact_lds = 0;
   int topk_rows_per_block = 4;
@@ -66,6 +66,8 @@ void layout_select(Geometry* geo, int64_t tpc) {
   off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
   geo->off_flags = off;
   off = align_up(off + (size_t)geo->rows_per_chunk * sizeof(int32_t));
+  geo->off_tmap = off;  // (sequence, tile) of each task of the chunk
+  off = align_up(off + (size_t)tpc * 2 * sizeof(int32_t));
   geo->off_nflag = off;
   off = align_up(off + sizeof(int32_t));
   geo->off_dense = off;
@@ -148,7 +150,9 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   geo->sbuf_words = std::min(d->top_k, hs2::kMaxRankedK);
   const size_t per_wave =
       (256 + (size_t)geo->bitmap_words + (size_t)geo->sbuf_words) * sizeof(uint32_t);
-  geo->topk_rows_per_block = (int)std::max<size_t>(1, std::min<size_t>(4, 40960 / per_wave));
+  // 1, 2 or 4 waves (rows) per block: a block's rows are consecutive tokens of one task
+  const size_t rpb = std::max<size_t>(1, std::min<size_t>(4, 40960 / per_wave));
+  geo->topk_rows_per_block = rpb >= 4 ? 4 : (rpb >= 2 ? 2 : 1);
   // shared-gather plan: union rows are relative to a group's first sequence and lie
   // below its last token, so they stay under max_len + 16 (32-bit byte offsets)
   const int nt = hs2::plan_tokens(geo->G);
@@ -243,7 +247,7 @@ int fit_workspace(Geometry* geo, void* ws, size_t bytes) {
   if (bytes >= geo->select_bytes) return HS2_OK;
   const size_t min_bytes = min_select_bytes(*geo);
   if (bytes < min_bytes) return HS2_ERR_WORKSPACE;
-  const size_t per_task = (size_t)geo->Hkv * geo->tok * ((size_t)geo->cand_cap * 8 + 8);
+  const size_t per_task = (size_t)geo->Hkv * geo->tok * ((size_t)geo->cand_cap * 8 + 8) + 8;
   int64_t tpc = std::min<int64_t>(geo->tasks_per_chunk, 1 + (int64_t)((bytes - min_bytes) / per_task));
   layout_select(geo, tpc);
   while (tpc > 1 && geo->select_bytes > bytes) layout_select(geo, --tpc);
@@ -274,6 +278,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   int32_t* nflag = reinterpret_cast<int32_t*>(w + geo.off_nflag);
   uint32_t* dense = reinterpret_cast<uint32_t*>(w + geo.off_dense);
   uint32_t* kmax = reinterpret_cast<uint32_t*>(w + geo.off_kmax);
+  int2* tmap = reinterpret_cast<int2*>(w + geo.off_tmap);
 
   const int G = geo.G;
   const float gk = (float)G / (float)std::max(1, k_end);
@@ -303,6 +308,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.flag_list = flags;
   sp.flag_count = nflag;
   sp.kmax = kmax;
+  sp.task_map = tmap;
 
   hs2::TopkParams tp{};
   tp.cu = v->cu_seqlens;
@@ -314,6 +320,8 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.k_end = k_end;
   tp.max_tiles = geo.max_tiles;
   tp.tok = geo.tok;
+  tp.tok_shift = __builtin_ctz((unsigned)geo.tok);
+  tp.task_map = tmap;
   tp.block = geo.block;
   tp.cand_cap = geo.cand_cap;
   tp.bitmap_words = geo.bitmap_words;
@@ -358,7 +366,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
     if (e != hipSuccess) return hip_fail(e, "zero flag counter");
     e = hs2::launch_scores(G, sp, (int)blocks, s);
     if (e != hipSuccess) return hip_fail(e, "scores kernel");
-    e = hs2::launch_topk(G, tp, (int)rows, geo.topk_rows_per_block, s);
+    e = hs2::launch_topk(G, tp, (int)nt, geo.topk_rows_per_block, s);
     if (e != hipSuccess) return hip_fail(e, "top-k kernel");
     e = hs2::launch_fallback(G, tp, geo.exact_lds, s);
     if (e != hipSuccess) return hip_fail(e, "exact-select kernel");

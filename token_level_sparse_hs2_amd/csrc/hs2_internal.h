@@ -103,6 +103,7 @@ struct ScoreParams {
   int32_t* cand_count;  // [chunk rows]: count, or -1 = exact path
   int32_t* flag_list;   // [chunk rows]: slots sent to the exact path
   int32_t* flag_count;  // [1]
+  int2* task_map;       // [chunk tasks]: (sequence, tile) of each task, read by the top-K kernel
 };
 
 struct TopkParams {
@@ -112,7 +113,9 @@ struct TopkParams {
   int k_end;            // budget at a sequence's last position (K: no decay)
   int max_tiles;
   int64_t task_begin;
-  int tok;              // tokens per task
+  int tok;              // tokens per task (a power of two)
+  int tok_shift;        // log2(tok)
+  const int2* task_map; // [chunk tasks]: (sequence, tile), written by the scores kernel
   int block;            // 0, or kBlockTokens: candidates are (block score, block index)
   int cand_cap;
   int bitmap_words;     // words per bitmap in LDS (covers max_seqlen)
@@ -238,7 +241,7 @@ hipError_t launch_key_norms(const uint16_t* k, const int32_t* cu, int B, int Hkv
 hipError_t launch_value_weights(const uint16_t* v, const int32_t* cu, int B, int Hkv, int64_t T,
                                 float beta, float* vw, uint32_t* vwmax, hipStream_t s);
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s);
-hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s);
+hipError_t launch_topk(int G, const TopkParams& p, int n_tasks, int rows_per_block, hipStream_t s);
 hipError_t launch_fallback(int G, const TopkParams& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_sparse(int G, bool precise, bool fp8, const SparseParams& p, hipStream_t s);
 // Device address of the no-allocation entry point's scratch array on the current

@@ -198,6 +198,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   const int64_t task = p.task_begin + blockIdx.x / p.Hkv;
   int seq, tile;
   plan_decode(p.cu, p.B, TOK, p.max_tiles, task, &seq, &tile);
+  // the top-K kernel of this chunk finds each row's task here instead of searching again
+  if (tid == 0 && g == 0) p.task_map[blockIdx.x / p.Hkv] = make_int2(seq, tile);
   const int base = p.cu[seq];
   const int L = p.cu[seq + 1] - base;
   const int t0 = tile * TOK;

@@ -263,16 +263,37 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
+// A wave-uniform value the compiler has to take as new at each call: the register
+// loops below compare their index against their own copy of the row's register
+// count, so those comparisons are made at each branch instead of being hoisted and
+// kept live in SGPR pairs across the kernel.
+__device__ __forceinline__ int fresh_uniform(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 template <int NREG>
 __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   extern __shared__ uint32_t smem[];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int waves = blockDim.x >> 6;
+  // the wave index is wave-uniform, so everything derived from it stays in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int wshift = (blockDim.x >> 6) >> 1;  // log2 of the waves per block: 1, 2 or 4 waves
   uint32_t* hist = smem + (size_t)w * (256 + p.bitmap_words + p.sbuf_words);
   uint32_t* bm = hist + 256;
-  const int64_t slot = (int64_t)blockIdx.x * waves + w;
+  // grid (chunk tasks * tok / waves, Hkv): block x holds `waves` consecutive tokens of
+  // one task, block y is the KV group; rows are numbered as the scores kernel wrote them
+  const int sub_shift = p.tok_shift - wshift;
+  const int tq = blockIdx.x >> sub_shift;
+  const int tl = ((blockIdx.x & ((1 << sub_shift) - 1)) << wshift) + w;
+  const int64_t slot = (((int64_t)tq * p.Hkv + blockIdx.y) << p.tok_shift) + tl;
   if (slot >= p.n_rows) return;
-  const RowInfo r = decode_slot(p, slot);
+  const int2 tm = p.task_map[tq];
+  RowInfo r;
+  r.seq = tm.x;
+  r.base = p.cu[tm.x];
+  r.L = p.cu[tm.x + 1] - r.base;
+  r.t = tm.y * p.tok + tl;
+  r.g = blockIdx.y;
   if (r.t >= r.L) return;
   const int KW = p.K + p.W;
   const int n_c = r.t - p.W + 1;
@@ -294,6 +315,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   // every load of the row is issued before the first use (a use right after each
   // load would wait out one memory latency per load); the guard is wave-uniform
   const int count_u = __builtin_amdgcn_readfirstlane(count);
+  const int nreg = (count_u + 63) >> 6;  // registers that hold candidates (wave-uniform)
   uint64_t ev[NREG];
 #pragma unroll
   for (int s = 0; s < NREG; s++) {
@@ -313,8 +335,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       mx = max(mx, key[s]);
     }
   }
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
+  mn = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(mn));
+  mx = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_u32(mx));
   // radix select of the K-th largest key below the common prefix, 8 bits per pass
   // (block mode: the (K / 64)-th largest block score). The loops over the lane's
   // registers stop at the row's count (wave-uniform), and the passes stop once the
@@ -334,10 +356,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
 #pragma unroll
       for (int u = 0; u < 4; u++) hist[l + 64 * u] = 0u;
       wave_lds_fence();
+      const int nr = fresh_uniform(nreg);
 #pragma unroll
       for (int s = 0; s < NREG; s++) {
-        if (64 * s >= count_u) break;
-        if ((key[s] & mask) == prefix) atomicAdd(&hist[(key[s] >> lo) & dmask], 1u);
+        if (s < nr)  // keys outside the prefix (sentinels included) add zero
+          atomicAdd(&hist[(key[s] >> lo) & dmask], (key[s] & mask) == prefix ? 1u : 0u);
       }
       wave_lds_fence();
       // lane l owns bins 4l .. 4l+3; inclusive suffix sums over lanes
@@ -346,7 +369,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       for (int u = 0; u < 4; u++) h[u] = hist[4 * l + u];
       const uint32_t local = h[0] + h[1] + h[2] + h[3];
       const uint32_t incl = (uint32_t)wave_incl_scan((int)local, l);
-      const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       const uint32_t suf = total - incl + local;  // this lane's bins and all above
       const uint32_t above = suf - local;
       const bool mine = above < (uint32_t)kr && (uint32_t)kr <= suf;
@@ -358,10 +381,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
         else if ((a += h[2]) + h[1] >= (uint32_t)kr) { d = 4 * l + 1; hd = h[1]; }
         else { a += h[1]; d = 4 * l; hd = h[0]; }
       }
+      // the bin, the count above it and its size, from the lane that holds it (wave-uniform)
       const int src = max(0, __ffsll((unsigned long long)__ballot(mine)) - 1);
-      d = __shfl(d, src, 64);
-      a = (uint32_t)__shfl((int)a, src, 64);
-      hd = (uint32_t)__shfl((int)hd, src, 64);
+      d = __builtin_amdgcn_readlane(d, src);
+      a = (uint32_t)__builtin_amdgcn_readlane((int)a, src);
+      hd = (uint32_t)__builtin_amdgcn_readlane((int)hd, src);
       kr -= (int)a;
       prefix |= (uint32_t)d << lo;
       mask |= dmask << lo;
@@ -369,12 +393,12 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       wave_lds_fence();
       if (hi >= 0 && hd == (uint32_t)kr) {  // the whole bin is taken: its smallest key
         uint32_t m = 0xFFFFFFFFu;
+        const int nr = fresh_uniform(nreg);
 #pragma unroll
         for (int s = 0; s < NREG; s++) {
-          if (64 * s >= count_u) break;
-          if ((key[s] & mask) == prefix) m = min(m, key[s]);
+          if (s < nr && (key[s] & mask) == prefix) m = min(m, key[s]);
         }
-        prefix = wave_min_u32(m);
+        prefix = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(m));
         all_ties = true;
         break;
       }
@@ -383,12 +407,14 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   const uint32_t kth = prefix;  // K-th largest key; kr of the keys equal to it are taken
   // ties at the boundary: take the kr lowest positions (binary search on position)
   uint32_t n_eq = 0;
+  {
+    const int nr = fresh_uniform(nreg);
 #pragma unroll
-  for (int s = 0; s < NREG; s++) {
-    if (64 * s >= count_u) break;
-    n_eq += (key[s] == kth) ? 1u : 0u;
+    for (int s = 0; s < NREG; s++) {
+      if (s < nr) n_eq += (key[s] == kth) ? 1u : 0u;
+    }
   }
-  n_eq = wave_sum_u32(n_eq);
+  n_eq = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_sum_u32(n_eq));
   if (all_ties) kr = (int)n_eq;  // the bin was taken whole: every key equal to its minimum
   uint32_t pos_cut = 0xFFFFFFFFu;  // ties with pos <= pos_cut are taken
   if (n_eq != (uint32_t)kr) {
@@ -397,12 +423,12 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     while (lo < hi) {
       const uint32_t mid = (lo + hi) >> 1;
       uint32_t c = 0;
+      const int nr = fresh_uniform(nreg);
 #pragma unroll
       for (int s = 0; s < NREG; s++) {
-        if (64 * s >= count_u) break;
-        c += (key[s] == kth && pos[s] <= mid) ? 1u : 0u;
+        if (s < nr) c += (key[s] == kth && pos[s] <= mid) ? 1u : 0u;
       }
-      c = wave_sum_u32(c);
+      c = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_sum_u32(c));
       if (c >= (uint32_t)kr) hi = mid; else lo = mid + 1;
     }
     pos_cut = lo;
@@ -411,49 +437,65 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   const int nwords = ceil_div(n_c, 32);
   for (int i = l; i < nwords; i += 64) bm[i] = 0u;
   wave_lds_fence();
+  if (p.block) {  // the block's candidate tokens [64 b, min(64 b + 64, n_c)): its own two words
+    const int nr = fresh_uniform(nreg);
 #pragma unroll
-  for (int s = 0; s < NREG; s++) {
-    if (64 * s >= count_u) break;
-    if (key[s] != kNoKey && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut))) {
-      if (p.block) {  // the block's candidate tokens [64 b, min(64 b + 64, n_c)): its own two words
+    for (int s = 0; s < NREG; s++) {
+      if (s < nr && key[s] != kNoKey &&
+          (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut))) {
         const int j0 = p.block * (int)pos[s], j1 = min(j0 + p.block, n_c);
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int nbits = min(max(j1 - (j0 + 32 * h), 0), 32);
           if (nbits > 0) bm[(j0 >> 5) + h] = nbits == 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
         }
-      } else {
-        atomicOr(&bm[pos[s] >> 5], 1u << (pos[s] & 31));
+      }
+    }
+  } else {  // a slot not taken ORs a zero word (sentinel slots hold position 0)
+    const int nr = fresh_uniform(nreg);
+#pragma unroll
+    for (int s = 0; s < NREG; s++) {
+      if (s < nr) {
+        const bool take =
+            key[s] != kNoKey && (key[s] > kth || (key[s] == kth && pos[s] <= pos_cut));
+        atomicOr(&bm[pos[s] >> 5], take ? 1u << (pos[s] & 31) : 0u);
       }
     }
   }
   wave_lds_fence();
-  // lane l compacts words [l * per, (l + 1) * per): count, one wave scan, write
-  const int per = ceil_div(nwords, 64);
-  const int wb = min(l * per, nwords), we = min(wb + per, nwords);
-  int cnt = 0;
-  for (int i = wb; i < we; i++) cnt += __popc(bm[i]);
-  const int incl = wave_incl_scan(cnt, l);
-  const int base = __shfl(incl, 63, 64);  // number of selected positions (K_t)
-  int off = incl - cnt;
-  // Each lane's positions form a contiguous run of the row: they go to the wave's
-  // LDS staging first and leave in coalesced stores (written straight from each
-  // lane, 64 runs would scatter every store instruction over ~36 cache lines).
+  // Ascending compaction, 64 consecutive words per step (lane l reads word c + l, so
+  // the LDS reads do not conflict): a wave scan of the words' popcounts gives each
+  // lane its first output slot, then the lanes emit their positions in as many rounds
+  // as the fullest word has bits. The positions go to the wave's LDS staging and leave
+  // in coalesced stores. Plain selection takes Kt positions, block selection at most K.
   uint32_t* sbuf = bm + p.bitmap_words;
-  const bool stage = base <= p.sbuf_words;  // wave-uniform
-  for (int i = wb; i < we; i++) {
-    uint32_t mm = bm[i];
-    while (mm) {
-      const int b = __ffs(mm) - 1;
-      mm &= mm - 1;
-      if (stage) sbuf[off] = (uint32_t)(i * 32 + b);
-      else if (off < KW) row[off] = i * 32 + b;
-      off++;
+  const int sbw = p.sbuf_words;
+  const bool stage = (p.block ? p.K : Kt) <= sbw;  // wave-uniform
+  int base = 0;  // positions emitted so far (wave-uniform)
+  for (int c = 0; c < nwords; c += 64) {
+    const int i = c + l;
+    uint32_t mm = i < nwords ? bm[i] : 0u;
+    const int cnt = __popc(mm);
+    const int incl = wave_incl_scan(cnt, l);
+    int off = base + incl - cnt;
+    base += __builtin_amdgcn_readlane(incl, 63);
+    const int rounds = __builtin_amdgcn_readlane(wave_incl_max(cnt), 63);
+    for (int it = 0; it < rounds; it++) {
+      const bool has = mm != 0u;
+      const uint32_t v = (uint32_t)(i * 32 + __ffs(mm) - 1);
+      mm &= mm - 1u;
+      if (stage) {  // a lane without a bit left writes the dead histogram instead
+        *((has && off < sbw) ? sbuf + off : hist + l) = v;
+      } else if (has && off < KW) {
+        row[off] = (int32_t)v;
+      }
+      off += has ? 1 : 0;
     }
   }
   if (stage) {
     wave_lds_fence();
-    for (int o = l; o < base; o += 64) row[o] = (int32_t)sbuf[o];
+    const int n = min(base, sbw);
+    for (int o = l; o < n; o += 64) row[o] = (int32_t)sbuf[o];
   }
   for (int j = n_c + l; j <= r.t; j += 64) {
     const int o = base + (j - n_c);
@@ -776,12 +818,17 @@ hipError_t launch_decode_select(int G, const DecodeParams& p, size_t lds_bytes, 
   }
 }
 
-hipError_t launch_topk(int G, const TopkParams& p, int n_rows, int rows_per_block, hipStream_t s) {
+hipError_t launch_topk(int G, const TopkParams& p, int n_tasks, int rows_per_block, hipStream_t s) {
   (void)G;
-  if (n_rows <= 0) return hipSuccess;
+  if (n_tasks <= 0) return hipSuccess;
+  // blocks of 1, 2 or 4 rows (consecutive tokens of one task; tok is a power of two >= 16)
+  if ((rows_per_block != 1 && rows_per_block != 2 && rows_per_block != 4) ||
+      p.tok != (1 << p.tok_shift) || p.tok < rows_per_block)
+    return hipErrorInvalidValue;
   const size_t lds =
       (size_t)rows_per_block * (256 + p.bitmap_words + p.sbuf_words) * sizeof(uint32_t);
-  const dim3 grid((n_rows + rows_per_block - 1) / rows_per_block), block(64 * rows_per_block);
+  const dim3 grid((unsigned)n_tasks * (unsigned)(p.tok / rows_per_block), (unsigned)p.Hkv),
+      block(64 * rows_per_block);
   const int nreg = p.cand_cap / 64;
   if (nreg <= 32) {
     if (lds > 65536) {
