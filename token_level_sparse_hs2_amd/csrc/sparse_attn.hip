@@ -242,7 +242,23 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 && !PLAN ? 4 : 3) : 2) void sp
         s[mt] = mfma16x16x32(ka, qb[ks], s[mt]);
       }
     }
-    if constexpr (PLAN) {
+    if constexpr (PLAN && NT * 16 <= 64) {
+      // entry 16*mt + e (lane lc = e holds its word) counts for column lc iff its mask
+      // holds token col_tok: the tokens' ballots over lanes 0..15, packed into one scalar
+      // word (bit 16*a + e), give each lane its four entries' bits with one shift
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const uint64_t ok = __ballot(entry_ok(j[mt]));
+        uint64_t tm = 0;
+#pragma unroll
+        for (int a = 0; a < NT; a++)
+          tm |= ((__ballot((mk[mt] >> a) & 1u) & ok) & 0xFFFFull) << (16 * a);
+        const uint32_t bits = (uint32_t)(tm >> (16 * col_tok + 4 * lq)) & 0xFu;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (!((bits >> i) & 1u)) s[mt][i] = -INFINITY;
+      }
+    } else if constexpr (PLAN) {
       // entry 16*mt + 4*lq + i counts for column lc iff its mask holds token col_tok:
       // bit (4*lq + i) of that token's ballot
 #pragma unroll
