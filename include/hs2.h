@@ -68,7 +68,7 @@ enum {
 
 /* Output element type of the sparse attention. */
 enum {
-  HS2_OUT_BF16 = 0, /* bf16 output (round to nearest even); P.V with P rounded to bf16 */
+  HS2_OUT_BF16 = 0, /* bf16 output (round to nearest even); P.V with P as two bf16 parts */
   HS2_OUT_F32 = 1   /* fp32 output; P.V with P as three bf16 parts (~fp32 precision)
                        -- the precise mode */
 };

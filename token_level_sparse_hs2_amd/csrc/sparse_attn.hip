@@ -14,8 +14,8 @@
 // row) into registers one step ahead, staged in the wave's LDS slice, and read
 // back as the A operands of S^T = K_sel Q'^T (keys x heads; all G heads of the
 // group share the gather) and, transposed, of O^T = V^T P^T. Online softmax in the log2 domain, fp32 accumulation. P enters
-// the matrix product rounded to bf16 for the bf16 output, and as a sum of three bf16
-// parts (~24 mantissa bits) in the precise mode, where rounding P adds no visible error.
+// the matrix product as a sum of bf16 parts (two parts: ~16 mantissa bits; three
+// in the precise mode: ~24 bits), so rounding P to bf16 adds no visible error.
 //
 // Shared gather (PLAN): consecutive tokens select largely the same rows (the
 // forced window, and keys that score high for all of them), so a wave can serve
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 && !PLAN ? 4 : 3) : 2) void sp
   };
   uint4(*kl)[16] = klds[w];
 
-  constexpr int NSPLIT = PRECISE ? 3 : 1;
+  constexpr int NSPLIT = PRECISE ? 3 : 2;
   constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
 
   auto consume = [&](const int (&j)[MT], const uint32_t (&mk)[MT], const Gather& gb) {
@@ -305,9 +305,9 @@ __global__ __launch_bounds__(256, CH == 16 ? (FP8 && !PLAN ? 4 : 3) : 2) void sp
     }
 
     // P^T operand (B): column = head, k slot s <-> key (s < 4 ? 4lq + s : 16 + 4lq + s - 4).
-    // P enters as its bf16 rounding p0 for the bf16 output; the precise mode splits it
-    // into p = p0 + p1 + p2, each the bf16 rounding of what the previous parts leave,
-    // so P.V keeps ~24 mantissa bits of P (V is bf16 already: every product is exact).
+    // P is split into bf16 parts p = p0 + p1 (+ p2 in the precise mode), each the
+    // bf16 rounding of what the previous parts leave, so P.V keeps ~16 (~24)
+    // mantissa bits of P; V is bf16 already, so every product is exact.
     // (MT = 1: 16x16x16 MFMA, k slot s <-> key 4lq + s.)
     uint32_t pk[NSPLIT][2 * MT];
     if constexpr (kCompact) {
