@@ -109,6 +109,15 @@ def test_budget_edges(K, W):
     run_case(w)
 
 
+@pytest.mark.parametrize("K,W", [(1536, 64), (2048, 128)])
+def test_large_budget_register_ranking(K, W):
+    """1024 < K <= 2048: up to 2K candidates per row, ranked by the 64-register top-K
+    (rows with at most 2K candidates emit all of them, longer rows go through the
+    sampled threshold)."""
+    w = synthgen.custom([2500, 6000], Hq=8, Hkv=2, K=K, W=W, n_sparse=1, seed=180 + K % 89)
+    run_case(w)
+
+
 def test_exact_flag_path():
     import token_level_sparse_hs2_amd as hs2
     w = synthgen.custom([300, 5000], Hq=8, Hkv=2, K=256, W=32, n_sparse=1, seed=77)
