@@ -43,6 +43,7 @@ struct Geometry {
   int topk_rows_per_block = 4;
   int sbuf_words = 0;
   bool exact_only = false;  // K above the register-ranked limit: every row takes the exact path
+  bool dense = false;       // every ranked row takes the exact path: dense score rows
   int block = 0;            // block selection: tokens per block
   // shared-gather plan of the sparse layers (usable when plan_ok)
   bool plan_ok = false;
@@ -129,14 +130,18 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   const int K = d->top_k;
   geo->block = (d->flags & HS2_FLAG_BLOCK_SELECT) ? hs2::kBlockTokens : 0;
   geo->exact_only = !geo->block && K > hs2::kMaxRankedK;
-  int64_t cap = geo->exact_only ? 64 : std::max<int64_t>(hs2::kMinCandCap, 2LL * K);
+  geo->dense = !geo->block && (geo->exact_only || (d->flags & HS2_FLAG_EXACT_SELECT));
+  int64_t cap = std::max<int64_t>(hs2::kMinCandCap, 2LL * K);
   if (geo->block)  // one entry per candidate block of the longest row (<= 4096, ranked in registers)
     cap = std::max<int64_t>(64, hs2::ceil_div(std::max(1, max_len), hs2::kBlockTokens));
+  if (geo->dense)  // the candidate rows hold one fp32 score per position (two per 8-byte slot)
+    cap = std::max<int64_t>(64, hs2::ceil_div(std::max(1, max_len), 2));
   cap = (cap + 63) / 64 * 64;
   geo->cand_cap = (int)cap;
   const int64_t rows_per_task = (int64_t)d->num_kv_heads * geo->tok;
   const int64_t row_bytes = cap * 8;
-  int64_t tpc = hs2::kCandBudgetBytes / (rows_per_task * row_bytes);
+  const int64_t budget = geo->dense ? hs2::kDenseBudgetBytes : hs2::kCandBudgetBytes;
+  int64_t tpc = budget / (rows_per_task * row_bytes);
   tpc = std::max<int64_t>(1, std::min<int64_t>(tpc, std::max<int64_t>(1, n_tasks)));
   geo->bitmap_words = hs2::ceil_div(std::max(1, max_len), 32);
   geo->Hq = d->num_q_heads;
@@ -309,6 +314,8 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.flag_count = nflag;
   sp.kmax = kmax;
   sp.task_map = tmap;
+  sp.dense_out = geo.dense ? reinterpret_cast<float*>(cand) : nullptr;
+  sp.dense_ld = 2 * (int64_t)geo.cand_cap;
 
   hs2::TopkParams tp{};
   tp.cu = v->cu_seqlens;
@@ -322,6 +329,8 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.tok = geo.tok;
   tp.tok_shift = __builtin_ctz((unsigned)geo.tok);
   tp.task_map = tmap;
+  tp.dense_rows = sp.dense_out;
+  tp.dense_ld = sp.dense_ld;
   tp.block = geo.block;
   tp.cand_cap = geo.cand_cap;
   tp.bitmap_words = geo.bitmap_words;

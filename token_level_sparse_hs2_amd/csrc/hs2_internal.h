@@ -20,6 +20,7 @@ constexpr int kMinCandCap = 2048;  // candidate slots per row: max(2048, 2K) ...
 constexpr int kMaxRankedK = 2048;  // ... held in registers by the top-K wave (<= 64 per lane);
                                    // a larger K sends every row to the exact path
 constexpr int64_t kCandBudgetBytes = 4LL << 30;  // candidate buffer cap per chunk
+constexpr int64_t kDenseBudgetBytes = 16LL << 30;  // dense score rows (exact path) per chunk
 constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact path
 constexpr int kBlockTokens = 64;                 // tokens per block in block selection (= kKeyTile)
 // sampled threshold: rank r = ceil(kTauAlpha * K * n_sample / n_cand) + kTauBeta
@@ -104,6 +105,8 @@ struct ScoreParams {
   int32_t* flag_list;   // [chunk rows]: slots sent to the exact path
   int32_t* flag_count;  // [1]
   int2* task_map;       // [chunk tasks]: (sequence, tile) of each task, read by the top-K kernel
+  float* dense_out;     // exact-path rows: [chunk rows, dense_ld] S of every candidate, or null
+  int64_t dense_ld;
 };
 
 struct TopkParams {
@@ -116,6 +119,8 @@ struct TopkParams {
   int tok;              // tokens per task (a power of two)
   int tok_shift;        // log2(tok)
   const int2* task_map; // [chunk tasks]: (sequence, tile), written by the scores kernel
+  const float* dense_rows;  // [chunk rows, dense_ld] S of every candidate (scores kernel), or
+  int64_t dense_ld;         // null: the exact path then recomputes the scores
   int block;            // 0, or kBlockTokens: candidates are (block score, block index)
   int cand_cap;
   int bitmap_words;     // words per bitmap in LDS (covers max_seqlen)

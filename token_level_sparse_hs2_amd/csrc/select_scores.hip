@@ -185,7 +185,10 @@ hipError_t launch_value_weights(const uint16_t* v, const int32_t* cu, int B, int
   return hipGetLastError();
 }
 
-template <int G>
+// DENSE: the rows the exact path ranks (every ranked row, with the exact flag or a
+// budget above the register-ranked limit) get the score of every candidate written
+// to p.dense_out, from which exact_kernel selects; the other rows are unchanged.
+template <int G, bool DENSE>
 __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   using Cfg = ScoreCfg<G>;
   constexpr int RT = Cfg::RT, TOK = Cfg::TOK, ROWS_W = Cfg::ROWS_W, NT = Cfg::NT;
@@ -644,6 +647,31 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
     __syncthreads();
   }
 
+  // ================= dense rows: every candidate's score (exact path) ========
+  if constexpr (DENSE) {
+    if (n_kt2 > 0) {
+      sweep(n_kt2, 0, 1, cand_end, Ring{}, wts, [&](int kt, int buf) HS2_INLINE {
+        read_weights(buf);
+        compute(buf);
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ct++) {
+            float S[NT];
+            group_scores(rt, ct, S);
+            const int j = kt * kKeyTile + 16 * ct + lc;
+#pragma unroll
+            for (int u = 0; u < NT; u++) {
+              const int tl = token_of(rt, u);
+              if (owner && tl < TOK && sm.mode[tl] == kModeExact && j <= t0 + tl - W)
+                p.dense_out[(size_t)(slot0 + tl) * p.dense_ld + j] = S[u];
+            }
+          }
+        }
+      });
+    }
+  }
+
   // ========================= sweep 3: collect ===============================
   if (!p.block && sm.any_emit) {
     float tau_r[RT][NT];
@@ -857,15 +885,23 @@ hipError_t launch_decode_logits(int G, const DecodeParams& p, hipStream_t s) {
   return p.k8 ? launch_decode_logits_t<true>(G, p, s) : launch_decode_logits_t<false>(G, p, s);
 }
 
+template <int G>
+static void launch_scores_g(bool dense, dim3 grid, dim3 block, const ScoreParams& p,
+                            hipStream_t s) {
+  if (dense) hipLaunchKernelGGL((scores_kernel<G, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((scores_kernel<G, false>), grid, block, 0, s, p);
+}
+
 hipError_t launch_scores(int G, const ScoreParams& p, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   dim3 grid(n_blocks), block(kSelThreads);
+  const bool dense = p.dense_out != nullptr;
   switch (G) {
-    case 1: hipLaunchKernelGGL(scores_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(scores_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(scores_kernel<4>, grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(scores_kernel<8>, grid, block, 0, s, p); break;
-    case 16: hipLaunchKernelGGL(scores_kernel<16>, grid, block, 0, s, p); break;
+    case 1: launch_scores_g<1>(dense, grid, block, p, s); break;
+    case 2: launch_scores_g<2>(dense, grid, block, p, s); break;
+    case 4: launch_scores_g<4>(dense, grid, block, p, s); break;
+    case 8: launch_scores_g<8>(dense, grid, block, p, s); break;
+    case 16: launch_scores_g<16>(dense, grid, block, p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

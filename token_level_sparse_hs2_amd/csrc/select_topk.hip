@@ -511,49 +511,55 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
   const TopkShared sh = carve_lds(smem, p, true);
   const int nflag = *p.flag_count;
   const int KW = p.K + p.W;
-  uint32_t* dense = p.dense + (size_t)blockIdx.x * p.max_seqlen;
+  uint32_t* scratch = p.dense + (size_t)blockIdx.x * p.max_seqlen;
   for (int f = blockIdx.x; f < nflag; f += gridDim.x) {
     const int64_t slot = p.flag_list[f];
     const RowInfo r = decode_slot(p, slot);
     const int n_c = r.t - p.W + 1;
     int32_t* row = p.idx + ((size_t)(r.base + r.t) * p.Hkv + r.g) * KW;
-    // queries of the group's heads (fp32) and their lse2
-    for (int i = threadIdx.x; i < G * kHeadDim; i += kSelThreads) {
-      const int hh = i / kHeadDim, e = i % kHeadDim;
-      sh.qf[i] = bf16_bits_to_f32(
-          p.q[((size_t)(r.base + r.t) * p.Hq + r.g * G + hh) * kHeadDim + e]);
-    }
-    __syncthreads();
-    float lse[G];
+    // the row's scores: written by the scores kernel, or recomputed here
+    const uint32_t* dense = p.dense_rows
+        ? reinterpret_cast<const uint32_t*>(p.dense_rows + (size_t)slot * p.dense_ld)
+        : scratch;
+    if (!p.dense_rows) {
+      // queries of the group's heads (fp32) and their lse2
+      for (int i = threadIdx.x; i < G * kHeadDim; i += kSelThreads) {
+        const int hh = i / kHeadDim, e = i % kHeadDim;
+        sh.qf[i] = bf16_bits_to_f32(
+            p.q[((size_t)(r.base + r.t) * p.Hq + r.g * G + hh) * kHeadDim + e]);
+      }
+      __syncthreads();
+      float lse[G];
 #pragma unroll
-    for (int hh = 0; hh < G; hh++) lse[hh] = p.lse2[(size_t)(r.base + r.t) * p.Hq + r.g * G + hh];
-    // S[j] for every candidate, recomputed with fp32 dot products
-    for (int j = threadIdx.x; j < n_c; j += kSelThreads) {
-      const uint16_t* kr = p.k + ((size_t)(r.base + j) * p.Hkv + r.g) * kHeadDim;
-      float dot[G];
+      for (int hh = 0; hh < G; hh++) lse[hh] = p.lse2[(size_t)(r.base + r.t) * p.Hq + r.g * G + hh];
+      // S[j] for every candidate, recomputed with fp32 dot products
+      for (int j = threadIdx.x; j < n_c; j += kSelThreads) {
+        const uint16_t* kr = p.k + ((size_t)(r.base + j) * p.Hkv + r.g) * kHeadDim;
+        float dot[G];
 #pragma unroll
-      for (int hh = 0; hh < G; hh++) dot[hh] = 0.f;
-      for (int e8 = 0; e8 < kHeadDim / 8; e8++) {
-        const uint4 kv = ldg128(kr + e8 * 8);
-        const uint32_t wv[4] = {kv.x, kv.y, kv.z, kv.w};
+        for (int hh = 0; hh < G; hh++) dot[hh] = 0.f;
+        for (int e8 = 0; e8 < kHeadDim / 8; e8++) {
+          const uint4 kv = ldg128(kr + e8 * 8);
+          const uint32_t wv[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const float k0 = __uint_as_float(wv[u] << 16), k1 = __uint_as_float(wv[u] & 0xFFFF0000u);
+          for (int u = 0; u < 4; u++) {
+            const float k0 = __uint_as_float(wv[u] << 16), k1 = __uint_as_float(wv[u] & 0xFFFF0000u);
 #pragma unroll
-          for (int hh = 0; hh < G; hh++) {
-            dot[hh] = fmaf(sh.qf[hh * kHeadDim + e8 * 8 + 2 * u], k0, dot[hh]);
-            dot[hh] = fmaf(sh.qf[hh * kHeadDim + e8 * 8 + 2 * u + 1], k1, dot[hh]);
+            for (int hh = 0; hh < G; hh++) {
+              dot[hh] = fmaf(sh.qf[hh * kHeadDim + e8 * 8 + 2 * u], k0, dot[hh]);
+              dot[hh] = fmaf(sh.qf[hh * kHeadDim + e8 * 8 + 2 * u + 1], k1, dot[hh]);
+            }
           }
         }
-      }
-      // output-aware metric: the key's log2 weight joins every head's exponent
-      const float lwj = p.vw ? p.vw[(size_t)(r.base + j) * p.Hkv + r.g] : 0.f;
-      float s = 0.f;
+        // output-aware metric: the key's log2 weight joins every head's exponent
+        const float lwj = p.vw ? p.vw[(size_t)(r.base + j) * p.Hkv + r.g] : 0.f;
+        float s = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < G; hh++) s += fast_exp2(fmaf(dot[hh], p.c, lwj - lse[hh]));
-      dense[j] = __float_as_uint(s);
+        for (int hh = 0; hh < G; hh++) s += fast_exp2(fmaf(dot[hh], p.c, lwj - lse[hh]));
+        scratch[j] = __float_as_uint(s);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     int krem;
     const uint32_t kth = radix_kth([&](int i) { return dense[i]; }, n_c,
                                    row_budget(p.K, p.k_end, r.t, r.L), sh, &krem);
