@@ -125,8 +125,8 @@ def summarize_profiles(prof_dir, workload, G, keys=None):
         "sparse_planned": (f"sparse_attn_kernel<{G}, false, false, 32, true>", "sparse_attn.hip"),
         "sparse_per_token": (f"sparse_attn_kernel<{G}, false, false, 32, false>", "sparse_attn.hip"),
         "sparse_planned_fp8": (f"sparse_attn_kernel<{G}, false, true, 16, true>", "sparse_attn.hip"),
-        "sparse_plan": (f"sparse_plan_kernel<{G}>", "sparse_attn.hip"),
-        "scores": (f"scores_kernel<{G}>", "select_scores.hip"),
+        "sparse_plan": (f"sparse_plan_kernel<{min(16 // G, 8)}>", "sparse_attn.hip"),
+        "scores": (f"scores_kernel<{G}, false>", "select_scores.hip"),
         "topk": ("topk_kernel<", "select_topk.hip"),
         "full_out": (f"full_out_kernel<{G}, false>", "full_out.hip"),
     }
