@@ -87,7 +87,8 @@ enum {
 /* Flags of hs2_dims.flags. */
 enum {
   /* Skip the sampled threshold: every row with more than top_k candidates is
-     selected by the exact full-row path (slow; results obey the same rule). */
+     selected by the exact full-row path (the score of every candidate written to
+     a dense row, then a full-row radix select; slower; results obey the same rule). */
   HS2_FLAG_EXACT_SELECT = 1u,
   /* Select aligned 64-token blocks instead of single tokens (the previous
      generation's granularity, the baseline of the pages' block-vs-token
@@ -125,7 +126,9 @@ typedef struct {
  * op:
  *   HS2_OP_SELECT       the selection (hs2_select, hs2_select_ex, hs2_select_full):
  *                       per-row statistics, candidate rows of one chunk of tasks
- *                       (at most 4 GiB of candidates), exact-path scratch. A smaller
+ *                       (at most 4 GiB of candidates; with the exact flag or top_k
+ *                       above 2048, dense score rows of at most 16 GiB), exact-path
+ *                       scratch. A smaller
  *                       workspace, down to HS2_OP_SELECT_MIN bytes, is accepted too:
  *                       the selection then runs in more, smaller chunks with the
  *                       same results.

@@ -14,8 +14,10 @@
 //   first). Selected positions go into an LDS bitmap, so the compaction into
 //   the index row comes out in ascending order.
 // exact_kernel: persistent workgroups over the rows the sweep could not settle
-//   (too many / too few candidates, or the exact flag). S is recomputed for the
-//   whole row into a scratch row, then the same select and assembly run.
+//   (too many / too few candidates, or the exact flag). S of the whole row comes
+//   from the dense rows the scoring kernel wrote (exact flag, or K above the
+//   register-ranked limit) or is recomputed into a scratch row; then a workgroup
+//   radix select and the same assembly run.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
