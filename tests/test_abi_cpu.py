@@ -172,6 +172,21 @@ def test_workspace_sizes_are_bounded(lib):
         assert sel - smin <= 4 * (1 << 30)
 
 
+def test_dense_exact_workspace_is_bounded(lib):
+    """top_k above 2048 (or the exact flag): every ranked row's scores go to a dense row,
+    so the selection workspace holds whole rows, at most 16 GiB of them per chunk."""
+    for flags, K in ((0, 3000), (hs2.HS2_FLAG_EXACT_SELECT, 1024)):
+        d = hs2.make_dims(32, 8, K, 128, flags=flags)
+        for lengths in ([1024], [32768], [131072], [196608, 4096, 50000]):
+            vl = varlen(lengths)
+            T, L = sum(lengths), max(lengths)
+            sel = hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_SELECT)
+            smin = hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_SELECT_MIN)
+            # one task's dense rows: 8 groups x 64 tokens, L scores each
+            assert 8 * 64 * L * 4 <= smin <= sel
+            assert sel <= (16 << 30) + T * 8 * 64 + (1 << 30)
+
+
 def test_sparse_plan_validation(lib):
     d = hs2.make_dims(32, 8, 1024, 128)
     v = varlen([5000, 70])
