@@ -1,0 +1,80 @@
+"""Seeded random configurations through the whole path as hs2_prefill_block runs it
+(selection, shared-gather plan or per-token layers, one or two sparse layers), each
+checked against the CPU oracle on every row: group sizes 1 to 16, one to three KV
+groups, budgets from 0 past the register-ranked limit (2048, where every ranked row
+takes the dense exact path), windows from 0, ragged packed lengths, and the exact flag.
+
+Per case: the index rows' structure and A1/A2 on all rows; A4 for every layer's fp32
+output and A3 for its bf16 output, both on the GPU's own index rows; and the bf16 call
+selects the same rows as the fp32 call (the selection does not depend on the output
+mode or on scheduling).
+"""
+import numpy as np
+import pytest
+
+import synthgen
+from hs2_testlib import (A3_TOL, A4_TOL, GpuCase, acceptance_select, assert_select_ok,
+                         check_structure, from_dev_bf16, log)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_level_sparse_hs2_amd as hs2
+    hs2.load_library()  # the in-tree HIP library; nothing falls back to the CPU
+
+
+def _configs(n=20, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        K = int(rng.choice([0, 1, 17, 128, 300, 1024, 1500, 2100, 2600]))
+        W = int(rng.choice([0, 1, 7, 64, 128, 200]))
+        if K + W == 0:
+            W = 1
+        B = int(rng.integers(1, 5))
+        # long enough that large budgets still leave rows to rank
+        hi = max(3500, K + W + 2000)
+        lengths = [int(x) for x in rng.integers(1, hi, size=B)]
+        n_sparse = int(rng.integers(1, 3))
+        exact = bool(rng.random() < 0.2)
+        out.append((i, G, Hkv, K, W, lengths, n_sparse, exact))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _configs(), ids=lambda c: f"case{c[0]}")
+def test_random_configuration(cfg):
+    import oracle
+    import token_level_sparse_hs2_amd as hs2
+    i, G, Hkv, K, W, lengths, n_sparse, exact = cfg
+    w = synthgen.custom(lengths, Hq=G * Hkv, Hkv=Hkv, K=K, W=W, n_sparse=n_sparse,
+                        seed=900 + i)
+    log(f"random case {i}: lengths={lengths} G={G} Hkv={Hkv} K={K} W={W} "
+        f"n_sparse={n_sparse} exact={exact}")
+    inp = synthgen.make_inputs(w)
+    case = GpuCase(w, inp, flags=hs2.HS2_FLAG_EXACT_SELECT if exact else 0)
+    idx_t, outs32 = case.prefill_block(precise=True)
+    idx = idx_t.cpu().numpy()
+    cu = inp["cu_seqlens"]
+    check_structure(idx, cu, K, W)
+    stats = acceptance_select(idx, inp, w)
+    log(f"  select: rows {stats['rows']} identical {stats['exact_rows']} overlap "
+        f"{stats['overlap']:.6f} A1 margin {stats['a1_worst_margin']:.3g}")
+    assert_select_ok(stats)
+    idx16_t, outs16 = case.prefill_block(precise=False)
+    assert (idx16_t.cpu().numpy() == idx).all(), "the bf16 call selected other rows"
+    for l, qs_np in enumerate(inp["q_sparse"]):
+        o64, o16 = oracle.sparse_attn(qs_np, inp["k"], inp["v"], cu, w.Hq, w.Hkv, idx,
+                                      scale=w.scale)
+        err4 = np.abs(outs32[l].cpu().numpy() - o64).max()
+        g = synthgen.bf16_to_float(from_dev_bf16(outs16[l])).astype(np.float64)
+        err3 = np.abs(g - synthgen.bf16_to_float(o16).astype(np.float64)).max()
+        log(f"  layer {l}: A4 max-abs {err4:.3g} A3 max-abs {err3:.3g}")
+        assert err4 <= A4_TOL and err3 <= A3_TOL
+    case.release_guarded()
