@@ -17,9 +17,11 @@
 // XOR-swizzled by which chunk each lane fetches). Per wave and tile:
 //   S^T = K Q^T (keys x rows), v_mfma_f32_16x16x32_bf16, A = K from LDS, B = Q
 //   in registers;
-//   P^T = exp2(c S^T - m) in the accumulator layout, which is the B-operand
-//   layout of v_mfma_f32_16x16x16_bf16;
-//   O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16).
+//   P^T = exp2(c S^T - m) in the accumulator layout; two 16-key subtiles side by
+//   side are the B operand of one v_mfma_f32_16x16x32_bf16 (its k slots taken in
+//   the order those scores sit in the accumulators);
+//   O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16), the
+//   A operand's k slots in the same key order.
 // P enters as one bf16 part for bf16 output and three (~24 bits) for fp32.
 #include <type_traits>
 
@@ -89,16 +91,43 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
   const uint32_t lds_k = (uint32_t)(uintptr_t)&sm.k[0][0][0];
   const uint32_t lds_v = (uint32_t)(uintptr_t)&sm.v[0][0][0];
   const int kend = t0 + ntok;  // keys [0, kend) cover every row's causal range
-  auto dma_tile = [&](int kt, int buf) HS2_INLINE {
+  // A whole tile (keys below kend) loads from a wave-uniform tile base in SGPRs plus
+  // fixed 32-bit lane offsets, so the addresses cost no vector ALU work per tile;
+  // only the last, partial tile clamps each key to kend - 1 (those keys are masked).
+  const size_t row_bytes = row_elems * sizeof(uint16_t);
+  uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int key = 16 * w + 4 * r + lq;
-      const int j = min(kt * kKeyTile + key, kend - 1);
-      const uint16_t* ks = kbase + (size_t)j * row_elems + 8 * (lc ^ (key & 15));
-      const uint16_t* vs = vbase + (size_t)j * row_elems + 8 * (lc ^ (2 * (key & 7)));
-      const uint32_t off = (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
-      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(ks), "{m0}"(lds_k + off) : "memory");
-      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vs), "{m0}"(lds_v + off) : "memory");
+  for (int r = 0; r < 4; r++) {
+    const int key = 16 * w + 4 * r + lq;
+    koff[r] = (uint32_t)(key * row_bytes) + 16u * (lc ^ (key & 15));
+    voff[r] = (uint32_t)(key * row_bytes) + 16u * (lc ^ (2 * (key & 7)));
+  }
+  auto dma_tile = [&](int kt, int buf) HS2_INLINE {
+    if (kt * kKeyTile + kKeyTile <= kend) {
+      const size_t tb = (size_t)kt * kKeyTile * row_bytes;
+      const uint16_t* kt_base = uniform_ptr(reinterpret_cast<const uint16_t*>(
+          reinterpret_cast<const char*>(kbase) + tb));
+      const uint16_t* vt_base = uniform_ptr(reinterpret_cast<const uint16_t*>(
+          reinterpret_cast<const char*>(vbase) + tb));
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const uint32_t off = (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(koff[r]), "s"(kt_base),
+                     "{m0}"(lds_k + off) : "memory");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff[r]), "s"(vt_base),
+                     "{m0}"(lds_v + off) : "memory");
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int key = 16 * w + 4 * r + lq;
+        const int j = min(kt * kKeyTile + key, kend - 1);
+        const uint16_t* ks = kbase + (size_t)j * row_elems + 8 * (lc ^ (key & 15));
+        const uint16_t* vs = vbase + (size_t)j * row_elems + 8 * (lc ^ (2 * (key & 7)));
+        const uint32_t off = (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(ks), "{m0}"(lds_k + off) : "memory");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vs), "{m0}"(lds_v + off) : "memory");
+      }
     }
   };
   auto lds_barrier = [&]() HS2_INLINE {
@@ -127,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
     const bool diag = kt * kKeyTile + kKeyTile - 1 > t0;
     // S^T of the tile's four 16-key subtiles (keys 16 kk + 4 lq + i, row lc of each
     // row tile) in the log2 domain relative to the row's running maximum m:
-    // z = c S - m (keys past a row's token at -inf)
+    // z = c S - m, then keys past a row's token at -inf
     f32x4 z[4][kOutRT];
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
@@ -140,12 +169,20 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) acc = mfma16x16x32(ka[ks], qb[rt][ks], acc);
+#pragma unroll
+        for (int i = 0; i < 4; i++) z[kk][rt][i] = fmaf(acc[i], c, -m[rt]);
+      }
+    }
+    if (diag) {  // only the last tile or two hold keys past some row's token
+      asm volatile("");  // keeps this a branch: selects on every tile cost ~90 VALU ops
+#pragma unroll
+      for (int rt = 0; rt < kOutRT; rt++) {
         const int t = t0 + (w * kOutRowsW + 16 * rt + lc) / G;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          z[kk][rt][i] = fmaf(acc[i], c, -m[rt]);
-          if (diag && kt * kKeyTile + 16 * kk + 4 * lq + i > t) z[kk][rt][i] = -INFINITY;
-        }
+        for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            if (kt * kKeyTile + 16 * kk + 4 * lq + i > t) z[kk][rt][i] = -INFINITY;
       }
     }
     // the row's maximum over the tile relative to m (16 values per lane, then its 4
@@ -154,11 +191,13 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
     // passes it by the slack, rescaling the row's sum and output.
 #pragma unroll
     for (int rt = 0; rt < kOutRT; rt++) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++)
-        mx = fmaxf(mx, fmaxf(fmaxf(z[kk][rt][0], z[kk][rt][1]), fmaxf(z[kk][rt][2], z[kk][rt][3])));
-      mx = max_xor32(max_xor16(mx));
+      const float a0 = max3_f32(z[0][rt][0], z[0][rt][1], z[0][rt][2]);
+      const float a1 = max3_f32(z[0][rt][3], z[1][rt][0], z[1][rt][1]);
+      const float a2 = max3_f32(z[1][rt][2], z[1][rt][3], z[2][rt][0]);
+      const float a3 = max3_f32(z[2][rt][1], z[2][rt][2], z[2][rt][3]);
+      const float a4 = max3_f32(z[3][rt][0], z[3][rt][1], z[3][rt][2]);
+      float mx = max3_f32(max3_f32(a0, a1, a2), max3_f32(a3, a4, z[3][rt][3]), -INFINITY);
+      mx = max_xor32_raw(max_xor16_raw(mx));
       const bool first = kt == 0;
       if (first || __any(mx > kRescaleSlack)) {
         const float dm = first ? mx : fmaxf(mx, 0.f);
@@ -174,41 +213,55 @@ __global__ __launch_bounds__(256, 2) void full_out_kernel(FullOutParams p) {
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) {  // 16-key subtiles
-      s16x4 pb[kOutRT][NSPLIT];
+    for (int kp = 0; kp < 2; kp++) {  // pairs of 16-key subtiles: 32 keys per MFMA
+      // P^T as the B operand of the 16x16x32 product: k slot 4 h + i of lane group lq
+      // holds key 16 (2 kp + h) + 4 lq + i, the accumulator position of that score
+      uint32_t pk[kOutRT][NSPLIT][4];
 #pragma unroll
       for (int rt = 0; rt < kOutRT; rt++) {
-        float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) pv[i] = fast_exp2(z[kk][rt][i]);
-        lsum[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        for (int h = 0; h < 2; h++) {
+          float pv[4];
 #pragma unroll
-        for (int part = 0; part < NSPLIT; part++) {
-          const uint32_t lo = pack_bf16x2(pv[0], pv[1]), hi = pack_bf16x2(pv[2], pv[3]);
-          pb[rt][part] = __builtin_bit_cast(s16x4, make_uint2(lo, hi));
-          if (part + 1 < NSPLIT) {
-            pv[0] -= bf16_bits_to_f32(lo & 0xFFFFu);
-            pv[1] -= __uint_as_float(lo & 0xFFFF0000u);
-            pv[2] -= bf16_bits_to_f32(hi & 0xFFFFu);
-            pv[3] -= __uint_as_float(hi & 0xFFFF0000u);
+          for (int i = 0; i < 4; i++) pv[i] = fast_exp2(z[2 * kp + h][rt][i]);
+          lsum[rt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+          for (int part = 0; part < NSPLIT; part++) {
+            const uint32_t lo = pack_bf16x2(pv[0], pv[1]), hi = pack_bf16x2(pv[2], pv[3]);
+            pk[rt][part][2 * h] = lo;
+            pk[rt][part][2 * h + 1] = hi;
+            if (part + 1 < NSPLIT) {
+              pv[0] -= bf16_bits_to_f32(lo & 0xFFFFu);
+              pv[1] -= __uint_as_float(lo & 0xFFFF0000u);
+              pv[2] -= bf16_bits_to_f32(hi & 0xFFFFu);
+              pv[3] -= __uint_as_float(hi & 0xFFFF0000u);
+            }
           }
         }
       }
-      // O^T += V^T P^T: lane reads V[16 kk + 4 lq + e][16 dt + lc] (e = 0..3) via one
-      // transposing read; lane j of the group addresses key 16 kk + 4 lq + (j >> 2),
-      // d = 16 dt + 4 (j & 3)
-      const int key = 16 * kk + 4 * lq + (lc >> 2);
+      // O^T += V^T P^T: the A operand's k slots 4 h + e are V[16 (2 kp + h) + 4 lq + e]
+      // [16 dt + lc], one transposing read per half: lane j of the group addresses key
+      // 16 (2 kp + h) + 4 lq + (j >> 2), d = 16 dt + 4 (j & 3)
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
         const int d0 = 16 * dt + 4 * (lc & 3);
-        const int phys = (d0 >> 3) ^ (2 * (key & 7));
-        const short* src = reinterpret_cast<const short*>(&sm.v[buf][key][phys]) + (d0 & 7);
-        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(src));
+        uint2 hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int key = 16 * (2 * kp + h) + 4 * lq + (lc >> 2);
+          const int phys = (d0 >> 3) ^ (2 * (key & 7));
+          const short* src = reinterpret_cast<const short*>(&sm.v[buf][key][phys]) + (d0 & 7);
+          hv[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (s16x4 __attribute__((address_space(3)))*)(src)));
+        }
+        const bf16x8 va = as_bf16x8(u32x4{hv[0].x, hv[0].y, hv[1].x, hv[1].y});
 #pragma unroll
         for (int rt = 0; rt < kOutRT; rt++)
 #pragma unroll
-          for (int part = 0; part < NSPLIT; part++) o[dt][rt] = mfma16x16x16(va, pb[rt][part], o[dt][rt]);
+          for (int part = 0; part < NSPLIT; part++)
+            o[dt][rt] = mfma16x16x32(va, as_bf16x8(u32x4{pk[rt][part][0], pk[rt][part][1],
+                                                         pk[rt][part][2], pk[rt][part][3]}),
+                                     o[dt][rt]);
       }
     }
   }

@@ -76,6 +76,37 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// max of three floats / of a lane pair as one v_max3_f32 / v_max_f32 from inline
+// asm: fmaxf in IEEE mode first quiets each operand the compiler cannot prove is
+// not a signalling NaN (one extra v_max per operand); scores and -inf are never NaN.
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max_xor16_raw(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32_raw(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// A pointer the caller knows to be wave-uniform, moved into SGPRs (for the saddr
+// form of global loads).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trip):
 // scans within each 16-lane row, then row broadcasts of lanes 15 and 31.
 __device__ __forceinline__ int wave_incl_scan(int x, int l) {
