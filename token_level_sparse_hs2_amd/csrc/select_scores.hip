@@ -269,7 +269,34 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
   const uint32_t lds_lw = (uint32_t)(uintptr_t)&sm.lw[0][0][0];
   // With wts (the output-aware metric) a fifth load per wave brings the tile's 64
   // log2 key weights into the wave's own copy, so the ring waits cover them too.
+  // A whole tile (every key below kend) loads from a wave-uniform tile base in
+  // SGPRs plus fixed 32-bit lane offsets, so its addresses cost no vector ALU work;
+  // only a partial last tile clamps each key to kend - 1.
+  const size_t krow_bytes = (size_t)Hkv * kHeadDim * sizeof(uint16_t);
+  uint32_t koff[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int key = 16 * w + 4 * r + lq;
+    koff[r] = (uint32_t)(key * krow_bytes) + 16u * (lc ^ (key & 15));
+  }
+  const uint32_t wofs = (uint32_t)(l * Hkv) * (uint32_t)sizeof(float);
   auto dma_tile = [&](int kt, int kend, int buf, bool wts) HS2_INLINE {
+    if (kt * kKeyTile + kKeyTile <= kend) {
+      const uint16_t* tb = uniform_ptr(kbase + (size_t)(base + kt * kKeyTile) * Hkv * kHeadDim);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const uint32_t dst = lds_ring + (uint32_t)(buf * kKeyTile + 16 * wu + 4 * r) * 256u;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(koff[r]), "s"(tb), "{m0}"(dst)
+                     : "memory");
+      }
+      if (wts) {
+        const float* wb = uniform_ptr(p.vw + (size_t)(base + kt * kKeyTile) * Hkv + g);
+        const uint32_t dst = lds_lw + (uint32_t)(buf * (kSelThreads / 64) + wu) * (kKeyTile * 4u);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(wofs), "s"(wb), "{m0}"(dst)
+                     : "memory");
+      }
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int key = 16 * w + 4 * r + lq;
