@@ -7,14 +7,17 @@ takes the dense exact path), windows from 0, ragged packed lengths, and the exac
 Per case: the index rows' structure and A1/A2 on all rows; A4 for every layer's fp32
 output and A3 for its bf16 output, both on the GPU's own index rows; and the bf16 call
 selects the same rows as the fp32 call (the selection does not depend on the output
-mode or on scheduling).
+mode or on scheduling). The same configurations drive the full layer's own output
+(hs2_full_attn): A4 / A3 against the oracle's dense causal attention and the rows'
+log2-domain log-sum-exp, on sampled tokens (every sequence's first and last tokens,
+the tiles' edges and a stride).
 """
 import numpy as np
 import pytest
 
 import synthgen
 from hs2_testlib import (A3_TOL, A4_TOL, GpuCase, acceptance_select, assert_select_ok,
-                         check_structure, from_dev_bf16, log)
+                         check_structure, from_dev_bf16, log, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,4 +80,47 @@ def test_random_configuration(cfg):
         err3 = np.abs(g - synthgen.bf16_to_float(o16).astype(np.float64)).max()
         log(f"  layer {l}: A4 max-abs {err4:.3g} A3 max-abs {err3:.3g}")
         assert err4 <= A4_TOL and err3 <= A3_TOL
+    case.release_guarded()
+
+
+@pytest.mark.parametrize("cfg", _configs(), ids=lambda c: f"case{c[0]}")
+def test_random_full_output(cfg):
+    import oracle
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    i, G, Hkv, K, W, lengths, n_sparse, exact = cfg
+    w = synthgen.custom(lengths, Hq=G * Hkv, Hkv=Hkv, K=K, W=W, n_sparse=n_sparse, seed=900 + i)
+    log(f"random full case {i}: lengths={lengths} G={G} Hkv={Hkv}")
+    inp = synthgen.make_inputs(w)
+    case = GpuCase(w, inp)
+    cu = inp["cu_seqlens"]
+    T = case.T
+    toks = sample_tokens(w.lengths, 64, 0, head=12, tail=12, stride=97)
+    o64, o16 = oracle.full_attn(inp["q_full"], inp["k"], inp["v"], cu, w.Hq, w.Hkv,
+                                scale=w.scale, tokens=toks)
+    for precise in (True, False):
+        out = case.guarded_empty((T, w.Hq, w.d), torch.float32 if precise else torch.bfloat16)
+        lse2 = case.guarded_empty((T, w.Hq), torch.float32)
+        hs2.hs2_full_attn(case.dims, case.varlen, case.q_full, case.k, case.v, out,
+                          hs2.HS2_OUT_F32 if precise else hs2.HS2_OUT_BF16, lse2)
+        case.check_guards()
+        if precise:
+            err = np.abs(out.cpu().numpy()[toks] - o64).max()
+            log(f"  fp32 max-abs {err:.3g}")
+            assert err <= A4_TOL
+        else:
+            g16 = synthgen.bf16_to_float(from_dev_bf16(out)[toks]).astype(np.float64)
+            err = np.abs(g16 - synthgen.bf16_to_float(o16).astype(np.float64)).max()
+            log(f"  bf16 max-abs {err:.3g}")
+            assert err <= A3_TOL
+        got = lse2.cpu().numpy()
+        worst = 0.0
+        for tg in toks[::5]:
+            for g in range(w.Hkv):
+                _, m, l = oracle.group_scores(inp["q_full"], inp["k"], cu, w.Hq, w.Hkv, int(tg),
+                                              g, scale=w.scale)
+                ref = (m + np.log(l)) / np.log(2.0)
+                worst = max(worst, np.abs(got[tg, g * G:(g + 1) * G] - ref).max())
+        log(f"  lse2 max-abs {worst:.3g}")
+        assert worst <= 1e-4
     case.release_guarded()
