@@ -120,6 +120,16 @@ __device__ __forceinline__ int wave_incl_scan(int x, int l) {
   return x;
 }
 
+// Inclusive prefix sum within each 16-lane row (the first four moves of
+// wave_incl_scan).
+__device__ __forceinline__ int row_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return x;
+}
+
 // Inclusive max scan over the 64 lanes (values >= -1), the DPP moves of
 // wave_incl_scan with -1 where a move brings nothing.
 __device__ __forceinline__ int wave_incl_max(int x) {

@@ -722,6 +722,15 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
         lim_r[rt][u] = t0 + tl - W;
         dst_r[rt][u] = reinterpret_cast<uint2*>(p.cand + (size_t)(slot0 + min(tl, TOK - 1)) * C);
       }
+    // per (row tile, token): the candidates appended so far. A token's keys all sit in
+    // the 16 lanes of one row group of one wave, so each lane's first slot is the
+    // count so far plus a prefix sum over that row (no LDS atomics); every lane of the
+    // row keeps the same count.
+    int cnt_r[RT][NT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int u = 0; u < NT; u++) cnt_r[rt][u] = 0;
     sweep(n_kt2, 0, 1, cand_end, Ring{}, wts, [&](int kt, int buf) HS2_INLINE {
       read_weights(buf);
       compute(buf);
@@ -740,24 +749,33 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
           for (int u = 0; u < NT; u++)
             ok[ct][u] = (Sv[ct][u] >= tau_r[rt][u]) & (jc[ct] <= lim_r[rt][u]);
         }
-        // one LDS atomic per lane and token for its (up to 4) passing keys; an entry is
-        // stored as the words (position, S bits), i.e. (S bits << 32) | position
+        // the lane's (up to 4) passing keys go to consecutive slots after those of the
+        // lanes before it in the row; an entry is stored as the words (position, S
+        // bits), i.e. (S bits << 32) | position
 #pragma unroll
         for (int u = 0; u < NT; u++) {
           const int n = (int)ok[0][u] + (int)ok[1][u] + (int)ok[2][u] + (int)ok[3][u];
-          if (n) {
-            int pos = atomicAdd(&sm.cnt[token_of(rt, u)], n);
+          const int incl = row_incl_scan(n);
+          int pos = cnt_r[rt][u] + incl - n;
+          cnt_r[rt][u] += __shfl(incl, l | 15, 64);  // the row's total
 #pragma unroll
-            for (int ct = 0; ct < 4; ct++) {
-              if (ok[ct][u]) {
-                if (pos < C) dst_r[rt][u][pos] = make_uint2((uint32_t)jc[ct], __float_as_uint(Sv[ct][u]));
-                pos++;
-              }
+          for (int ct = 0; ct < 4; ct++) {
+            if (ok[ct][u]) {
+              if (pos < C) dst_r[rt][u][pos] = make_uint2((uint32_t)jc[ct], __float_as_uint(Sv[ct][u]));
+              pos++;
             }
           }
         }
       }
     });
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int u = 0; u < NT; u++) {
+        const int tl = token_of(rt, u);
+        if (owner && lc == 0 && sm.mode[tl] == kModeEmit) sm.cnt[tl] = cnt_r[rt][u];
+      }
+    __syncthreads();
   }
 
   // ============================ row verdicts ================================
