@@ -71,3 +71,9 @@ def test_full_output_ragged_every_group_size(G):
 def test_full_output_8k_sampled():
     w = synthgen.workload("8k")
     run_full(w, tokens=sample_tokens(w.lengths, w.K, w.W, head=64, tail=16, stride=509))
+
+
+def test_full_output_128k_sampled():
+    # the largest configuration the bench times the full layer's output on (G = 8)
+    w = synthgen.workload("128k")
+    run_full(w, tokens=sample_tokens(w.lengths, w.K, w.W, head=16, tail=8, stride=8191))
