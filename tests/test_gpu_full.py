@@ -77,3 +77,9 @@ def test_full_output_128k_sampled():
     # the largest configuration the bench times the full layer's output on (G = 8)
     w = synthgen.workload("128k")
     run_full(w, tokens=sample_tokens(w.lengths, w.K, w.W, head=16, tail=8, stride=8191))
+
+
+def test_full_output_varlen_sampled():
+    # the mixed-length batch the bench times (8 sequences, 290k tokens, up to 97k each)
+    w = synthgen.workload("varlen")
+    run_full(w, tokens=sample_tokens(w.lengths, w.K, w.W, head=8, tail=4, stride=16381))
