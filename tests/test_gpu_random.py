@@ -1,8 +1,9 @@
 """Seeded random configurations through the whole path as hs2_prefill_block runs it
-(selection, shared-gather plan or per-token layers, one or two sparse layers), each
-checked against the CPU oracle on every row: group sizes 1 to 16, one to three KV
+(selection, shared-gather plan or per-token layers, one to three sparse layers), each
+checked against the CPU oracle on every row: group sizes 1 to 16, one to sixteen KV
 groups, budgets from 0 past the register-ranked limit (2048, where every ranked row
-takes the dense exact path), windows from 0, ragged packed lengths, and the exact flag.
+takes the dense exact path), windows from 0, ragged packed lengths (up to 8 sequences,
+many under 200 tokens), and the exact flag.
 
 Per case: the index rows' structure and A1/A2 on all rows; A4 for every layer's fp32
 output and A3 for its bf16 output, both on the GPU's own index rows; and the bf16 call
@@ -51,7 +52,30 @@ def _configs(n=20, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("cfg", _configs(), ids=lambda c: f"case{c[0]}")
+def _wide_configs(n=20, seed=77):
+    """More KV groups (4, 5, 8, 16), up to 8 packed sequences, half of the cases
+    with sequences under 200 tokens, budgets at the register-ranking edges."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([4, 5, 8, 16])) if G <= 4 else int(rng.choice([4, 5, 8]))
+        K = int(rng.choice([0, 1, 5, 64, 256, 1024, 2048, 2049]))
+        W = int(rng.choice([0, 1, 3, 63, 64, 65, 128]))
+        if K + W == 0:
+            W = 1
+        B = int(rng.integers(1, 9))
+        if rng.random() < 0.5:
+            lengths = [int(x) for x in rng.integers(1, 200, size=B)]
+        else:
+            lengths = [int(x) for x in rng.integers(1, max(3000, K + W + 1500), size=B)]
+        n_sparse = int(rng.integers(1, 4))
+        exact = bool(rng.random() < 0.25)
+        out.append((1000 + i, G, Hkv, K, W, lengths, n_sparse, exact))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _configs() + _wide_configs(), ids=lambda c: f"case{c[0]}")
 def test_random_configuration(cfg):
     import oracle
     import token_level_sparse_hs2_amd as hs2
@@ -83,7 +107,7 @@ def test_random_configuration(cfg):
     case.release_guarded()
 
 
-@pytest.mark.parametrize("cfg", _configs(), ids=lambda c: f"case{c[0]}")
+@pytest.mark.parametrize("cfg", _configs() + _wide_configs(), ids=lambda c: f"case{c[0]}")
 def test_random_full_output(cfg):
     import oracle
     import torch
