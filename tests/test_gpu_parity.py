@@ -208,3 +208,36 @@ def test_128k_workload_sampled():
 def test_varlen_workload_sampled():
     w = synthgen.workload("varlen")
     run_case(w, tokens=sample_tokens(w.lengths, w.K, w.W, head=32, tail=4, stride=4999))
+
+
+def test_longest_sequence_sampled():
+    """One sequence of the longest length the boundary accepts (HS2_MAX_SEQLEN), at a
+    small head count: selection (A1/A2, K-th score) and the per-token sparse layer on
+    sampled rows, then the full layer's output and row statistics on the same rows."""
+    import oracle
+    import token_level_sparse_hs2_amd as hs2
+    w = synthgen.custom([hs2.HS2_MAX_SEQLEN], Hq=8, Hkv=2, K=1024, W=128, n_sparse=1, seed=2621)
+    toks = sample_tokens(w.lengths, w.K, w.W, head=16, tail=8, stride=32749)
+    case, _ = run_case(w, tokens=toks)
+    import torch
+    inp = case.inputs
+    o64, o16 = oracle.full_attn(inp["q_full"], inp["k"], inp["v"], inp["cu_seqlens"], w.Hq, w.Hkv,
+                                scale=w.scale, tokens=toks)
+    out = case.guarded_empty((case.T, w.Hq, w.d), torch.float32)
+    lse2 = case.guarded_empty((case.T, w.Hq), torch.float32)
+    hs2.hs2_full_attn(case.dims, case.varlen, case.q_full, case.k, case.v, out, hs2.HS2_OUT_F32,
+                      lse2)
+    case.check_guards()
+    err = np.abs(out.cpu().numpy()[toks] - o64).max()
+    log(f"  full output fp32 max-abs {err:.3g}")
+    assert err <= A4_TOL
+    got = lse2.cpu().numpy()
+    worst = 0.0
+    G = w.Hq // w.Hkv
+    for tg in toks[::3]:
+        for g in range(w.Hkv):
+            _, m, l = oracle.group_scores(inp["q_full"], inp["k"], inp["cu_seqlens"], w.Hq, w.Hkv,
+                                          int(tg), g, scale=w.scale)
+            worst = max(worst, np.abs(got[tg, g * G:(g + 1) * G] - (m + np.log(l)) / np.log(2.0)).max())
+    log(f"  lse2 max-abs {worst:.3g}")
+    assert worst <= 1e-4

@@ -248,9 +248,11 @@ def test_prefill_block_runs_the_plan():
 
 
 def run_sampled_workload(name, head, tail, stride):
-    """A bench configuration: the unions of the groups holding sampled tokens checked
-    against the host union, the planned layer on the sampled tokens."""
-    w = synthgen.workload(name)
+    """A bench configuration (or a given one-sequence workload): the unions of the
+    groups holding sampled tokens checked against the host union, the planned layer
+    on the sampled tokens."""
+    w = synthgen.workload(name) if isinstance(name, str) else name
+    name = w.name
     w.n_sparse = 1
     toks = sample_tokens(w.lengths, w.K, w.W, head=head, tail=tail, stride=stride)
     inp = synthgen.make_inputs(w)
@@ -310,3 +312,10 @@ def test_prefill_block_without_sparse_layers():
     case.check_guards()
     idx_s, _ = case.select()
     assert torch.equal(idx_b, idx_s)
+
+
+def test_longest_sequence_planned_sampled():
+    """One sequence of the longest length the boundary accepts (HS2_MAX_SEQLEN)."""
+    import token_level_sparse_hs2_amd as hs2
+    w = synthgen.custom([hs2.HS2_MAX_SEQLEN], Hq=8, Hkv=2, K=1024, W=128, n_sparse=1, seed=2622)
+    run_sampled_workload(w, head=16, tail=8, stride=32749)
