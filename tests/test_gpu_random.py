@@ -3,7 +3,7 @@
 checked against the CPU oracle on every row: group sizes 1 to 16, one to sixteen KV
 groups, budgets from 0 past the register-ranked limit (2048, where every ranked row
 takes the dense exact path), windows from 0, ragged packed lengths (up to 8 sequences,
-many under 200 tokens), and the exact flag.
+many under 200 tokens, and one batch of 500 sequences), and the exact flag.
 
 Per case: the index rows' structure and A1/A2 on all rows; A4 for every layer's fp32
 output and A3 for its bf16 output, both on the GPU's own index rows; and the bf16 call
@@ -75,7 +75,14 @@ def _wide_configs(n=20, seed=77):
     return out
 
 
-@pytest.mark.parametrize("cfg", _configs() + _wide_configs(), ids=lambda c: f"case{c[0]}")
+def _many_sequences():
+    """500 packed sequences of 1-399 tokens (100k tokens)."""
+    rng = np.random.default_rng(99)
+    return [(2000, 4, 2, 64, 16, [int(x) for x in rng.integers(1, 400, size=500)], 2, False)]
+
+
+@pytest.mark.parametrize("cfg", _configs() + _wide_configs() + _many_sequences(),
+                         ids=lambda c: f"case{c[0]}")
 def test_random_configuration(cfg):
     import oracle
     import token_level_sparse_hs2_amd as hs2
@@ -107,7 +114,8 @@ def test_random_configuration(cfg):
     case.release_guarded()
 
 
-@pytest.mark.parametrize("cfg", _configs() + _wide_configs(), ids=lambda c: f"case{c[0]}")
+@pytest.mark.parametrize("cfg", _configs() + _wide_configs() + _many_sequences(),
+                         ids=lambda c: f"case{c[0]}")
 def test_random_full_output(cfg):
     import oracle
     import torch
