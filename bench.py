@@ -537,6 +537,15 @@ def main_decode(args):
     wall = time.perf_counter() - t0
     sel_ms = timed(select, 20)
     sp_ms = timed(lambda: sparse(0), 20)
+    # the same step captured once in a HIP graph and replayed (no per-call host work)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        hs2.hs2_decode_select(dims, cache, q, k, idx, None, ws, stream=cap)
+        for i in range(len(qs)):
+            hs2.hs2_decode_sparse_attn(dims, cache, qs[i], k, v, idx, outs[i], hs2.HS2_OUT_BF16,
+                                       ws_sp, stream=cap)
+    graph_ms = timed(graph.replay, steps)
     b_sel, b_sp = decode_work(w.lengths, Hq, Hkv, d, K, W, len(qs))
     # the same step over an FP8 (E4M3) KV cache: selection and sparse layers read codes
     ks8, vs8 = 1.0 / 16, 1.0 / 16
@@ -588,6 +597,7 @@ def main_decode(args):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "whole decode step", "algorithmic_bytes_per_step": b_step},
         "select_ms": round(sel_ms, 5), "sparse_layer_ms": round(sp_ms, 5),
+        "graph_ms_per_step": round(graph_ms, 5),
         "select_bytes": b_sel, "sparse_layer_bytes": b_sp,
         "fp8_kv": {"ms_per_step": round(step8_ms, 5),
                    "tokens_per_s": round(B / (step8_ms * 1e-3), 1),
