@@ -147,9 +147,11 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   geo->Hq = d->num_q_heads;
   geo->Hkv = d->num_kv_heads;
   layout_select(geo, tpc);
-  // exact path: histogram, scratch words, two bitmaps, G query rows in fp32
-  geo->exact_lds =
-      (hs2::kTopkBins + 16 + 2 * (size_t)geo->bitmap_words + 16 * hs2::kHeadDim) * sizeof(uint32_t);
+  // exact path: histogram, scratch words, two bitmaps, then G query rows in fp32 or
+  // (after them) the boundary-bin list of keys and positions
+  geo->exact_lds = (hs2::kTopkBins + 16 + 2 * (size_t)geo->bitmap_words +
+                    std::max<size_t>(16 * hs2::kHeadDim, 2 * (size_t)hs2::kExactListCap)) *
+                   sizeof(uint32_t);
   // top-K waves: a 256-bin histogram and one bitmap each; up to 4 waves per block
   // a 256-bin histogram, a bitmap and the staging of the selected positions
   geo->sbuf_words = std::min(d->top_k, hs2::kMaxRankedK);

@@ -22,6 +22,7 @@ constexpr int kMaxRankedK = 2048;  // ... held in registers by the top-K wave (<
 constexpr int64_t kCandBudgetBytes = 4LL << 30;  // candidate buffer cap per chunk
 constexpr int64_t kDenseBudgetBytes = 16LL << 30;  // dense score rows (exact path) per chunk
 constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact path
+constexpr int kExactListCap = 2048;              // boundary-bin values the exact path ranks in LDS
 constexpr int kBlockTokens = 64;                 // tokens per block in block selection (= kKeyTile)
 // sampled threshold: rank r = ceil(kTauAlpha * K * n_sample / n_cand) + kTauBeta
 constexpr float kTauAlpha = 1.2f;

@@ -148,9 +148,12 @@ __device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int
 // positions whose key equals kth.
 template <class KeyFn, class PosFn>
 __device__ void mark_selected(KeyFn key, PosFn pos, int n, uint32_t kth, int krem, int nwords,
-                              const TopkShared& sh) {
+                              const TopkShared& sh, bool keep_sel = false) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < nwords; i += kSelThreads) { sh.sel[i] = 0u; sh.tie[i] = 0u; }
+  for (int i = tid; i < nwords; i += kSelThreads) {
+    if (!keep_sel) sh.sel[i] = 0u;
+    sh.tie[i] = 0u;
+  }
   if (tid == 0) sh.misc[2] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += kSelThreads) {
@@ -507,6 +510,104 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   if (kth_out && l == 0) *kth_out = __uint_as_float(kth);
 }
 
+// The exact path's ranking of one dense row in two passes over it: a histogram of
+// the top bits of S (S >= 0, so bits 30..20: exponent and 3 mantissa bits) gives
+// the bin d1 holding the kt-th largest value and how many lie above it; the second
+// pass marks every value above d1 as selected and copies the values of d1, with their
+// positions, into an LDS list, where the radix select finishes and the ties take the
+// lowest positions. Returns false (nothing changed but the histogram) when kt is
+// outside (0, n), or d1 holds more than kExactListCap values: then the whole-row
+// radix select runs instead. On true, sh.sel holds the kt selected positions.
+// fn(i, row[i]) for every i < n, spread over the workgroup; the body reads the row
+// 16 bytes per lane, two loads in flight (row is 4-byte aligned).
+template <class Fn>
+__device__ __forceinline__ void sweep_row(const uint32_t* row, int n, Fn fn) {
+  const int tid = threadIdx.x;
+  const int head = min(n, (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) >> 2));
+  if (tid < head) fn(tid, row[tid]);
+  const int nv = (n - head) >> 2;
+  const uint4* v = reinterpret_cast<const uint4*>(row + head);
+  int j = tid;
+  for (; j + kSelThreads < nv; j += 2 * kSelThreads) {
+    const uint4 x = v[j], y = v[j + kSelThreads];
+    const int i = head + 4 * j, i2 = i + 4 * kSelThreads;
+    fn(i, x.x); fn(i + 1, x.y); fn(i + 2, x.z); fn(i + 3, x.w);
+    fn(i2, y.x); fn(i2 + 1, y.y); fn(i2 + 2, y.z); fn(i2 + 3, y.w);
+  }
+  if (j < nv) {
+    const uint4 x = v[j];
+    const int i = head + 4 * j;
+    fn(i, x.x); fn(i + 1, x.y); fn(i + 2, x.z); fn(i + 3, x.w);
+  }
+  for (int i = head + 4 * nv + tid; i < n; i += kSelThreads) fn(i, row[i]);
+}
+
+// Top digit of a score's bits for the exact path's first pass (scores are >= 0;
+// anything with the sign bit set lands in the last bin, which keeps the order).
+__device__ __forceinline__ uint32_t top_digit(uint32_t b) {
+  return min(b >> 20, (uint32_t)kTopkBins - 1u);
+}
+
+__device__ bool rank_via_list(const uint32_t* dense, int n, int kt, int nwords,
+                              const TopkShared& sh, uint32_t* kth_out, int* krem_out) {
+  if (kt <= 0 || kt >= n) return false;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTopkBins; i += kSelThreads) sh.hist[i] = 0u;
+  __syncthreads();
+  sweep_row(dense, n, [&](int, uint32_t b) { atomicAdd(&sh.hist[top_digit(b)], 1u); });
+  __syncthreads();
+  constexpr int kPer = kTopkBins / kSelThreads;
+  uint32_t h[kPer];
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; u++) {
+    h[u] = sh.hist[kPer * tid + u];
+    local += (int)h[u];
+  }
+  int total;
+  const int excl = block_excl_scan(local, sh.misc, &total);
+  const int above = total - excl - local;
+  if (above < kt && kt <= above + local) {
+    int a = above, d = kPer * tid;
+#pragma unroll
+    for (int u = kPer - 1; u >= 0; u--) {
+      if (a + (int)h[u] >= kt) { d = kPer * tid + u; break; }
+      a += (int)h[u];
+    }
+    sh.misc[0] = d;
+    sh.misc[1] = a;
+  }
+  __syncthreads();
+  const uint32_t d1 = (uint32_t)sh.misc[0];
+  const int a1 = sh.misc[1];
+  const int n1 = (int)sh.hist[d1];
+  if (n1 > kExactListCap) return false;  // (uniform: every thread read the same words)
+  uint32_t* lkey = sh.keys;
+  uint32_t* lpos = sh.keys + kExactListCap;
+  for (int i = tid; i < nwords; i += kSelThreads) sh.sel[i] = 0u;
+  if (tid == 0) sh.misc[3] = 0;
+  __syncthreads();
+  sweep_row(dense, n, [&](int i, uint32_t b) {
+    const uint32_t dg = top_digit(b);
+    if (dg > d1) {
+      atomicOr(&sh.sel[i >> 5], 1u << (i & 31));
+    } else if (dg == d1) {
+      const int slot = atomicAdd(&sh.misc[3], 1);
+      lkey[slot] = b;
+      lpos[slot] = (uint32_t)i;
+    }
+  });
+  __syncthreads();
+  // the kt - a1 largest of the list (1 <= kt - a1 <= n1)
+  int krem;
+  const uint32_t kth = radix_kth([&](int i) { return lkey[i]; }, n1, kt - a1, sh, &krem);
+  mark_selected([&](int i) { return lkey[i]; }, [&](int i) { return lpos[i]; }, n1, kth, krem,
+                nwords, sh, /*keep_sel=*/true);
+  *kth_out = kth;
+  *krem_out = krem;
+  return true;
+}
+
 template <int G>
 __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
   extern __shared__ uint32_t smem[];
@@ -562,12 +663,15 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
       }
       __syncthreads();
     }
-    int krem;
-    const uint32_t kth = radix_kth([&](int i) { return dense[i]; }, n_c,
-                                   row_budget(p.K, p.k_end, r.t, r.L), sh, &krem);
+    const int kt = row_budget(p.K, p.k_end, r.t, r.L);
     const int nwords = ceil_div(n_c, 32);
-    mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth,
-                  krem, nwords, sh);
+    int krem;
+    uint32_t kth;
+    if (!rank_via_list(dense, n_c, kt, nwords, sh, &kth, &krem)) {
+      kth = radix_kth([&](int i) { return dense[i]; }, n_c, kt, sh, &krem);
+      mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth,
+                    krem, nwords, sh);
+    }
     write_selected_row(nwords, n_c, r.t, KW, row, sh);
     if (p.kth && threadIdx.x == 0)
       p.kth[(size_t)(r.base + r.t) * p.Hkv + r.g] = __uint_as_float(kth);
