@@ -144,6 +144,34 @@ def test_zero_queries_tie_rule_bit_exact():
     assert (idx.cpu().numpy().reshape(o_idx.shape) == o_idx).all()
 
 
+@pytest.mark.parametrize("K", [256, 3000])
+@pytest.mark.parametrize("qscale", [0.0, 1e-2])
+def test_exact_path_crowded_rows(K, qscale):
+    """The exact path on rows whose scores crowd into one top-bits bin: with Q = 0
+    every score ties (the lower positions win, bit-exact against the oracle); with Q
+    scaled by 1e-2 the scores differ by about one percent. Rows with up to 2048
+    values in the bin that holds the K-th score are ranked from the LDS list, longer
+    ones by the whole-row radix select, so both routes run here."""
+    import oracle
+    import token_level_sparse_hs2_amd as hs2
+    w = synthgen.custom([200, 4700], Hq=8, Hkv=2, K=K, W=32, n_sparse=1, seed=6)
+    inp = synthgen.make_inputs(w)
+    inp["q_full"] = synthgen.float_to_bf16(synthgen.bf16_to_float(inp["q_full"]) * qscale)
+    case = GpuCase(w, inp)
+    idx_t, _ = case.select(flags=hs2.HS2_FLAG_EXACT_SELECT)
+    idx = idx_t.cpu().numpy()
+    check_structure(idx, inp["cu_seqlens"], w.K, w.W)
+    if qscale == 0.0:
+        o_idx, _ = oracle.select(inp["q_full"], inp["k"], inp["cu_seqlens"], w.Hq, w.Hkv, w.K,
+                                 w.W, scale=w.scale)
+        assert (idx.reshape(o_idx.shape) == o_idx).all()
+    else:
+        stats = acceptance_select(idx, inp, w)
+        log(f"  select: rows {stats['rows']} identical {stats['exact_rows']} overlap "
+            f"{stats['overlap']:.6f} A1 margin {stats['a1_worst_margin']:.3g}")
+        assert_select_ok(stats)
+
+
 def test_peaked_softmax_rows():
     """Queries scaled by 8: the full layer's softmax is sharply peaked and a
     norm-based bound on each row's maximum overshoots by far more than the

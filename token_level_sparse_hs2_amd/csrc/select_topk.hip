@@ -61,43 +61,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// K-th largest key among key(i), i < n (1 <= k <= n). Returns the key and, in
-// *krem, how many elements equal to it belong to the top k. Radix select on the
-// bits below the keys' common prefix, up to 11 bits (2048 bins) per pass. With
-// max_passes, it stops early and returns the lower edge of the bin that holds the
-// K-th largest key (at least k keys reach it; *krem is then meaningless).
+// The digit passes of radix_kth for keys that all share the bits in mask (equal to
+// prefix); hi is the highest bit below them.
 template <class KeyFn>
-__device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int* krem,
-                              int max_passes = 3) {
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = tid; i < n; i += kSelThreads) {
-    const uint32_t b = key(i);
-    mn = min(mn, b);
-    mx = max(mx, b);
-  }
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if (l == 0) {
-    sh.misc[4 + w] = (int)mn;
-    sh.misc[8 + w] = (int)mx;
-  }
-  __syncthreads();
-  mn = (uint32_t)sh.misc[4];
-  mx = (uint32_t)sh.misc[8];
-#pragma unroll
-  for (int i = 1; i < 4; i++) {
-    mn = min(mn, (uint32_t)sh.misc[4 + i]);
-    mx = max(mx, (uint32_t)sh.misc[8 + i]);
-  }
-  __syncthreads();
-  if (mn == mx) {
-    *krem = k;
-    return mn;
-  }
-  int hi = 31 - __clz(mn ^ mx);  // highest bit where the keys differ
-  uint32_t mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
-  uint32_t prefix = mx & mask;
+__device__ uint32_t radix_digits(KeyFn key, int n, int k, const TopkShared& sh, int* krem, int hi,
+                                 uint32_t mask, uint32_t prefix, int max_passes = 3) {
+  const int tid = threadIdx.x;
   int kr = k;
   constexpr int kPer = kTopkBins / kSelThreads;  // bins per thread in the scan
   for (int pass = 0; hi >= 0 && pass < max_passes; pass++) {
@@ -142,6 +111,45 @@ __device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int
   }
   *krem = kr;
   return prefix;
+}
+
+// K-th largest key among key(i), i < n (1 <= k <= n). Returns the key and, in
+// *krem, how many elements equal to it belong to the top k. Radix select on the
+// bits below the keys' common prefix, up to 11 bits (2048 bins) per pass. With
+// max_passes, it stops early and returns the lower edge of the bin that holds the
+// K-th largest key (at least k keys reach it; *krem is then meaningless).
+template <class KeyFn>
+__device__ uint32_t radix_kth(KeyFn key, int n, int k, const TopkShared& sh, int* krem,
+                              int max_passes = 3) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = tid; i < n; i += kSelThreads) {
+    const uint32_t b = key(i);
+    mn = min(mn, b);
+    mx = max(mx, b);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (l == 0) {
+    sh.misc[4 + w] = (int)mn;
+    sh.misc[8 + w] = (int)mx;
+  }
+  __syncthreads();
+  mn = (uint32_t)sh.misc[4];
+  mx = (uint32_t)sh.misc[8];
+#pragma unroll
+  for (int i = 1; i < 4; i++) {
+    mn = min(mn, (uint32_t)sh.misc[4 + i]);
+    mx = max(mx, (uint32_t)sh.misc[8 + i]);
+  }
+  __syncthreads();
+  if (mn == mx) {
+    *krem = k;
+    return mn;
+  }
+  const int hi = 31 - __clz(mn ^ mx);  // highest bit where the keys differ
+  const uint32_t mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
+  return radix_digits(key, n, k, sh, krem, hi, mask, mx & mask, max_passes);
 }
 
 // Marks in sh.sel every position whose key is above kth, plus the krem lowest
@@ -519,7 +527,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
 // outside (0, n), or d1 holds more than kExactListCap values: then the whole-row
 // radix select runs instead. On true, sh.sel holds the kt selected positions.
 // fn(i, row[i]) for every i < n, spread over the workgroup; the body reads the row
-// 16 bytes per lane, two loads in flight (row is 4-byte aligned).
+// 16 bytes per lane with kSweepLoads loads in flight per lane (row is 4-byte aligned).
+#ifndef HS2_SWEEP_LOADS
+#define HS2_SWEEP_LOADS 8
+#endif
+constexpr int kSweepLoads = HS2_SWEEP_LOADS;
 template <class Fn>
 __device__ __forceinline__ void sweep_row(const uint32_t* row, int n, Fn fn) {
   const int tid = threadIdx.x;
@@ -527,17 +539,19 @@ __device__ __forceinline__ void sweep_row(const uint32_t* row, int n, Fn fn) {
   if (tid < head) fn(tid, row[tid]);
   const int nv = (n - head) >> 2;
   const uint4* v = reinterpret_cast<const uint4*>(row + head);
-  int j = tid;
-  for (; j + kSelThreads < nv; j += 2 * kSelThreads) {
-    const uint4 x = v[j], y = v[j + kSelThreads];
-    const int i = head + 4 * j, i2 = i + 4 * kSelThreads;
-    fn(i, x.x); fn(i + 1, x.y); fn(i + 2, x.z); fn(i + 3, x.w);
-    fn(i2, y.x); fn(i2 + 1, y.y); fn(i2 + 2, y.z); fn(i2 + 3, y.w);
-  }
-  if (j < nv) {
-    const uint4 x = v[j];
-    const int i = head + 4 * j;
-    fn(i, x.x); fn(i + 1, x.y); fn(i + 2, x.z); fn(i + 3, x.w);
+  for (int j0 = 0; j0 < nv; j0 += kSweepLoads * kSelThreads) {
+    uint4 x[kSweepLoads];
+#pragma unroll
+    for (int u = 0; u < kSweepLoads; u++)  // (clamped, not branched: all loads in flight)
+      x[u] = v[min(j0 + u * kSelThreads + tid, nv - 1)];
+#pragma unroll
+    for (int u = 0; u < kSweepLoads; u++) {
+      const int j = j0 + u * kSelThreads + tid;
+      if (j < nv) {
+        const int i = head + 4 * j;
+        fn(i, x[u].x); fn(i + 1, x[u].y); fn(i + 2, x[u].z); fn(i + 3, x[u].w);
+      }
+    }
   }
   for (int i = head + 4 * nv + tid; i < n; i += kSelThreads) fn(i, row[i]);
 }
@@ -598,11 +612,16 @@ __device__ bool rank_via_list(const uint32_t* dense, int n, int kt, int nwords,
     }
   });
   __syncthreads();
-  // the kt - a1 largest of the list (1 <= kt - a1 <= n1)
+  // the kt - a1 largest of the list (1 <= kt - a1 <= n1); below the last bin the
+  // list's keys share their top 12 bits (d1 and a clear sign bit)
   int krem;
-  const uint32_t kth = radix_kth([&](int i) { return lkey[i]; }, n1, kt - a1, sh, &krem);
-  mark_selected([&](int i) { return lkey[i]; }, [&](int i) { return lpos[i]; }, n1, kth, krem,
-                nwords, sh, /*keep_sel=*/true);
+  const auto lk = [&](int i) { return lkey[i]; };
+  const uint32_t kth =
+      d1 < (uint32_t)kTopkBins - 1u
+          ? radix_digits(lk, n1, kt - a1, sh, &krem, 19, 0xFFF00000u, d1 << 20)
+          : radix_kth(lk, n1, kt - a1, sh, &krem);
+  mark_selected(lk, [&](int i) { return lpos[i]; }, n1, kth, krem, nwords, sh,
+                /*keep_sel=*/true);
   *kth_out = kth;
   *krem_out = krem;
   return true;
