@@ -126,8 +126,9 @@ typedef struct {
  * op:
  *   HS2_OP_SELECT       the selection (hs2_select, hs2_select_ex, hs2_select_full):
  *                       per-row statistics, candidate rows of one chunk of tasks
- *                       (at most 4 GiB of candidates; with the exact flag or top_k
- *                       above 2048, dense score rows of at most 16 GiB), exact-path
+ *                       (at most 4 GiB of candidates, 2 * top_k slots per row when
+ *                       top_k > 1024; with the exact flag or top_k above 8192, dense
+ *                       score rows of at most 16 GiB), exact-path
  *                       scratch. A smaller
  *                       workspace, down to HS2_OP_SELECT_MIN bytes, is accepted too:
  *                       the selection then runs in more, smaller chunks with the

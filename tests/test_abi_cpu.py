@@ -172,10 +172,34 @@ def test_workspace_sizes_are_bounded(lib):
         assert sel - smin <= 4 * (1 << 30)
 
 
+def test_list_ranked_workspace(lib):
+    """top_k from 2049 to 8192 with a row longer than two lists: candidate rows of
+    2 * top_k slots (ranked from the lists), at most 4 GiB of them per chunk; with no
+    such row, dense score rows (at most 16 GiB per chunk). One task's rows fit the
+    smallest workspace."""
+    for K in (2049, 3000, 8192):
+        d = hs2.make_dims(32, 8, K, 128)
+        cap = (2 * K + 63) // 64 * 64
+        for lengths in ([1024], [2 * cap], [2 * cap + 1], [32768], [131072],
+                        [196608, 4096, 50000]):
+            vl = varlen(lengths)
+            L = max(lengths)
+            sel = hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_SELECT)
+            smin = hs2.hs2_workspace_size(d, vl, hs2.HS2_OP_SELECT_MIN)
+            if L > 2 * cap:
+                # one task's candidate rows: 8 groups x 64 tokens, cap slots of 8 bytes
+                assert 8 * 64 * cap * 8 <= smin <= sel
+                assert sel - smin <= 4 * (1 << 30)
+            else:
+                # one task's dense rows: 8 groups x 64 tokens, L scores each
+                assert 8 * 64 * L * 4 <= smin <= sel
+                assert sel - smin <= 16 * (1 << 30)
+
+
 def test_dense_exact_workspace_is_bounded(lib):
-    """top_k above 2048 (or the exact flag): every ranked row's scores go to a dense row,
+    """top_k above 8192 (or the exact flag): every ranked row's scores go to a dense row,
     so the selection workspace holds whole rows, at most 16 GiB of them per chunk."""
-    for flags, K in ((0, 3000), (hs2.HS2_FLAG_EXACT_SELECT, 1024)):
+    for flags, K in ((0, 8193), (hs2.HS2_FLAG_EXACT_SELECT, 1024)):
         d = hs2.make_dims(32, 8, K, 128, flags=flags)
         for lengths in ([1024], [32768], [131072], [196608, 4096, 50000]):
             vl = varlen(lengths)

@@ -10,7 +10,8 @@ it times it:
   - hs2_select_ex with the output-aware metric (beta 0.5) and with the
     position-decaying budget (mu 0.5);
   - 64-token block selection;
-  - the exact path (top_k 3000, above the register-ranked limit);
+  - top_k 3000 (above the register-ranked limit: rows ranked from their candidate
+    lists) and the exact path (the exact flag at top_k 1024);
   - run-to-run identity of the selection, and identity when the workspace forces
     one selection task per chunk.
 
@@ -278,14 +279,16 @@ def test_block_selection_as_benched(w32):
     assert rel.max() <= 1e-3
 
 
-def test_exact_path_as_benched(w32):
-    """top_k 3000 (bench.py's exact_path figure): every row with more candidates is
-    ranked by the exact kernel over its whole row."""
+@pytest.mark.parametrize("K,flags", [(3000, 0), (1024, 1)], ids=["large_budget", "exact_flag"])
+def test_large_budget_and_exact_path_as_benched(w32, K, flags):
+    """bench.py's large_budget figure (top_k 3000: every row with more candidates is
+    ranked from its candidate list by the exact kernel) and exact_path figure (the
+    exact flag at top_k 1024: every such row ranked over its whole row of scores)."""
     import torch
     import token_level_sparse_hs2_amd as hs2
     w, inp, case, toks = w32
-    K = 3000
-    dims = hs2.make_dims(w.Hq, w.Hkv, K, w.W, w.scale)
+    dims = hs2.make_dims(w.Hq, w.Hkv, K, w.W, w.scale,
+                         flags=hs2.HS2_FLAG_EXACT_SELECT if flags else 0)
     ws = torch.empty(hs2.hs2_workspace_size(dims, case.varlen, hs2.HS2_OP_SELECT),
                      dtype=torch.uint8, device="cuda")
     idx_t = case.new_idx(K + w.W)
@@ -296,7 +299,7 @@ def test_exact_path_as_benched(w32):
     wk = synthgen.workload("32k")
     wk.K = K
     stats = acceptance_select(idx, inp, wk, tokens=toks)
-    log(f"  exact path K={K}: rows {stats['rows']} identical {stats['exact_rows']} overlap "
+    log(f"  K={K} flags={flags}: rows {stats['rows']} identical {stats['exact_rows']} overlap "
         f"{stats['overlap']:.6f} A1 margin {stats['a1_worst_margin']:.3g}")
     assert_select_ok(stats)
 

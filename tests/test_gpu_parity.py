@@ -102,8 +102,8 @@ def test_ragged_varlen_every_group_size(G):
 @pytest.mark.parametrize("K,W", [(0, 32), (256, 0), (1, 1), (3000, 16), (6000, 64)])
 def test_budget_edges(K, W):
     """K = 0 (the window only), W = 0 (no window), K = W = 1, K above the
-    register-ranked limit (every ranked row takes the exact path) and K + W above
-    every length (all causal keys: dense)."""
+    register-ranked limit with every sequence shorter than two candidate lists (the
+    dense exact path) and K + W above every length (all causal keys: dense)."""
     w = synthgen.custom([1, 2, 33, 700, 2100, 4500], Hq=8, Hkv=2, K=K, W=W, n_sparse=1,
                         seed=170 + K % 97 + W)
     run_case(w)
@@ -116,6 +116,38 @@ def test_large_budget_register_ranking(K, W):
     sampled threshold)."""
     w = synthgen.custom([2500, 6000], Hq=8, Hkv=2, K=K, W=W, n_sparse=1, seed=180 + K % 89)
     run_case(w)
+
+
+@pytest.mark.parametrize("K,W,lengths", [(2049, 64, [2500, 9000]), (3000, 128, [5000, 14000]),
+                                         (8192, 64, [3000, 34000])])
+def test_large_budget_list_ranking(K, W, lengths):
+    """2048 < K <= 8192 with a sequence longer than 2C: up to C = 2K candidates per row
+    (all of a row's candidates when it has at most C, else those at or above its sampled
+    threshold), ranked from the candidate lists by the exact kernel. Sampled rows (the sequences' heads and tails,
+    a stride, and the rows around the budget and around n_c = C) follow the oracle;
+    every row equals the dense exact path's (the exact flag) bit for bit, since both
+    rank the same scores and a list holds every key that can reach the top K."""
+    import torch
+    import token_level_sparse_hs2_amd as hs2
+    w = synthgen.custom(lengths, Hq=8, Hkv=2, K=K, W=W, n_sparse=1, seed=190 + K % 83)
+    C = (2 * K + 63) // 64 * 64
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    extra = [int(cu[i]) + t for i, L in enumerate(lengths)
+             for t in (C + W - 2, C + W - 1, C + W, C + W + 1) if t < L]
+    toks = np.union1d(sample_tokens(lengths, K, W, head=8, tail=8, stride=397),
+                      np.array(extra, dtype=np.int64))
+    case, idx_t = run_case(w, tokens=toks)
+    idx_exact, _ = case.select(flags=hs2.HS2_FLAG_EXACT_SELECT)
+    same = (idx_t == idx_exact).all(dim=2).float().mean().item()
+    log(f"  rows identical to the dense exact path: {same:.6f}")
+    assert torch.equal(idx_t, idx_exact)
+
+
+def test_budget_above_the_list_limit():
+    """K > 8192: every ranked row takes the dense exact path (its scores written whole)."""
+    w = synthgen.custom([700, 10500], Hq=8, Hkv=2, K=8200, W=32, n_sparse=1, seed=211)
+    toks = sample_tokens(w.lengths, w.K, w.W, head=8, tail=64, stride=211)
+    run_case(w, tokens=toks)
 
 
 def test_exact_flag_path():

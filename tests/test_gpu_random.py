@@ -1,9 +1,10 @@
 """Seeded random configurations through the whole path as hs2_prefill_block runs it
 (selection, shared-gather plan or per-token layers, one to three sparse layers), each
 checked against the CPU oracle on every row: group sizes 1 to 16, one to sixteen KV
-groups, budgets from 0 past the register-ranked limit (2048, where every ranked row
-takes the dense exact path), windows from 0, ragged packed lengths (up to 8 sequences,
-many under 200 tokens, and one batch of 500 sequences), and the exact flag.
+groups, budgets from 0 past the register-ranked limit (2048; above it the rows are
+ranked from their candidate lists when a sequence is longer than two lists, else by the
+dense exact path), windows from 0, ragged packed lengths (up to 8 sequences, many
+under 200 tokens, and one batch of 500 sequences), and the exact flag.
 
 Per case: the index rows' structure and A1/A2 on all rows; A4 for every layer's fp32
 output and A3 for its bf16 output, both on the GPU's own index rows; and the bf16 call
@@ -75,14 +76,29 @@ def _wide_configs(n=20, seed=77):
     return out
 
 
+def _list_ranked_configs():
+    """Budgets above the register-ranked limit with one sequence longer than two
+    candidate lists (2 * 2K slots), so the rows are ranked from their lists."""
+    rng = np.random.default_rng(31)
+    out = []
+    for i, K in enumerate((2049, 2500, 3000)):
+        G = int(rng.choice([1, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        W = int(rng.choice([0, 64, 128]))
+        C = (2 * K + 63) // 64 * 64
+        lengths = [int(x) for x in rng.integers(1, 3000, size=2)] + [2 * C + 300 + 100 * i]
+        out.append((3000 + i, G, Hkv, K, W, lengths, 2, False))
+    return out
+
+
 def _many_sequences():
     """500 packed sequences of 1-399 tokens (100k tokens)."""
     rng = np.random.default_rng(99)
     return [(2000, 4, 2, 64, 16, [int(x) for x in rng.integers(1, 400, size=500)], 2, False)]
 
 
-@pytest.mark.parametrize("cfg", _configs() + _wide_configs() + _many_sequences(),
-                         ids=lambda c: f"case{c[0]}")
+@pytest.mark.parametrize("cfg", _configs() + _wide_configs() + _list_ranked_configs() +
+                         _many_sequences(), ids=lambda c: f"case{c[0]}")
 def test_random_configuration(cfg):
     import oracle
     import token_level_sparse_hs2_amd as hs2

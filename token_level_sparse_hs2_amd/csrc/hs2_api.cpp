@@ -42,7 +42,9 @@ struct Geometry {
   size_t exact_lds = 0;
   int topk_rows_per_block = 4;
   int sbuf_words = 0;
-  bool exact_only = false;  // K above the register-ranked limit: every row takes the exact path
+  bool exact_only = false;  // K above the list-ranked limit: every row takes the exact path
+  bool list_rank = false;   // K above the register-ranked limit: candidate lists ranked by
+                            // exact_kernel instead of the top-K waves
   bool dense = false;       // every ranked row takes the exact path: dense score rows
   int block = 0;            // block selection: tokens per block
   // shared-gather plan of the sparse layers (usable when plan_ok)
@@ -129,9 +131,15 @@ int validate(const hs2_dims* d, const hs2_varlen* v, Geometry* geo) {
   // candidate rows: C slots each; chunks of whole tasks under the byte budget
   const int K = d->top_k;
   geo->block = (d->flags & HS2_FLAG_BLOCK_SELECT) ? hs2::kBlockTokens : 0;
-  geo->exact_only = !geo->block && K > hs2::kMaxRankedK;
-  geo->dense = !geo->block && (geo->exact_only || (d->flags & HS2_FLAG_EXACT_SELECT));
   int64_t cap = std::max<int64_t>(hs2::kMinCandCap, 2LL * K);
+  // K above the register-ranked limit: the rows are ranked from their candidate lists
+  // (up to 2K each) when the longest row exceeds two lists; with shorter rows a list is
+  // most of its row at twice the bytes per entry, and the dense rows measured faster
+  // (8k tokens, K = 3000: 1.73 against 1.98 ms)
+  const bool big = !geo->block && K > hs2::kMaxRankedK;
+  geo->exact_only = big && (K > hs2::kMaxListK || (int64_t)max_len <= 2 * cap);
+  geo->dense = !geo->block && (geo->exact_only || (d->flags & HS2_FLAG_EXACT_SELECT));
+  geo->list_rank = big && !geo->dense;
   if (geo->block)  // one entry per candidate block of the longest row (<= 4096, ranked in registers)
     cap = std::max<int64_t>(64, hs2::ceil_div(std::max(1, max_len), hs2::kBlockTokens));
   if (geo->dense)  // the candidate rows hold one fp32 score per position (two per 8-byte slot)
@@ -308,6 +316,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   sp.cand_cap = geo.cand_cap;
   sp.flags = d->flags | (geo.exact_only ? (uint32_t)HS2_FLAG_EXACT_SELECT : 0u);
   sp.block = geo.block;
+  sp.list_rank = geo.list_rank ? 1 : 0;
   sp.lse2 = lse2;
   sp.lse_given = lse_given ? 1 : 0;
   sp.cand = cand;
@@ -334,6 +343,7 @@ int run_select(const hs2_dims* d, const hs2_varlen* v, const Geometry& geo, cons
   tp.dense_rows = sp.dense_out;
   tp.dense_ld = sp.dense_ld;
   tp.block = geo.block;
+  tp.list_rank = geo.list_rank ? 1 : 0;
   tp.cand_cap = geo.cand_cap;
   tp.bitmap_words = geo.bitmap_words;
   tp.sbuf_words = geo.sbuf_words;

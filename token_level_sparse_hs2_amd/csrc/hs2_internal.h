@@ -18,11 +18,14 @@ constexpr int kSelThreads = 256;  // threads of every selection workgroup
 constexpr int kTopkBins = 2048;   // radix bins per pass of the top-K select (11 bits)
 constexpr int kMinCandCap = 2048;  // candidate slots per row: max(2048, 2K) ...
 constexpr int kMaxRankedK = 2048;  // ... held in registers by the top-K wave (<= 64 per lane);
-                                   // a larger K sends every row to the exact path
+                                   // a larger K is ranked by exact_kernel from the lists
+constexpr int kMaxListK = 8192;    // largest K ranked from candidate lists (2K slots per row),
+                                   // when some row is longer than 4K; otherwise, and above
+                                   // it, every row takes the dense exact path
 constexpr int64_t kCandBudgetBytes = 4LL << 30;  // candidate buffer cap per chunk
 constexpr int64_t kDenseBudgetBytes = 16LL << 30;  // dense score rows (exact path) per chunk
-constexpr int kFallbackBlocks = 1024;            // persistent grid of the exact path
-constexpr int kExactListCap = 2048;              // boundary-bin values the exact path ranks in LDS
+constexpr int kFallbackBlocks = 1280;            // persistent grid of the exact path (5 per CU)
+constexpr int kExactListCap = 1024;              // boundary-bin values the exact path ranks in LDS
 constexpr int kBlockTokens = 64;                 // tokens per block in block selection (= kKeyTile)
 // sampled threshold: rank r = ceil(kTauAlpha * K * n_sample / n_cand) + kTauBeta
 constexpr float kTauAlpha = 1.2f;
@@ -96,6 +99,7 @@ struct ScoreParams {
   const uint32_t* kmax; // [B * Hkv] largest key norm of each (sequence, group), float bits
   int cand_cap;         // C
   uint32_t flags;
+  int list_rank;        // K > kMaxRankedK: rows within [K, C] candidates go to exact_kernel too
   int block;            // 0, or kBlockTokens: block selection (candidates are block scores)
   const float* vw;      // [T, Hkv] log2 key weights beta * max(0, log2 |v|), or null (plain score)
   const uint32_t* vwmax;  // [B * Hkv] largest weight of each (sequence, group), float bits
@@ -123,6 +127,7 @@ struct TopkParams {
   const float* dense_rows;  // [chunk rows, dense_ld] S of every candidate (scores kernel), or
   int64_t dense_ld;         // null: the exact path then recomputes the scores
   int block;            // 0, or kBlockTokens: candidates are (block score, block index)
+  int list_rank;        // rows with a candidate count >= 0 are ranked by exact_kernel
   int cand_cap;
   int bitmap_words;     // words per bitmap in LDS (covers max_seqlen)
   int sbuf_words;       // per-wave LDS staging of the selected positions (min(K, kMaxRankedK))

@@ -791,7 +791,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
         count = -1;
     }
     p.cand_count[slot0 + tid] = count;
-    if (count < 0) {
+    if (count < 0 || (p.list_rank && mode == kModeEmit)) {
       const int f = atomicAdd(p.flag_count, 1);
       p.flag_list[f] = (int32_t)(slot0 + tid);
     }

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     return;
   }
   const int count = p.cand_count[slot];
-  if (count < 0) return;  // settled by exact_kernel
+  if (count < 0 || p.list_rank) return;  // settled by exact_kernel
   const uint64_t* cand = p.cand + (size_t)slot * p.cand_cap;
   uint32_t key[NREG], pos[NREG];
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -518,7 +518,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   if (kth_out && l == 0) *kth_out = __uint_as_float(kth);
 }
 
-// The exact path's ranking of one dense row in two passes over it: a histogram of
+// The exact path's ranking of one row of (position, score) entries (a dense row, or a
+// candidate list) in two passes over it: a histogram of
 // the top bits of S (S >= 0, so bits 30..20: exponent and 3 mantissa bits) gives
 // the bin d1 holding the kt-th largest value and how many lie above it; the second
 // pass marks every value above d1 as selected and copies the values of d1, with their
@@ -528,10 +529,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
 // radix select runs instead. On true, sh.sel holds the kt selected positions.
 // fn(i, row[i]) for every i < n, spread over the workgroup; the body reads the row
 // 16 bytes per lane with kSweepLoads loads in flight per lane (row is 4-byte aligned).
-#ifndef HS2_SWEEP_LOADS
-#define HS2_SWEEP_LOADS 8
-#endif
-constexpr int kSweepLoads = HS2_SWEEP_LOADS;
+constexpr int kSweepLoads = 8;
 template <class Fn>
 __device__ __forceinline__ void sweep_row(const uint32_t* row, int n, Fn fn) {
   const int tid = threadIdx.x;
@@ -556,19 +554,46 @@ __device__ __forceinline__ void sweep_row(const uint32_t* row, int n, Fn fn) {
   for (int i = head + 4 * nv + tid; i < n; i += kSelThreads) fn(i, row[i]);
 }
 
+// fn(position, S bits) for every entry of a candidate list (8-byte entries: the
+// position in the low word, S in the high word; the list is 16-byte aligned)
+template <class Fn>
+__device__ __forceinline__ void sweep_cand(const uint64_t* list, int n, Fn fn) {
+  const int tid = threadIdx.x;
+  const int nv = n >> 1;
+  const uint4* v = reinterpret_cast<const uint4*>(list);
+  for (int j0 = 0; j0 < nv; j0 += kSweepLoads * kSelThreads) {
+    uint4 x[kSweepLoads];
+#pragma unroll
+    for (int u = 0; u < kSweepLoads; u++)  // (clamped, not branched: all loads in flight)
+      x[u] = v[min(j0 + u * kSelThreads + tid, nv - 1)];
+#pragma unroll
+    for (int u = 0; u < kSweepLoads; u++) {
+      if (j0 + u * kSelThreads + tid < nv) {
+        fn(x[u].x, x[u].y);
+        fn(x[u].z, x[u].w);
+      }
+    }
+  }
+  if ((n & 1) && tid == 0) {
+    const uint2 e = reinterpret_cast<const uint2*>(list)[n - 1];
+    fn(e.x, e.y);
+  }
+}
+
 // Top digit of a score's bits for the exact path's first pass (scores are >= 0;
 // anything with the sign bit set lands in the last bin, which keeps the order).
 __device__ __forceinline__ uint32_t top_digit(uint32_t b) {
   return min(b >> 20, (uint32_t)kTopkBins - 1u);
 }
 
-__device__ bool rank_via_list(const uint32_t* dense, int n, int kt, int nwords,
-                              const TopkShared& sh, uint32_t* kth_out, int* krem_out) {
+template <class SweepFn>
+__device__ bool rank_via_list(SweepFn sweep, int n, int kt, int nwords, const TopkShared& sh,
+                              uint32_t* kth_out, int* krem_out) {
   if (kt <= 0 || kt >= n) return false;
   const int tid = threadIdx.x;
   for (int i = tid; i < kTopkBins; i += kSelThreads) sh.hist[i] = 0u;
   __syncthreads();
-  sweep_row(dense, n, [&](int, uint32_t b) { atomicAdd(&sh.hist[top_digit(b)], 1u); });
+  sweep([&](uint32_t, uint32_t b) { atomicAdd(&sh.hist[top_digit(b)], 1u); });
   __syncthreads();
   constexpr int kPer = kTopkBins / kSelThreads;
   uint32_t h[kPer];
@@ -601,14 +626,14 @@ __device__ bool rank_via_list(const uint32_t* dense, int n, int kt, int nwords,
   for (int i = tid; i < nwords; i += kSelThreads) sh.sel[i] = 0u;
   if (tid == 0) sh.misc[3] = 0;
   __syncthreads();
-  sweep_row(dense, n, [&](int i, uint32_t b) {
+  sweep([&](uint32_t i, uint32_t b) {
     const uint32_t dg = top_digit(b);
     if (dg > d1) {
       atomicOr(&sh.sel[i >> 5], 1u << (i & 31));
     } else if (dg == d1) {
       const int slot = atomicAdd(&sh.misc[3], 1);
       lkey[slot] = b;
-      lpos[slot] = (uint32_t)i;
+      lpos[slot] = i;
     }
   });
   __syncthreads();
@@ -639,6 +664,27 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
     const RowInfo r = decode_slot(p, slot);
     const int n_c = r.t - p.W + 1;
     int32_t* row = p.idx + ((size_t)(r.base + r.t) * p.Hkv + r.g) * KW;
+    const int kt = row_budget(p.K, p.k_end, r.t, r.L);
+    const int nwords = ceil_div(n_c, 32);
+    int krem;
+    uint32_t kth;
+    const int count = p.list_rank ? p.cand_count[slot] : -1;
+    if (count >= 0) {
+      // a candidate list of count entries, kt <= count <= C (budgets above the
+      // register-ranked limit): ranked here from the list, not from dense scores
+      const uint64_t* list = p.cand + (size_t)slot * p.cand_cap;
+      if (!rank_via_list([&](auto fn) { sweep_cand(list, count, fn); }, count, kt, nwords, sh,
+                         &kth, &krem)) {
+        kth = radix_kth([&](int i) { return (uint32_t)(list[i] >> 32); }, count, kt, sh, &krem);
+        mark_selected([&](int i) { return (uint32_t)(list[i] >> 32); },
+                      [&](int i) { return (uint32_t)list[i]; }, count, kth, krem, nwords, sh);
+      }
+      write_selected_row(nwords, n_c, r.t, KW, row, sh);
+      if (p.kth && threadIdx.x == 0)
+        p.kth[(size_t)(r.base + r.t) * p.Hkv + r.g] = __uint_as_float(kth);
+      __syncthreads();
+      continue;
+    }
     // the row's scores: written by the scores kernel, or recomputed here
     const uint32_t* dense = p.dense_rows
         ? reinterpret_cast<const uint32_t*>(p.dense_rows + (size_t)slot * p.dense_ld)
@@ -682,11 +728,8 @@ __global__ __launch_bounds__(kSelThreads) void exact_kernel(TopkParams p) {
       }
       __syncthreads();
     }
-    const int kt = row_budget(p.K, p.k_end, r.t, r.L);
-    const int nwords = ceil_div(n_c, 32);
-    int krem;
-    uint32_t kth;
-    if (!rank_via_list(dense, n_c, kt, nwords, sh, &kth, &krem)) {
+    if (!rank_via_list([&](auto fn) { sweep_row(dense, n_c, fn); }, n_c, kt, nwords, sh, &kth,
+                       &krem)) {
       kth = radix_kth([&](int i) { return dense[i]; }, n_c, kt, sh, &krem);
       mark_selected([&](int i) { return dense[i]; }, [&](int i) { return (uint32_t)i; }, n_c, kth,
                     krem, nwords, sh);
@@ -960,7 +1003,7 @@ hipError_t launch_topk(int G, const TopkParams& p, int n_tasks, int rows_per_blo
       (size_t)rows_per_block * (256 + p.bitmap_words + p.sbuf_words) * sizeof(uint32_t);
   const dim3 grid((unsigned)n_tasks * (unsigned)(p.tok / rows_per_block), (unsigned)p.Hkv),
       block(64 * rows_per_block);
-  const int nreg = p.cand_cap / 64;
+  const int nreg = p.list_rank ? 32 : p.cand_cap / 64;  // (list-ranked rows are not read)
   if (nreg <= 32) {
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<32>,
