@@ -578,10 +578,25 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 
   // ========================= sweep 2: sample ================================
   if (sm.any_sample) {
+    // which of the lane's tokens take part, and their last candidate key, read once:
+    // the modes do not change during this sweep, and reading them between the
+    // histogram atomics would make every key group wait for the previous atomics
+    bool samp[RT][NT];
+    int jlim[RT][NT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int u = 0; u < NT; u++) {
+        const int tl = token_of(rt, u);
+        samp[rt][u] = owner && tl < TOK && sm.mode[tl] == kModeSample;
+        jlim[rt][u] = t0 + tl - W;
+      }
     sweep(ceil_div(n_kt2, kSampleStride), 0, kSampleStride, cand_end, Pair{}, wts,
           [&](int kt, int buf) HS2_INLINE {
       read_weights(buf);
       compute(buf);
+      // every group score and bin of the tile first, then the atomics
+      uint32_t addr[RT][4][NT], inc[RT][4][NT];
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
 #pragma unroll
@@ -592,14 +607,20 @@ __global__ __launch_bounds__(kSelThreads, 2) void scores_kernel(ScoreParams p) {
 #pragma unroll
           for (int u = 0; u < NT; u++) {
             const int tl = token_of(rt, u);
-            if (owner && tl < TOK && sm.mode[tl] == kModeSample && j <= t0 + tl - W) {
-              int bin = (int)(__float_as_uint(S[u]) >> 20) - bin_base;
-              bin = min(max(bin, 0), kBins - 1);
-              atomicAdd(&sm.u.s.hist[tl][bin >> 1], (bin & 1) ? 65536u : 1u);
-            }
+            int bin = (int)(__float_as_uint(S[u]) >> 20) - bin_base;
+            bin = min(max(bin, 0), kBins - 1);
+            addr[rt][ct][u] = (uint32_t)(tl * (kBins / 2) + (bin >> 1));
+            inc[rt][ct][u] = (samp[rt][u] && j <= jlim[rt][u]) ? ((bin & 1) ? 65536u : 1u) : 0u;
           }
         }
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+          for (int u = 0; u < NT; u++)
+            if (inc[rt][ct][u]) atomicAdd(&sm.u.s.hist[0][0] + addr[rt][ct][u], inc[rt][ct][u]);
     });
     // threshold: interpolated where the sample's top count reaches r
     if (tid < TOK && sm.mode[tid] == kModeSample) {
